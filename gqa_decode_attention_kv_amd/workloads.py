@@ -1,0 +1,242 @@
+"""Seeded synthetic workloads for the GQA decode step.
+
+This module only draws random inputs and describes shapes; it holds none of
+the step's arithmetic (no norm, rotation, rounding to a cache format chosen
+by the method, quantiser or softmax).  The GPU path and the CPU oracle both
+consume what it returns, as data.
+
+Recipe (every draw is ``numpy.random.default_rng([seed, stream, ...])``,
+standard normal float32 unless stated):
+  * lengths: fixed, or uniform integers in [lo, hi] (stream 0);
+  * q_in [B][H][d], k_in and v_in [B][Hkv][d]: streams 1, 2, 3;
+  * QK-norm weights w_q, w_k [d]: stream 4, as mean + std * N(0, 1);
+  * cached keys and values: one block per (b, kv head), streams 5 (K) and
+    6 (V), filling only the visible cached rows [lo_b, L_b - 1).  bf16
+    entries keep the top 16 bits of the float32 draw (a random bf16 number);
+    f32 entries are the draw itself.  vq8 value rows are drawn directly as
+    int8 codes (rounded N(0,1) * 127 / 2.8, clipped to +-127) and an f32
+    scale near 2.8 / 127 (stream 7);
+  * every other cache row (before the window, the new token's slot and
+    beyond) holds a NaN poison (int8 codes 0 with a NaN scale), so a kernel
+    that reads outside the visible range cannot pass a test.
+
+Blocks are filled from a thread pool; each block has its own seed, so the
+result does not depend on the number of threads.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+F32, BF16, I8 = 0, 1, 2
+NEOX, INTERLEAVED = 0, 1
+PLAIN, LLAMA3 = 0, 1
+
+BF16_NAN = np.uint16(0x7FC0)
+STORAGE = {F32: np.float32, BF16: np.uint16, I8: np.int8}
+ELEM_BYTES = {F32: 4, BF16: 2, I8: 1}
+
+
+@dataclass(frozen=True)
+class Rope:
+    pairing: int = NEOX
+    scaling: int = PLAIN
+    theta: float = 10000.0
+    factor: float = 1.0
+    low: float = 1.0
+    high: float = 4.0
+    orig: int = 8192
+
+    def as_dict(self) -> dict:
+        return dict(pairing=self.pairing, scaling=self.scaling, theta=self.theta,
+                    factor=self.factor, low=self.low, high=self.high, orig=self.orig)
+
+
+@dataclass(frozen=True)
+class QKNorm:
+    enabled: bool = False
+    eps: float = 1e-6
+    offset: int = 0
+    w_mean: float = 1.0
+    w_std: float = 0.1
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    lens: tuple            # ("fixed", L) or ("uniform", lo, hi): keys incl. the new one
+    capacity: int
+    k_dtype: int = BF16
+    v_dtype: int = BF16
+    rope: Rope = field(default_factory=Rope)
+    qk_norm: QKNorm = field(default_factory=QKNorm)
+    window: int = 0
+    softcap: float = 0.0
+    split_size: int = 512
+    seed: tuple = (0,)
+
+    @property
+    def group(self) -> int:
+        return self.n_heads // self.n_kv_heads
+
+    def seq_lens(self) -> np.ndarray:
+        if self.lens[0] == "fixed":
+            return np.full(self.batch, self.lens[1], dtype=np.int32)
+        _, lo, hi = self.lens
+        rng = np.random.default_rng([*self.seed, 0])
+        return rng.integers(lo, hi, endpoint=True, size=self.batch).astype(np.int32)
+
+    def visible(self, L: int) -> tuple[int, int]:
+        """[lo, L): keys attended by a sequence of L keys (window counts the new key)."""
+        lo = L - self.window if (self.window > 0 and L > self.window) else 0
+        return lo, L
+
+    def max_splits(self) -> int:
+        return int(-(-int(self.seq_lens().max()) // self.split_size))
+
+    def kv_row_bytes(self) -> int:
+        """Algorithmic bytes per visible (token, kv head): K row + V row (+ vq8 scale)."""
+        d = self.head_dim
+        b = d * ELEM_BYTES[self.k_dtype] + d * ELEM_BYTES[self.v_dtype]
+        return b + (4 if self.v_dtype == I8 else 0)
+
+    def kv_bytes(self) -> int:
+        """Algorithmic KV bytes one decode step reads (visible rows only)."""
+        rows = sum(hi - lo for lo, hi in (self.visible(int(L)) for L in self.seq_lens()))
+        return rows * self.n_kv_heads * self.kv_row_bytes()
+
+
+# The workloads of the decode step.  Names give the model shape they follow.
+WORKLOADS = {
+    # 128 cached tokens plus the new one at position 128; two splits of 65 keys.
+    "tiny": Workload("tiny", 1, 4, 2, 64, ("fixed", 129), 129, F32, F32,
+                     Rope(NEOX, PLAIN, 10000.0), split_size=65, seed=(1,)),
+    "llama3.2-1b": Workload("llama3.2-1b", 1, 32, 8, 64, ("fixed", 4096), 4096, BF16, BF16,
+                            Rope(INTERLEAVED, LLAMA3, 500000.0, 32.0, 1.0, 4.0, 8192),
+                            split_size=512, seed=(2,)),
+    "llama3.1-8b-ragged": Workload("llama3.1-8b-ragged", 32, 32, 8, 128, ("uniform", 512, 8192),
+                                   8192, BF16, BF16,
+                                   Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
+                                   split_size=512, seed=(3,)),
+    "qwen3-vq8": Workload("qwen3-vq8", 16, 32, 8, 128, ("fixed", 16384), 16384, BF16, I8,
+                          Rope(NEOX, PLAIN, 1000000.0),
+                          QKNorm(True, 1e-6, 0, 1.0, 0.1), split_size=512, seed=(4,)),
+    "gemma2-local": Workload("gemma2-local", 8, 16, 8, 256, ("fixed", 32768), 32768, BF16, BF16,
+                             Rope(NEOX, PLAIN, 10000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),
+                             window=4096, softcap=50.0, split_size=512, seed=(5, 0)),
+    "gemma2-global": Workload("gemma2-global", 8, 16, 8, 256, ("fixed", 32768), 32768, BF16, BF16,
+                              Rope(NEOX, PLAIN, 1000000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),
+                              window=0, softcap=50.0, split_size=512, seed=(5, 1)),
+    # The measured workload: B=32 sequences of 8192 keys, 32/8 heads, d=128, bf16 KV.
+    "llama3.1-8b-b32-ctx8k": Workload("llama3.1-8b-b32-ctx8k", 32, 32, 8, 128, ("fixed", 8192),
+                                      8192, BF16, BF16,
+                                      Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
+                                      split_size=512, seed=(6,)),
+}
+
+HEADLINE = "llama3.1-8b-b32-ctx8k"
+
+
+def shrink(w: Workload, **kw) -> Workload:
+    """A copy of w with some fields replaced (for small test variants)."""
+    return replace(w, **kw)
+
+
+@dataclass
+class Inputs:
+    workload: Workload
+    seq_lens: np.ndarray      # [B] int32, keys incl. the new one
+    positions: np.ndarray     # [B] int32, slot of the new token = L_b - 1
+    q_in: np.ndarray          # [B][H][d] f32
+    k_in: np.ndarray          # [B][Hkv][d] f32
+    v_in: np.ndarray          # [B][Hkv][d] f32
+    w_q: np.ndarray | None    # [d] f32
+    w_k: np.ndarray | None
+    cache_k: np.ndarray       # [B][Hkv][cap][d] f32 or uint16 (bf16 bits)
+    cache_v: np.ndarray       # [B][Hkv][cap][d] f32, uint16 or int8
+    v_scale: np.ndarray | None  # [B][Hkv][cap] f32 (vq8 only)
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _normal(seed, shape) -> np.ndarray:
+    out = np.empty(shape, dtype=np.float32)
+    np.random.default_rng(seed).standard_normal(dtype=np.float32, out=out)
+    return out
+
+
+def make_inputs(w: Workload, seq_lens=None) -> Inputs:
+    B, H, Hkv, d, cap = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.capacity
+    lens = w.seq_lens() if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
+    if lens.shape != (B,) or lens.min() < 1 or lens.max() > cap:
+        raise ValueError(f"{w.name}: seq_lens must be [{B}] within [1, {cap}]")
+    s = tuple(w.seed)
+    q_in = _normal([*s, 1], (B, H, d))
+    k_in = _normal([*s, 2], (B, Hkv, d))
+    v_in = _normal([*s, 3], (B, Hkv, d))
+    w_q = w_k = None
+    if w.qk_norm.enabled:
+        z = _normal([*s, 4], (2, d))
+        w_q = (w.qk_norm.w_mean + w.qk_norm.w_std * z[0]).astype(np.float32)
+        w_k = (w.qk_norm.w_mean + w.qk_norm.w_std * z[1]).astype(np.float32)
+
+    cache_k = np.empty((B, Hkv, cap, d), dtype=STORAGE[w.k_dtype])
+    cache_v = np.empty((B, Hkv, cap, d), dtype=STORAGE[w.v_dtype])
+    v_scale = np.empty((B, Hkv, cap), dtype=np.float32) if w.v_dtype == I8 else None
+
+    def fill(bu):
+        b, u = bu
+        L = int(lens[b])
+        lo, _ = w.visible(L)
+        n = max(0, (L - 1) - lo)          # cached visible rows: [lo, L - 1)
+        for arr, dt in ((cache_k, w.k_dtype), (cache_v, w.v_dtype)):
+            slab = arr[b, u]
+            if dt == F32:
+                slab[:lo] = np.nan
+                slab[lo + n:] = np.nan
+            elif dt == BF16:
+                slab[:lo] = BF16_NAN
+                slab[lo + n:] = BF16_NAN
+            else:
+                slab[:lo] = 0
+                slab[lo + n:] = 0
+        if n > 0:
+            zk = _normal([*s, 5, b, u], (n, d))
+            if w.k_dtype == F32:
+                cache_k[b, u, lo:lo + n] = zk
+            else:
+                cache_k[b, u, lo:lo + n] = zk.view(np.uint16)[:, 1::2]
+            if w.v_dtype == I8:
+                rng = np.random.default_rng([*s, 7, b, u])
+                z = rng.standard_normal((n, d), dtype=np.float32)
+                cache_v[b, u, lo:lo + n] = np.clip(np.rint(z * (127.0 / 2.8)), -127, 127)
+                v_scale[b, u, lo:lo + n] = (2.8 / 127.0) * (
+                    1.0 + 0.05 * rng.standard_normal(n, dtype=np.float32))
+            else:
+                zv = _normal([*s, 6, b, u], (n, d))
+                if w.v_dtype == F32:
+                    cache_v[b, u, lo:lo + n] = zv
+                else:
+                    cache_v[b, u, lo:lo + n] = zv.view(np.uint16)[:, 1::2]
+        if v_scale is not None:
+            v_scale[b, u, :lo] = np.nan
+            v_scale[b, u, lo + n:] = np.nan
+
+    jobs = [(b, u) for b in range(B) for u in range(Hkv)]
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, jobs))
+    return Inputs(w, lens, (lens - 1).astype(np.int32), q_in, k_in, v_in, w_q, w_k,
+                  cache_k, cache_v, v_scale)

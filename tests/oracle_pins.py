@@ -1,0 +1,646 @@
+"""Pins of the CPU oracle: facts the oracle must reproduce that do not come
+from the oracle itself -- closed forms, invariants, special cases that reduce
+to a textbook result, values the pages state, and brute force on tiny inputs.
+
+Every pin is a function ``pin_*(o)`` taking a loaded ``oracle.Oracle`` and
+raising AssertionError on a mismatch.  ``test_oracle_pins.py`` runs them on
+the oracle; ``test_oracle_teeth.py`` runs them on deliberately broken copies
+of the oracle and requires each copy to fail at least one pin.
+
+Page citations name the page title and section:
+  UAII      "Universal AI Inference - Hugging Face decoder completeness"
+  ALGENTA   "Algenta - Model support matrix"
+  FREETOKEN "FreeToken PR #722 - serve Llama and Mistral llama-arch GGUF"
+  LLAMAY    "llamay - Models and formats"
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(*seed):
+    return np.random.default_rng(list(seed))
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm  (UAII P1.1 Gemma RMSNorm (1+w); P1.2 Qwen3 QK-norm)
+# ---------------------------------------------------------------------------
+
+def pin_rms_norm_constant_vector(o):
+    """x = c * 1 has mean square c^2, so y_i = c / sqrt(c^2 + eps) * (w_i + offset)."""
+    d, eps = 64, 1e-6
+    w = _rng(11).standard_normal(d).astype(np.float32)
+    for c in (0.5, -3.0, 1e-3):
+        for off in (0, 1):
+            y = o.rms_norm(np.full(d, c), w, off, eps)
+            want = c / math.sqrt(c * c + eps) * (w.astype(np.float64) + off)
+            assert np.allclose(y, want, rtol=1e-14, atol=0), (c, off)
+
+
+def pin_rms_norm_hand_row(o):
+    """One hand-computed row per offset (UAII P1.1 asks for exactly this check):
+    x = (3, 4): mean square 12.5; with eps = 0.5, r = 1/sqrt(13) exactly."""
+    x = np.array([3.0, 4.0])
+    w = np.array([1.0, 2.0], dtype=np.float32)
+    r = 1.0 / math.sqrt(13.0)
+    y0 = o.rms_norm(x, w, 0, 0.5)
+    y1 = o.rms_norm(x, w, 1, 0.5)
+    assert np.allclose(y0, [3 * r, 8 * r], rtol=1e-15, atol=0), y0
+    assert np.allclose(y1, [6 * r, 12 * r], rtol=1e-15, atol=0), y1
+
+
+def pin_rms_norm_offset_identity(o):
+    """Gain (1 + w) with offset 1 equals gain w' = 1 + w with offset 0 (w on a
+    1/256 grid, so 1 + w is exact in f32 and the two agree to rounding)."""
+    d = 128
+    x = _rng(12).standard_normal(d)
+    w = (_rng(13).integers(-64, 64, d) / 256.0).astype(np.float32)
+    a = o.rms_norm(x, w, 1, 1e-6)
+    b = o.rms_norm(x, (1.0 + w).astype(np.float32), 0, 1e-6)
+    assert np.allclose(a, b, rtol=1e-15, atol=0)
+    c = o.rms_norm(x, w, 0, 1e-6)
+    assert not np.allclose(a, c, rtol=1e-3)
+
+
+def pin_rms_norm_unit_rms(o):
+    """With w = 1, offset 0 and tiny eps the output has unit root-mean-square
+    and is a positive multiple of x (scale invariance)."""
+    d = 256
+    x = 7.0 * _rng(14).standard_normal(d)
+    y = o.rms_norm(x, np.ones(d, np.float32), 0, 1e-12)
+    assert abs(math.sqrt(np.mean(y * y)) - 1.0) < 1e-12
+    y2 = o.rms_norm(3.0 * x, np.ones(d, np.float32), 0, 1e-12)
+    assert np.allclose(y, y2, rtol=1e-11, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# RoPE frequencies  (UAII P0.2 RoPE scaling; FREETOKEN Changes and Results)
+# ---------------------------------------------------------------------------
+
+def pin_freqs_plain_geometric(o):
+    """Plain frequencies theta^(-2i/d): g_0 = 1 and a constant ratio
+    theta^(-2/d) between neighbours, i.e. g_i = exp(-2i ln(theta) / d)."""
+    for d, theta in ((64, 1e4), (128, 5e5), (256, 1e6)):
+        g = o.rope_freqs(d, O.PLAIN, theta)
+        assert g[0] == 1.0
+        i = np.arange(d // 2)
+        assert np.allclose(g, np.exp(-2.0 * i * math.log(theta) / d), rtol=1e-13, atol=0)
+
+
+def pin_freqs_llama31_first8(o):
+    """'First 8 RoPE frequencies ... for Llama-3.1 8B config' (UAII P0.2 Tests):
+    the eight highest frequencies lie in the unscaled band, so with llama3
+    scaling (factor 8, low 1, high 4, original 8192) they equal the plain
+    theta^(-i/64), theta = 5e5."""
+    g = o.rope_freqs(128, O.LLAMA3, 5e5, 8.0, 1.0, 4.0, 8192)
+    plain = np.exp(-np.arange(8) * math.log(5e5) / 64.0)
+    assert np.allclose(g[:8], plain, rtol=1e-13, atol=0), g[:8]
+
+
+def pin_freqs_llama3_recovered_factor(o):
+    """FREETOKEN Changes/Results: the llama3 factor is the largest rope_freqs
+    divisor f_i / g_i; it equals 32 for Llama-3.2-1B (d 64) and 8 for
+    Llama-3.1-8B (d 128), both theta 5e5, low 1, high 4, original 8192.  The
+    smallest divisor is 1 and the divisors never decrease with i."""
+    for case in _golden("llama3_rope_factors.json")["cases"]:
+        d, theta, factor = case["head_dim"], case["theta"], case["factor"]
+        f = o.rope_freqs(d, O.PLAIN, theta)
+        g = o.rope_freqs(d, O.LLAMA3, theta, factor, case["low"], case["high"], case["original"])
+        div = f / g
+        assert abs(div.max() - case["recovered_factor"]) < 1e-12, (case, div.max())
+        assert abs(div.min() - 1.0) < 1e-15
+        assert np.all(np.diff(div) >= -1e-12)
+
+
+def pin_freqs_llama3_bands(o):
+    """Band membership by wavelength lambda = 2 pi / f: below original/high the
+    frequency is kept, above original/low it is divided by factor, between the
+    two the divisor lies strictly inside (1, factor)."""
+    for d, factor in ((64, 32.0), (128, 8.0), (256, 16.0)):
+        f = o.rope_freqs(d, O.PLAIN, 5e5)
+        g = o.rope_freqs(d, O.LLAMA3, 5e5, factor, 1.0, 4.0, 8192)
+        lam = 2 * math.pi / f
+        keep, scaled = lam < 8192 / 4.0, lam > 8192 / 1.0
+        assert np.array_equal(g[keep], f[keep])
+        assert np.allclose(g[scaled], f[scaled] / factor, rtol=1e-15, atol=0)
+        mid = ~(keep | scaled)
+        assert mid.any()
+        assert np.all((f[mid] / g[mid] > 1.0) & (f[mid] / g[mid] < factor))
+
+
+def pin_freqs_llama3_continuous(o):
+    """The scaled frequency is continuous in the wavelength: on a dense grid of
+    frequencies (huge head_dim, plain step r = theta^(2/d) - 1 ~ 4e-4)
+    neighbouring divisors differ by O(r) (the smooth band's slope is bounded by
+    a few r at factor 8), with no jump at either band edge."""
+    d = 1 << 16
+    f = o.rope_freqs(d, O.PLAIN, 5e5)
+    g = o.rope_freqs(d, O.LLAMA3, 5e5, 8.0, 1.0, 4.0, 8192)
+    div = f / g
+    step = f[0] / f[1]
+    assert np.all(div[1:] / div[:-1] <= 1.0 + 20.0 * (step - 1.0))
+    assert np.all(div[1:] / div[:-1] >= 1.0 - 1e-12)
+
+
+def pin_freqs_llama3_factor_one(o):
+    """factor = 1 reduces llama3 scaling to plain frequencies."""
+    f = o.rope_freqs(128, O.PLAIN, 5e5)
+    g = o.rope_freqs(128, O.LLAMA3, 5e5, 1.0, 1.0, 4.0, 8192)
+    assert np.allclose(f, g, rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# RoPE rotation  (UAII P0.2; LLAMAY Architectures; FREETOKEN Changes)
+# ---------------------------------------------------------------------------
+
+def pin_rope_unit_vectors(o):
+    """Closed forms with unit vectors: with d = 4 the frequencies are (1, theta^-1/2).
+    NeoX pairs (0, 2), (1, 3); interleaved pairs (0, 1), (2, 3).  The first
+    unit vector turns by angle p toward its partner: e_a -> cos p e_a + sin p e_b
+    (the rotation direction is a convention, fixed here by construction)."""
+    g = o.rope_freqs(4, O.PLAIN, 100.0)
+    assert np.allclose(g, [1.0, 0.1], rtol=1e-15, atol=0)
+    p = 3
+    c, s = math.cos(p), math.sin(p)
+    e0 = np.array([1.0, 0, 0, 0])
+    assert np.allclose(o.rope_apply(e0, O.NEOX, g, p), [c, 0, s, 0], atol=1e-15)
+    assert np.allclose(o.rope_apply(e0, O.INTERLEAVED, g, p), [c, s, 0, 0], atol=1e-15)
+    e3 = np.array([0, 0, 0, 1.0])
+    c1, s1 = math.cos(0.1 * p), math.sin(0.1 * p)
+    assert np.allclose(o.rope_apply(e3, O.NEOX, g, p), [0, -s1, 0, c1], atol=1e-15)
+    assert np.allclose(o.rope_apply(e3, O.INTERLEAVED, g, p), [0, 0, -s1, c1], atol=1e-15)
+
+
+def pin_rope_identity_at_zero(o):
+    x = _rng(21).standard_normal(128)
+    g = o.rope_freqs(128, O.LLAMA3, 5e5, 8.0, 1.0, 4.0, 8192)
+    for pairing in (O.NEOX, O.INTERLEAVED):
+        assert np.array_equal(o.rope_apply(x, pairing, g, 0), x)
+
+
+def _pairs(d, pairing):
+    if pairing == O.NEOX:
+        return [(i, i + d // 2) for i in range(d // 2)]
+    return [(2 * i, 2 * i + 1) for i in range(d // 2)]
+
+
+def pin_rope_pair_norms(o):
+    """Each rotated pair keeps its Euclidean norm."""
+    d = 64
+    x = _rng(22).standard_normal(d)
+    g = o.rope_freqs(d, O.PLAIN, 1e4)
+    for pairing in (O.NEOX, O.INTERLEAVED):
+        y = o.rope_apply(x, pairing, g, 4097)
+        for a, b in _pairs(d, pairing):
+            assert abs(math.hypot(y[a], y[b]) - math.hypot(x[a], x[b])) < 1e-13
+
+
+def pin_rope_relative_position(o):
+    """q.k after rotation depends only on the position difference."""
+    d = 128
+    q, k = _rng(23).standard_normal((2, d))
+    g = o.rope_freqs(d, O.LLAMA3, 5e5, 8.0, 1.0, 4.0, 8192)
+    for pairing in (O.NEOX, O.INTERLEAVED):
+        a = o.rope_apply(q, pairing, g, 100) @ o.rope_apply(k, pairing, g, 37)
+        b = o.rope_apply(q, pairing, g, 100 + 5000) @ o.rope_apply(k, pairing, g, 37 + 5000)
+        assert abs(a - b) < 1e-10 * max(1.0, abs(a)), (a, b)
+
+
+def pin_rope_group_law(o):
+    """Rotating by p1 then p2 equals rotating by p1 + p2."""
+    d = 64
+    x = _rng(24).standard_normal(d)
+    g = o.rope_freqs(d, O.PLAIN, 1e4)
+    for pairing in (O.NEOX, O.INTERLEAVED):
+        y = o.rope_apply(o.rope_apply(x, pairing, g, 123), pairing, g, 456)
+        assert np.allclose(y, o.rope_apply(x, pairing, g, 579), atol=1e-11)
+
+
+def pin_rope_neox_interleaved_permutation(o):
+    """FREETOKEN Changes: interleaved rotary equals NeoX rotary up to a
+    permutation of each head's rows.  With pi mapping NeoX index i -> 2i and
+    i + d/2 -> 2i + 1: RoPE_interleaved(pi x) = pi RoPE_neox(x)."""
+    d = 128
+    x = _rng(25).standard_normal(d)
+    g = o.rope_freqs(d, O.LLAMA3, 5e5, 8.0, 1.0, 4.0, 8192)
+    perm = np.empty(d, dtype=np.int64)
+    for i in range(d // 2):
+        perm[2 * i], perm[2 * i + 1] = i, i + d // 2   # (pi x)[2i] = x[i]
+    for p in (1, 777, 8191):
+        a = o.rope_apply(x[perm], O.INTERLEAVED, g, p)
+        b = o.rope_apply(x, O.NEOX, g, p)[perm]
+        assert np.allclose(a, b, atol=1e-14), p
+
+
+# ---------------------------------------------------------------------------
+# Storage codecs  (UAII P0.1 BF16; LLAMAY The KV cache, in three precisions)
+# ---------------------------------------------------------------------------
+
+def pin_bf16_crafted(o):
+    """Round to nearest, ties to even (values from tests/golden/bf16_rounding.json)."""
+    for case in _golden("bf16_rounding.json")["cases"]:
+        x = float.fromhex(case["x"])
+        got = o.bf16_from_double(x)
+        assert got == int(case["bits"], 16), (case, hex(got))
+
+
+def pin_bf16_roundtrip_exhaustive(o):
+    """Every non-NaN bf16 pattern decodes to a value that re-encodes to itself."""
+    enc, dec = o.lib.oracle_bf16_from_double, o.lib.oracle_bf16_to_double
+    for bits in range(0, 1 << 16, 1):
+        if (bits & 0x7F80) == 0x7F80 and (bits & 0x7F):
+            continue  # NaN payloads
+        assert enc(dec(bits)) == bits, hex(bits)
+
+
+def pin_bf16_nearest_brute_force(o):
+    """Random doubles: the encoded value is at least as close as its two
+    neighbours (brute force over the adjacent bf16 patterns)."""
+    xs = _rng(31).standard_normal(3000) * np.exp2(_rng(32).integers(-130, 120, 3000))
+    for x in xs:
+        bits = o.bf16_from_double(x)
+        v = o.bf16_to_double(bits)
+        for nb in (bits - 1, bits + 1):
+            if (nb & 0x7FFF) >= 0x7F80 or nb < 0 or nb > 0xFFFF:
+                continue
+            if (nb ^ bits) & 0x8000:
+                continue
+            assert abs(x - v) <= abs(x - o.bf16_to_double(nb)), (x, hex(bits))
+
+
+def pin_quantizer_crafted(o):
+    """vq8 quantiser: absmax 127 makes the scale exactly 1.0f, so codes are the
+    values rounded half away from zero (tests/golden/vq8_quantizer.json)."""
+    for case in _golden("vq8_quantizer.json")["cases"]:
+        v = np.array(case["v"], dtype=np.float32)
+        codes, scale = o.quantize_v(v)
+        assert scale == np.float32(case["scale"]), (case, scale)
+        assert codes.tolist() == case["codes"], (case, codes.tolist())
+
+
+def pin_quantizer_properties(o):
+    """Zero vector -> scale 0 and codes 0; the absmax element maps to +-127;
+    |code| <= 127; |v - code * scale| <= scale / 2 (plus one f32 rounding);
+    scale is the IEEE f32 quotient absmax / 127."""
+    codes, scale = o.quantize_v(np.zeros(64, np.float32))
+    assert scale == 0.0 and not codes.any()
+    rng = _rng(33)
+    for t in range(300):
+        d = (64, 128, 256)[t % 3]
+        v = (rng.standard_normal(d) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+        codes, scale = o.quantize_v(v)
+        a = np.max(np.abs(v))
+        assert scale == np.float32(a) / np.float32(127.0)
+        assert np.all(np.abs(codes.astype(np.int32)) <= 127)
+        assert abs(int(codes[np.argmax(np.abs(v))])) == 127
+        err = np.abs(v.astype(np.float64) - codes.astype(np.float64) * np.float64(scale))
+        assert np.all(err <= np.float64(scale) * 0.5 * (1 + 2.0 ** -21)), err.max() / scale
+
+
+# ---------------------------------------------------------------------------
+# Attention  (ALGENTA Structural fact requirements: GQA ratio, scale
+# 1/sqrt(head_dim); UAII P1.4 sliding window, logit softcap)
+# ---------------------------------------------------------------------------
+
+def _cache(B, Hkv, cap, d, seed, kdt=O.F32, vdt=O.F32):
+    rng = _rng(seed)
+    K = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    return K, V
+
+
+def pin_attention_zero_query_window(o):
+    """q = 0 gives uniform weights, so the output is the mean of the visible
+    values.  With position-coded values (v_j[0] = j) that mean is
+    (lo + L - 1) / 2, which fixes where the window starts: a window of W keys
+    counts the new key, lo = max(0, L - W)."""
+    B, H, Hkv, d, cap = 3, 4, 2, 64, 40
+    K, _ = _cache(B, Hkv, cap, d, 41)
+    V = np.zeros((B, Hkv, cap, d), np.float32)
+    V[..., 0] = np.arange(cap, dtype=np.float32)
+    V[..., 1] = 1.0
+    q = np.zeros((B, H, d))
+    lens = np.array([40, 17, 1], np.int32)
+    for W in (0, 1, 2, 7, 16, 17, 39, 40, 45):
+        out = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                       seq_lens=lens, window=W)
+        for b, L in enumerate(lens):
+            lo = L - W if (W > 0 and L > W) else 0
+            assert np.allclose(out[b, :, 0], (lo + L - 1) / 2.0, rtol=1e-14, atol=1e-14), (W, L)
+            assert np.allclose(out[b, :, 1], 1.0, rtol=1e-14)
+
+
+def pin_attention_constant_values(o):
+    """Constant values give that constant, with any window or softcap."""
+    B, H, Hkv, d, cap = 2, 8, 2, 64, 50
+    K, _ = _cache(B, Hkv, cap, d, 42)
+    c = _rng(43).standard_normal(d).astype(np.float32)
+    V = np.broadcast_to(c, (B, Hkv, cap, d)).copy()
+    q = 3.0 * _rng(44).standard_normal((B, H, d))
+    for W, cap_ in ((0, 0.0), (5, 0.0), (0, 2.0), (9, 50.0)):
+        out = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                       seq_lens=np.array([50, 23], np.int32), window=W, softcap=cap_)
+        assert np.allclose(out, np.broadcast_to(c, out.shape), rtol=1e-13, atol=1e-14)
+
+
+def pin_attention_two_keys_logistic(o):
+    """Two keys: the weights are the logistic function of the score gap.
+    q = a e_0, k_0 = x e_0, k_1 = 0 give scores a x / sqrt(d) and 0."""
+    d = 64
+    K = np.zeros((1, 1, 2, d), np.float32)
+    V = np.zeros((1, 1, 2, d), np.float32)
+    K[0, 0, 0, 0] = 1.5
+    V[0, 0, 0, :] = 2.0
+    V[0, 0, 1, :] = -1.0
+    for a in (0.0, 1.0, -4.0, 10.0):
+        q = np.zeros((1, 1, d))
+        q[0, 0, 0] = a
+        s = a * 1.5 / math.sqrt(d)
+        w0 = 1.0 / (1.0 + math.exp(-s))
+        out = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                       seq_lens=np.array([2], np.int32))
+        assert np.allclose(out[0, 0], 2.0 * w0 - (1.0 - w0), rtol=1e-14, atol=1e-15), a
+
+
+def pin_attention_window_limits(o):
+    """A window of at least L keys equals full attention; a window of 1 key
+    returns the newest value."""
+    B, H, Hkv, d, cap = 2, 4, 4, 64, 33
+    K, V = _cache(B, Hkv, cap, d, 45)
+    q = _rng(46).standard_normal((B, H, d))
+    lens = np.array([33, 12], np.int32)
+    full = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens)
+    for W in (33, 34, 1000):
+        w = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens,
+                     window=W)
+        assert np.array_equal(w, full)
+    one = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens,
+                   window=1)
+    for b, L in enumerate(lens):
+        for h in range(H):
+            assert np.allclose(one[b, h], V[b, h, L - 1], rtol=1e-15, atol=0)
+
+
+def pin_attention_softcap(o):
+    """Capped scores equal c * tanh(s / c) of the uncapped ones; a huge cap
+    leaves the scores unchanged to O(s^3 / c^2); the argmax is unchanged.
+    Query head 1 of 4 over 2 kv heads reads kv head 0 (consecutive groups)."""
+    H, Hkv, d, cap = 4, 2, 64, 30
+    K, _ = _cache(1, Hkv, cap, d, 47)
+    K[0, 1] = 0.0
+    q = 6.0 * _rng(48).standard_normal(d)
+    s0 = o.scores(q=q, cache_k=K, k_dtype=O.F32, n_heads=H, b=0, h=1, L=30)
+    assert np.allclose(s0, K[0, 0, :30].astype(np.float64) @ q / 8.0, rtol=1e-12, atol=1e-13)
+    for c in (0.5, 5.0, 50.0):
+        sc = o.scores(q=q, cache_k=K, k_dtype=O.F32, n_heads=H, b=0, h=1, L=30, softcap=c)
+        assert np.allclose(sc, c * np.tanh(s0 / c), rtol=1e-14, atol=1e-15)
+        assert np.all(np.abs(sc) <= c)
+        assert np.argmax(sc) == np.argmax(s0)
+    big = o.scores(q=q, cache_k=K, k_dtype=O.F32, n_heads=H, b=0, h=1, L=30, softcap=1e6)
+    assert np.all(np.abs(big - s0) <= np.abs(s0) ** 3 / 3e12 + 1e-12)
+    win = o.scores(q=q, cache_k=K, k_dtype=O.F32, n_heads=H, b=0, h=1, L=30, window=4)
+    assert np.all(win[:26] == -np.inf) and np.array_equal(win[26:], s0[26:])
+
+
+def pin_attention_gqa_expansion(o):
+    """GQA equals multi-head attention on keys and values repeated G times per
+    kv head, with consecutive query heads sharing a kv head (h -> h // G);
+    kv-head-constant values expose the map directly."""
+    B, H, Hkv, d, cap = 2, 8, 2, 64, 20
+    G = H // Hkv
+    K, V = _cache(B, Hkv, cap, d, 49)
+    q = _rng(50).standard_normal((B, H, d))
+    lens = np.array([20, 9], np.int32)
+    gqa = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens)
+    Ke = np.ascontiguousarray(np.repeat(K, G, axis=1))
+    Ve = np.ascontiguousarray(np.repeat(V, G, axis=1))
+    mha = o.decode(q=q, cache_k=Ke, cache_v=Ve, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens)
+    assert np.array_equal(gqa, mha)
+    Vc = np.zeros_like(V)
+    for u in range(Hkv):
+        Vc[:, u] = u + 1
+    out = o.decode(q=q, cache_k=K, cache_v=Vc, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens)
+    for h in range(H):
+        assert np.allclose(out[:, h], h // G + 1, rtol=1e-14)
+
+
+def pin_attention_dominant_key(o):
+    """q = alpha k_j with large alpha puts (almost) all weight on key j."""
+    d = 128
+    K, V = _cache(1, 1, 64, d, 51)
+    j = 37
+    q = (60.0 * K[0, 0, j] / np.linalg.norm(K[0, 0, j])).reshape(1, 1, d)
+    out = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                   seq_lens=np.array([64], np.int32))
+    assert np.allclose(out[0, 0], V[0, 0, j], atol=1e-6)
+
+
+def pin_attention_brute_force(o):
+    """Tiny shapes against a second formulation: long double, scores by
+    explicit loops, no max subtraction, weights normalised at the end."""
+    rng = _rng(52)
+    for t in range(6):
+        B, Hkv, G, d = 2, 2, (1, 2, 4)[t % 3], (64, 128)[t % 2]
+        H, cap = Hkv * G, 24
+        K = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+        V = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+        q = rng.standard_normal((B, H, d))
+        lens = rng.integers(1, cap + 1, B).astype(np.int32)
+        W = [0, 3, 30][t % 3]
+        cap_c = [0.0, 0.0, 7.0][t % 3]
+        out = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens,
+                       window=W, softcap=cap_c)
+        for b in range(B):
+            L = int(lens[b])
+            for h in range(H):
+                u = h // G
+                num = np.zeros(d, dtype=np.longdouble)
+                den = np.longdouble(0)
+                for j in range(L):
+                    if W > 0 and j < L - W:
+                        continue
+                    s = np.longdouble(0)
+                    for i in range(d):
+                        s += np.longdouble(q[b, h, i]) * np.longdouble(K[b, u, j, i])
+                    s /= np.sqrt(np.longdouble(d))
+                    if cap_c > 0:
+                        s = np.longdouble(cap_c) * np.tanh(s / np.longdouble(cap_c))
+                    e = np.exp(s)
+                    den += e
+                    num += e * V[b, u, j].astype(np.longdouble)
+                ref = (num / den).astype(np.float64)
+                assert np.allclose(out[b, h], ref, rtol=1e-12, atol=1e-13), (t, b, h)
+
+
+def pin_attention_storage_formats(o):
+    """bf16 caches give the same result as f32 caches holding the decoded
+    bf16 values; vq8 values give the result of f32 values code * scale."""
+    B, H, Hkv, d, cap = 2, 4, 2, 64, 30
+    rng = _rng(53)
+    Kf = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    Vf = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    Kb = (Kf.view(np.uint32) >> 16).astype(np.uint16)
+    Vb = (Vf.view(np.uint32) >> 16).astype(np.uint16)
+    Kbf = (Kb.astype(np.uint32) << 16).view(np.float32)
+    Vbf = (Vb.astype(np.uint32) << 16).view(np.float32)
+    q = rng.standard_normal((B, H, d))
+    lens = np.array([30, 11], np.int32)
+    a = o.decode(q=q, cache_k=Kb, cache_v=Vb, k_dtype=O.BF16, v_dtype=O.BF16, seq_lens=lens)
+    b = o.decode(q=q, cache_k=Kbf, cache_v=Vbf, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens)
+    assert np.array_equal(a, b)
+    codes = rng.integers(-127, 128, (B, Hkv, cap, d)).astype(np.int8)
+    scale = np.exp2(-rng.integers(4, 10, (B, Hkv, cap))).astype(np.float32)
+    deq = codes.astype(np.float32) * scale[..., None]      # exact: power-of-two scales
+    c = o.decode(q=q, cache_k=Kb, cache_v=codes, v_scale=scale, k_dtype=O.BF16, v_dtype=O.I8,
+                 seq_lens=lens)
+    e = o.decode(q=q, cache_k=Kb, cache_v=deq, k_dtype=O.BF16, v_dtype=O.F32, seq_lens=lens)
+    assert np.array_equal(c, e)
+
+
+# ---------------------------------------------------------------------------
+# Split-K flash decoding  (ALGENTA Kernel path capabilities: split-K decode
+# partials; Conformance CLI: decode_attn=splitk_flash_decoding)
+# ---------------------------------------------------------------------------
+
+def pin_split_combine_equals_single_pass(o):
+    """For any split size, combining the per-split partials with their
+    log-sum-exp weights reproduces single-pass attention; empty splits
+    (before the window) have lse = -inf and drop out."""
+    H, Hkv, d, cap = 4, 2, 64, 77
+    K, V = _cache(1, Hkv, cap, d, 54)
+    q = 2.0 * _rng(55).standard_normal((1, H, d))
+    L = 77
+    for W, cap_c in ((0, 0.0), (20, 0.0), (0, 30.0), (33, 5.0)):
+        single = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                          seq_lens=np.array([L], np.int32), window=W, softcap=cap_c)
+        for S in (1, 2, 3, 64, L - 1, L, 2 * L):
+            for h in (0, 3):
+                n = -(-L // S)
+                os_, ls = np.zeros((n, d)), np.zeros(n)
+                total = 0
+                for sg in range(n):
+                    os_[sg], ls[sg], k = o.split_partial(
+                        q_bh=q[0, h], cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                        n_heads=H, b=0, h=h, L=L, window=W, softcap=cap_c, split_size=S,
+                        sigma=sg)
+                    total += k
+                    assert (k == 0) == (ls[sg] == -math.inf)
+                lo = L - W if (W > 0 and L > W) else 0
+                assert total == L - lo
+                out, used = o.combine(os_, ls)
+                assert used == int(np.sum(ls > -math.inf))
+                assert np.allclose(out, single[0, h], rtol=1e-12, atol=1e-13), (W, S, h)
+
+
+def pin_split_partial_is_local_attention(o):
+    """A split's partial is softmax attention over its own keys, and its lse
+    is the log of the sum of e^s over those keys."""
+    H, Hkv, d, cap = 2, 1, 64, 40
+    K, V = _cache(1, Hkv, cap, d, 56)
+    q = _rng(57).standard_normal(d)
+    s = o.scores(q=q, cache_k=K, k_dtype=O.F32, n_heads=H, b=0, h=0, L=40)
+    o1, lse, n = o.split_partial(q_bh=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                                 n_heads=H, b=0, h=0, L=40, window=0, softcap=0.0,
+                                 split_size=16, sigma=1)
+    assert n == 16
+    assert abs(lse - math.log(np.sum(np.exp(s[16:32])))) < 1e-12
+    w = np.exp(s[16:32] - lse)
+    assert np.allclose(o1, w @ V[0, 0, 16:32].astype(np.float64), rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Producer  (UAII P1.2: norm before RoPE; P1.3: absolute positions)
+# ---------------------------------------------------------------------------
+
+def pin_produce_writes_one_slot(o):
+    """The producer writes exactly slot positions[b] of each (b, kv head)."""
+    B, H, Hkv, d, cap = 3, 4, 2, 64, 16
+    rng = _rng(61)
+    qi, ki, vi = (rng.standard_normal(s).astype(np.float32)
+                  for s in ((B, H, d), (B, Hkv, d), (B, Hkv, d)))
+    pos = np.array([0, 7, 15], np.int32)
+    for kdt, vdt in ((O.F32, O.F32), (O.BF16, O.BF16), (O.BF16, O.I8)):
+        ck = np.full((B, Hkv, cap, d), 0x55, dtype={O.F32: np.float32, O.BF16: np.uint16}[kdt])
+        cv = np.full((B, Hkv, cap, d), 0x55,
+                     dtype={O.F32: np.float32, O.BF16: np.uint16, O.I8: np.int8}[vdt])
+        vs = np.full((B, Hkv, cap), 7.0, np.float32)
+        ck0, cv0, vs0 = ck.copy(), cv.copy(), vs.copy()
+        o.kv_produce(rope=dict(pairing=O.NEOX, scaling=O.PLAIN, theta=1e4), norm=None,
+                     q_in=qi, k_in=ki, v_in=vi, positions=pos, k_dtype=kdt, v_dtype=vdt,
+                     cache_k=ck, cache_v=cv, v_scale=vs)
+        mask = np.zeros((B, Hkv, cap), bool)
+        for b in range(B):
+            mask[b, :, pos[b]] = True
+        assert np.array_equal(ck[~mask], ck0[~mask]) and np.array_equal(cv[~mask], cv0[~mask])
+        assert np.array_equal(vs[~mask], vs0[~mask])
+        assert not np.array_equal(ck[mask], ck0[mask])
+
+
+def pin_produce_position_zero(o):
+    """At position 0 RoPE is the identity: without QK-norm q' = q and the
+    stored key and value are the inputs in the cache's format (f32 exact;
+    vq8 codes and scale of the value quantiser)."""
+    B, H, Hkv, d, cap = 2, 4, 2, 128, 4
+    rng = _rng(62)
+    qi = rng.standard_normal((B, H, d)).astype(np.float32)
+    ki = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+    vi = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+    ck = np.zeros((B, Hkv, cap, d), np.float32)
+    cv = np.zeros((B, Hkv, cap, d), np.int8)
+    vs = np.zeros((B, Hkv, cap), np.float32)
+    qo = o.kv_produce(rope=dict(pairing=O.INTERLEAVED, scaling=O.LLAMA3, theta=5e5, factor=8.0),
+                      norm=None, q_in=qi, k_in=ki, v_in=vi, positions=np.zeros(B, np.int32),
+                      k_dtype=O.F32, v_dtype=O.I8, cache_k=ck, cache_v=cv, v_scale=vs)
+    assert np.array_equal(qo, qi.astype(np.float64))
+    assert np.array_equal(ck[:, :, 0], ki)
+    for b in range(B):
+        for u in range(Hkv):
+            c, s = o.quantize_v(vi[b, u])
+            assert np.array_equal(cv[b, u, 0], c) and vs[b, u, 0] == s
+
+
+def pin_produce_norm_before_rope(o):
+    """The producer normalises, then rotates: with a non-uniform gain the two
+    orders differ, and the output matches norm-then-rope."""
+    d = 64
+    rng = _rng(63)
+    qi = rng.standard_normal((1, 1, d)).astype(np.float32)
+    ki = rng.standard_normal((1, 1, d)).astype(np.float32)
+    w = (1.0 + 0.5 * rng.standard_normal(d)).astype(np.float32)
+    g = o.rope_freqs(d, O.PLAIN, 1e4)
+    ck = np.zeros((1, 1, 8, d), np.float32)
+    cv = np.zeros((1, 1, 8, d), np.float32)
+    qo = o.kv_produce(rope=dict(pairing=O.NEOX, scaling=O.PLAIN, theta=1e4),
+                      norm=dict(enabled=True, eps=1e-6, offset=0, w_q=w, w_k=w),
+                      q_in=qi, k_in=ki, v_in=ki, positions=np.array([5], np.int32),
+                      k_dtype=O.F32, v_dtype=O.F32, cache_k=ck, cache_v=cv)
+    x = qi[0, 0].astype(np.float64)
+    # Norm-then-rope written with numpy (unit rms, then gain, then rotation by
+    # the oracle's own pieces is avoided: rotation here uses explicit pairs).
+    r = 1.0 / math.sqrt(np.mean(x * x) + 1e-6)
+    y = x * r * w
+    z = y.copy()
+    for i in range(d // 2):
+        t = 5 * g[i]
+        z[i] = y[i] * math.cos(t) - y[i + d // 2] * math.sin(t)
+        z[i + d // 2] = y[i] * math.sin(t) + y[i + d // 2] * math.cos(t)
+    assert np.allclose(qo[0, 0], z, rtol=1e-13, atol=1e-14)
+    xr = o.rope_apply(x, O.NEOX, g, 5)
+    other = xr / math.sqrt(np.mean(xr * xr) + 1e-6) * w
+    assert not np.allclose(qo[0, 0], other, rtol=1e-6)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,68 @@
+"""Negative controls: each plausible mistake planted in a copy of the oracle
+(on the CPU) must make at least one pin fail, so no pin set is vacuous.
+The one-bit value cache follows the llamay page's 'teeth' row
+('llamay - Models and formats', The bound, and why it is the one it is)."""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+from oracle import build as obuild
+
+SRC = open(obuild.SOURCE).read()
+
+# (name, text in oracle.c, replacement).  Each text occurs exactly once.
+MUTANTS = [
+    ("window_off_by_one", "? L - W : 0;", "? L - W + 1 : 0;"),
+    ("window_excludes_current", "? L - W : 0;", "? L - W - 1 : 0;"),
+    ("pairing_swapped_neox",
+     "int a = (pairing == OR_NEOX) ? i : 2 * i;\n        int b = (pairing == OR_NEOX) ? i + d / 2 : 2 * i + 1;",
+     "int a = (pairing != OR_NEOX) ? i : 2 * i;\n        int b = (pairing != OR_NEOX) ? i + d / 2 : 2 * i + 1;"),
+    ("rotation_sign", "x[a] = xa * c - xb * s;\n        x[b] = xa * s + xb * c;",
+     "x[a] = xa * c + xb * s;\n        x[b] = -xa * s + xb * c;"),
+    ("angle_uses_index", "double t = (double)pos * g[i];", "double t = (double)pos * g[0];"),
+    ("freq_exponent", "pow(theta, -2.0 * (double)i / (double)d)", "pow(theta, -(double)i / (double)d)"),
+    ("llama3_smooth_dropped", "g[i] = (1.0 - mu) * f / factor + mu * f;", "g[i] = f / factor;"),
+    ("llama3_mu_swapped", "g[i] = (1.0 - mu) * f / factor + mu * f;", "g[i] = mu * f / factor + (1.0 - mu) * f;"),
+    ("gqa_modulo_map", "int u = h / G;\n    int64_t slab = (int64_t)b * Hkv + u;\n    int64_t lo = visible_lo(L, W);\n    if (j0",
+     "int u = h % Hkv;\n    int64_t slab = (int64_t)b * Hkv + u;\n    int64_t lo = visible_lo(L, W);\n    if (j0"),
+    ("gqa_modulo_map_scores", "int u = h / G;\n    int64_t slab = (int64_t)b * Hkv + u;\n    int64_t lo = visible_lo(L, W);\n    double scale",
+     "int u = h % Hkv;\n    int64_t slab = (int64_t)b * Hkv + u;\n    int64_t lo = visible_lo(L, W);\n    double scale"),
+    ("one_bit_values", "float scale = a / 127.0f;", "float scale = a / 1.0f;"),
+    ("quantizer_half_even", "float r = roundf(t);", "float r = nearbyintf(t);"),
+    ("norm_eps_outside", "double r = 1.0 / sqrt(ss / (double)d + eps);", "double r = 1.0 / sqrt(ss / (double)d) + eps;"),
+    ("norm_offset_ignored", "y[i] = x[i] * r * ((double)w[i] + (double)offset);", "y[i] = x[i] * r * (double)w[i];"),
+    ("norm_sum_not_mean", "double r = 1.0 / sqrt(ss / (double)d + eps);", "double r = 1.0 / sqrt(ss + eps);"),
+    ("bf16_truncates", "double r = nearbyint(x / quantum) * quantum;", "double r = trunc(x / quantum) * quantum;"),
+    ("softcap_unscaled", "s = softcap * tanh(s / softcap);", "s = softcap * tanh(s);"),
+    ("score_unscaled", "double s = scale * acc;", "double s = acc;"),
+    ("softmax_unnormalised", "    for (int i = 0; i < d; ++i)\n        out[i] /= l;\n", "\n"),
+    ("combine_unnormalised", "    for (int i = 0; i < d; ++i)\n        out[i] /= den;\n", "\n"),
+    ("lse_missing_max", "*lse = m + log(l);", "*lse = log(l);"),
+    ("vq8_scale_ignored", "return (double)((const int8_t *)base)[idx] * (double)scale[row];",
+     "return (double)((const int8_t *)base)[idx];"),
+    ("produce_norm_after_rope",
+     "    if (norm_enabled)\n        oracle_rms_norm(x, d, w, offset, eps, out);\n    else\n        memcpy(out, x, sizeof(double) * (size_t)d);\n    oracle_rope_apply(out, d, pairing, g, pos);",
+     "    oracle_rope_apply(x, d, pairing, g, pos);\n    if (norm_enabled)\n        oracle_rms_norm(x, d, w, offset, eps, out);\n    else\n        memcpy(out, x, sizeof(double) * (size_t)d);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_fails_a_pin(tmp_path, name, old, new):
+    assert SRC.count(old) == 1, f"{name}: anchor text not found exactly once in oracle.c"
+    src = tmp_path / f"oracle_{name}.c"
+    src.write_text(SRC.replace(old, new))
+    lib = obuild.build(str(src), str(tmp_path / f"lib_{name}.so"), quiet=True)
+    mutant = oracle.Oracle(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except AssertionError:
+            failed.append(pin.__name__)
+            break
+        except (ValueError, FloatingPointError, OverflowError):
+            failed.append(pin.__name__)
+            break
+    assert failed, f"mutant {name} passes every pin"
