@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of one GQA decode step on one MI355X.
+
+A step is the whole hot path over one batch: KV producer (norm, RoPE,
+append), split-K decode partials, log-sum-exp combine, all through the C ABI
+on the current stream.  Inputs are seeded synthetic caches already resident
+in HBM when the timed region starts.
+
+Prints ONE JSON line:
+  value          KV GB/s of the whole step (algorithmic visible-KV bytes / step time)
+  roofline       the dominant kernel (decode partials): algorithmic bytes per launch
+                 / its mean launch time, timed with HIP events on the launch stream,
+                 against the 8 TB/s HBM peak; traffic from rocprofv3 counters when
+                 they were taken on the current kernel source, else null
+  cpu_baseline   the CPU oracle (scalar double precision) on a bounded sample of
+                 the same workload, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV GB/s & % of HBM peak; seq-steps/s at B=32, ctx 8K, d128"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "gqa_decode_attention_kv_amd", "csrc", "decode_partial.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per partial-kernel launch from the committed counter runs, if
+    they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(workload)
+    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inputs, min_seconds: float = 10.0, max_rounds: int = 8) -> dict:
+    """Time the oracle (produce + single-pass attention of every head) on whole
+    sequences of the workload, one thread per sequence group, until at least
+    min_seconds of wall time (or max_rounds sequences groups) have run."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    w = inputs.workload
+    o = oracle.load()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+    norm = None
+    if w.qk_norm.enabled:
+        norm = dict(enabled=True, eps=w.qk_norm.eps, offset=w.qk_norm.offset, w_q=inputs.w_q,
+                    w_k=inputs.w_k)
+    ck, cv = inputs.cache_k, inputs.cache_v
+    vs = inputs.v_scale
+    t0 = time.perf_counter()
+    q = o.kv_produce(rope=w.rope.as_dict(), norm=norm, q_in=inputs.q_in, k_in=inputs.k_in,
+                     v_in=inputs.v_in, positions=inputs.positions, k_dtype=w.k_dtype,
+                     v_dtype=w.v_dtype, cache_k=ck, cache_v=cv, v_scale=vs)
+    t_produce = time.perf_counter() - t0
+    seqs_done, kv_bytes, elapsed = 0, 0, t_produce
+    order = list(range(w.batch))
+    per_round = min(w.batch, threads)
+    rounds = 0
+    while rounds < max_rounds and (elapsed < min_seconds or rounds == 0):
+        seqs = [order[(rounds * per_round + i) % w.batch] for i in range(per_round)]
+
+        def one(b):
+            pairs = [(b, h) for h in range(w.n_heads)]
+            o.decode(q=q, cache_k=ck, cache_v=cv, v_scale=vs, k_dtype=w.k_dtype,
+                     v_dtype=w.v_dtype, seq_lens=inputs.seq_lens, window=w.window,
+                     softcap=w.softcap, pairs=pairs)
+
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(per_round) as ex:
+            list(ex.map(one, seqs))
+        elapsed += time.perf_counter() - t0
+        for b in seqs:
+            lo, hi = w.visible(int(inputs.seq_lens[b]))
+            kv_bytes += (hi - lo) * w.n_kv_heads * w.kv_row_bytes()
+        seqs_done += len(seqs)
+        rounds += 1
+    gbs = kv_bytes / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": per_round, "kind": "oracle",
+            "sample": (f"{seqs_done} sequence-steps of {w.name} (produce for all {w.batch} sequences, "
+                       f"then single-pass double-precision attention of all {w.n_heads} heads of "
+                       f"each sampled sequence), {elapsed:.1f} s wall on {per_round} threads"),
+            "seq_steps_per_s": round(seqs_done / elapsed, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: the B=32 ctx-8K one)")
+    ap.add_argument("--split-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this decode path runs on one GPU "
+              "(the kernel on one GPU's share); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from gqa_decode_attention_kv_amd import workloads as W
+    from gqa_decode_attention_kv_amd.step import DeviceStep
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    name = args.workload or W.HEADLINE
+    w = W.WORKLOADS[name]
+    t_gen = time.perf_counter()
+    inputs = W.make_inputs(w)
+    t_gen = time.perf_counter() - t_gen
+    print(f"bench: {name} inputs generated in {t_gen:.1f} s", file=sys.stderr, flush=True)
+    st = DeviceStep(inputs, split_size=args.split_size)
+    kv_bytes = w.kv_bytes()
+
+    if args.copy_probe:
+        n = 1 << 28  # 1 GiB of f32
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: copy probe moved {n * 4} bytes each way", file=sys.stderr, flush=True)
+        del src, dst
+
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        st.produce()
+        ev[i][0].record()
+        st.attn()
+        ev[i][1].record()
+        st.combine()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / K
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_mean = float(np.mean(attn_ms))
+    assert torch.isfinite(st.out).all().item(), "non-finite output"
+
+    step_gbs = kv_bytes / (ms_step * 1e-3) / 1e9
+    attn_gbs = kv_bytes / (attn_mean * 1e-3) / 1e9
+    traffic = measured_traffic(name)
+    result = {
+        "metric": METRIC,
+        "value": round(step_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": w.batch, "ctx": int(inputs.seq_lens.max()),
+                   "n_heads": w.n_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "kv_cache": {0: "f32", 1: "bf16", 2: "int8"}[w.k_dtype] + "/" +
+                   {0: "f32", 1: "bf16", 2: "int8(vq8)"}[w.v_dtype],
+                   "split_size": st.split_size, "window": w.window, "softcap": w.softcap,
+                   "parallelism": "single-gpu"},
+        "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "attn_partial_ms": round(attn_mean, 5),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {
+            "kernel": "decode_partial_kernel",
+            "bound": "hbm",
+            "achieved": round(attn_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "kernel_source_sha256_16": kernel_source_hash(),
+        },
+    }
+    if not args.no_cpu_baseline:
+        del st
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(inputs)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

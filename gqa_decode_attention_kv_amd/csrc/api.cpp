@@ -1,0 +1,314 @@
+// C-ABI entry points of the GQA decode-step library: argument validation
+// (fail closed, typed messages), the per-sequence work table, and the
+// kernel launches on the caller's stream.  See include/uaii_decode.h for
+// the contract of each call.
+//
+// Refusal style follows "Algenta - Model support matrix" (Conformance CLI:
+// a refusal names the exact fact, its value and the supported range) and
+// "Universal AI Inference - Hugging Face decoder completeness" (section 6:
+// every message says what failed and what to do; support contract: fail
+// closed with InvalidArgument / NotImplemented).
+#include "uaii_decode.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+uaii_status fail(uaii_status st, const char* fn, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = std::string(fn) + ": " + buf;
+  return st;
+}
+
+#define REQUIRE(cond, st, ...)                    \
+  do {                                            \
+    if (!(cond)) return fail((st), fn, __VA_ARGS__); \
+  } while (0)
+
+constexpr uaii_status kInvalid = UAII_ERR_INVALID_ARGUMENT;
+constexpr uaii_status kNotImpl = UAII_ERR_NOT_IMPLEMENTED;
+constexpr int32_t kMaxCapacity = 1 << 30;
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+uaii_status check_device_ptr(const char* fn, const char* name, const void* p, uintptr_t align) {
+  REQUIRE(p != nullptr, kInvalid, "%s is NULL; pass a device buffer", name);
+  REQUIRE(aligned(p, align), kInvalid, "%s=%p is not %u-byte aligned; allocate it with the device allocator",
+          name, p, static_cast<unsigned>(align));
+  return UAII_OK;
+}
+
+#define CHECK_PTR(name, p, align)                                        \
+  do {                                                                   \
+    uaii_status st_ = check_device_ptr(fn, (name), (p), (align));        \
+    if (st_ != UAII_OK) return st_;                                      \
+  } while (0)
+
+uaii_status check_shape(const char* fn, const uaii_attn_shape* s) {
+  REQUIRE(s != nullptr, kInvalid, "shape is NULL; pass a uaii_attn_shape");
+  REQUIRE(s->batch >= 1, kInvalid, "batch=%d is invalid (must be >= 1)", s->batch);
+  REQUIRE(s->batch <= uaii::kMaxBatch, kNotImpl,
+          "batch=%d is not supported (supported: 1..%d); split the batch into calls of at most %d sequences",
+          s->batch, uaii::kMaxBatch, uaii::kMaxBatch);
+  REQUIRE(s->n_heads >= 1, kInvalid, "n_heads=%d is invalid (must be >= 1)", s->n_heads);
+  REQUIRE(s->n_kv_heads >= 1, kInvalid, "n_kv_heads=%d is invalid (must be >= 1)", s->n_kv_heads);
+  REQUIRE(s->n_heads <= 65535, kNotImpl, "n_heads=%d is not supported (supported: 1..65535)",
+          s->n_heads);
+  REQUIRE(s->n_heads % s->n_kv_heads == 0, kInvalid,
+          "n_heads=%d is not an exact multiple of n_kv_heads=%d (the GQA ratio must be integral)",
+          s->n_heads, s->n_kv_heads);
+  REQUIRE(s->head_dim >= 1, kInvalid, "head_dim=%d is invalid (must be >= 1)", s->head_dim);
+  REQUIRE(s->head_dim == 64 || s->head_dim == 128 || s->head_dim == 256, kNotImpl,
+          "head_dim=%d is not supported (supported: {64, 128, 256})", s->head_dim);
+  const int g = s->n_heads / s->n_kv_heads;
+  REQUIRE(g == 1 || g == 2 || g == 4 || g == 8, kNotImpl,
+          "GQA ratio n_heads/n_kv_heads=%d is not supported (supported: {1, 2, 4, 8})", g);
+  return UAII_OK;
+}
+
+uaii_status check_cache(const char* fn, const uaii_kv_cache* c) {
+  REQUIRE(c != nullptr, kInvalid, "cache is NULL; pass a uaii_kv_cache");
+  REQUIRE(c->k_dtype != UAII_I8, kNotImpl,
+          "k_dtype=int8 (a q8 cache, int8 keys) is not supported; keys stay exact: use k_dtype f32 or "
+          "bf16, with v_dtype int8 for the vq8 cache");
+  REQUIRE(c->k_dtype == UAII_F32 || c->k_dtype == UAII_BF16, kInvalid,
+          "k_dtype=%d is not a dtype code (f32=0, bf16=1)", c->k_dtype);
+  REQUIRE(c->v_dtype == UAII_F32 || c->v_dtype == UAII_BF16 || c->v_dtype == UAII_I8, kInvalid,
+          "v_dtype=%d is not a dtype code (f32=0, bf16=1, int8=2)", c->v_dtype);
+  REQUIRE(c->capacity >= 1, kInvalid, "capacity=%d is invalid (must be >= 1)", c->capacity);
+  REQUIRE(c->capacity <= kMaxCapacity, kNotImpl, "capacity=%d is not supported (supported: 1..%d)",
+          c->capacity, kMaxCapacity);
+  CHECK_PTR("cache.k", c->k, 16);
+  CHECK_PTR("cache.v", c->v, 16);
+  if (c->v_dtype == UAII_I8) {
+    REQUIRE(c->v_scale != nullptr, kInvalid,
+            "cache.v_scale is NULL but v_dtype is int8 (vq8 needs one f32 scale per token per kv head)");
+    CHECK_PTR("cache.v_scale", c->v_scale, 4);
+  }
+  return UAII_OK;
+}
+
+bool finite_pos(double x) { return std::isfinite(x) && x > 0.0; }
+
+// Visible keys [lo, L) and the splits [first, last] that intersect them.
+void build_table(int B, const int32_t* lens, int32_t window, int32_t split, uaii::SeqTable* t) {
+  std::memset(t, 0, sizeof *t);
+  int32_t prefix = 0;
+  for (int b = 0; b < B; ++b) {
+    const int32_t L = lens[b];
+    const int32_t lo = (window > 0 && L > window) ? L - window : 0;
+    const int32_t first = lo / split, last = (L - 1) / split;
+    t->len[b] = L;
+    t->lo[b] = lo;
+    t->first_split[b] = first;
+    t->work_prefix[b] = prefix;
+    prefix += last - first + 1;
+  }
+  t->work_prefix[B] = prefix;
+  t->n_seq = B;
+}
+
+uaii_status device_status(const char* fn, hipError_t e) {
+  if (e == hipSuccess) return UAII_OK;
+  return fail(UAII_ERR_DEVICE, fn, "HIP error %d (%s) while enqueuing the kernel", static_cast<int>(e),
+              hipGetErrorString(e));
+}
+
+uaii_status check_lens(const char* fn, const uaii_attn_shape* s, const int32_t* seq_lens, int32_t cap,
+                       int32_t split_size, int32_t max_splits, int32_t window) {
+  REQUIRE(seq_lens != nullptr, kInvalid, "seq_lens is NULL; pass a host array of batch=%d lengths",
+          s->batch);
+  REQUIRE(window >= 0, kInvalid, "window=%d is invalid (0 = no window, W > 0 keeps the last W keys)",
+          window);
+  REQUIRE(split_size >= 1, kInvalid, "split_size=%d is invalid (must be >= 1)", split_size);
+  int32_t max_len = 0;
+  for (int b = 0; b < s->batch; ++b) {
+    REQUIRE(seq_lens[b] >= 1 && seq_lens[b] <= cap, kInvalid,
+            "seq_lens[%d]=%d is outside [1, %d] (keys including the new token, at most the capacity)", b,
+            seq_lens[b], cap);
+    if (seq_lens[b] > max_len) max_len = seq_lens[b];
+  }
+  const int64_t need = (static_cast<int64_t>(max_len) + split_size - 1) / split_size;
+  REQUIRE(max_splits >= need, kInvalid,
+          "max_splits=%d is too small: seq_lens up to %d with split_size=%d need %lld splits", max_splits,
+          max_len, split_size, static_cast<long long>(need));
+  int64_t work = 0;
+  for (int b = 0; b < s->batch; ++b) {
+    const int64_t L = seq_lens[b];
+    const int64_t lo = (window > 0 && L > window) ? L - window : 0;
+    work += (L - 1) / split_size - lo / split_size + 1;
+  }
+  REQUIRE(work <= (int64_t{1} << 30), kNotImpl,
+          "%lld split work items are not supported (supported: up to 2^30); use a larger split_size",
+          static_cast<long long>(work));
+  return UAII_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* uaii_last_error(void) { return g_error.c_str(); }
+
+uaii_status uaii_kv_produce(const uaii_attn_shape* shape, const uaii_rope* rope,
+                            const uaii_qk_norm* qk_norm, const float* q_in, const float* k_in,
+                            const float* v_in, const int32_t* positions, const uaii_kv_cache* cache,
+                            float* q_out, void* stream) {
+  const char* fn = "uaii_kv_produce";
+  g_error.clear();
+  uaii_status st = check_shape(fn, shape);
+  if (st != UAII_OK) return st;
+  st = check_cache(fn, cache);
+  if (st != UAII_OK) return st;
+  REQUIRE(rope != nullptr, kInvalid, "rope is NULL; pass a uaii_rope");
+  REQUIRE(rope->pairing == UAII_ROPE_NEOX || rope->pairing == UAII_ROPE_INTERLEAVED, kInvalid,
+          "rope.pairing=%d is not a pairing code (neox=0, interleaved=1)", rope->pairing);
+  REQUIRE(rope->scaling == UAII_ROPE_PLAIN || rope->scaling == UAII_ROPE_LLAMA3, kNotImpl,
+          "unsupported rope_scaling.type=%d (supported: plain=0, llama3=1)", rope->scaling);
+  REQUIRE(finite_pos(rope->theta), kInvalid, "rope.theta=%g is invalid (must be finite and > 0)",
+          rope->theta);
+  if (rope->scaling == UAII_ROPE_LLAMA3) {
+    REQUIRE(std::isfinite(rope->factor) && rope->factor >= 1.0, kInvalid,
+            "rope.factor=%g is invalid for llama3 scaling (must be finite and >= 1)", rope->factor);
+    REQUIRE(finite_pos(rope->low_freq_factor), kInvalid,
+            "rope.low_freq_factor=%g is invalid (must be finite and > 0)", rope->low_freq_factor);
+    REQUIRE(std::isfinite(rope->high_freq_factor) && rope->high_freq_factor > rope->low_freq_factor,
+            kInvalid, "rope.high_freq_factor=%g must be finite and > low_freq_factor=%g",
+            rope->high_freq_factor, rope->low_freq_factor);
+    REQUIRE(rope->original_max_position > 0, kInvalid,
+            "rope.original_max_position=%d is invalid (must be > 0)", rope->original_max_position);
+  }
+  const bool norm = qk_norm != nullptr && qk_norm->enabled != 0;
+  if (norm) {
+    REQUIRE(std::isfinite(qk_norm->eps) && qk_norm->eps > 0.0f, kInvalid,
+            "qk_norm.eps=%g is invalid (must be finite and > 0)", static_cast<double>(qk_norm->eps));
+    REQUIRE(qk_norm->offset == 0 || qk_norm->offset == 1, kInvalid,
+            "qk_norm.offset=%d is invalid (0: gain w, 1: gain 1 + w)", qk_norm->offset);
+    CHECK_PTR("qk_norm.q_weight", qk_norm->q_weight, 4);
+    CHECK_PTR("qk_norm.k_weight", qk_norm->k_weight, 4);
+  }
+  CHECK_PTR("q_in", q_in, 16);
+  CHECK_PTR("k_in", k_in, 16);
+  CHECK_PTR("v_in", v_in, 16);
+  CHECK_PTR("q_out", q_out, 16);
+  REQUIRE(positions != nullptr, kInvalid, "positions is NULL; pass a host array of batch=%d positions",
+          shape->batch);
+  for (int b = 0; b < shape->batch; ++b)
+    REQUIRE(positions[b] >= 0 && positions[b] < cache->capacity, kInvalid,
+            "positions[%d]=%d is outside [0, capacity=%d)", b, positions[b], cache->capacity);
+
+  uaii::ProduceArgs a{};
+  a.B = shape->batch;
+  a.H = shape->n_heads;
+  a.Hkv = shape->n_kv_heads;
+  a.D = shape->head_dim;
+  a.pairing = rope->pairing;
+  a.scaling = rope->scaling;
+  a.theta = rope->theta;
+  a.factor = rope->factor;
+  a.low = rope->low_freq_factor;
+  a.high = rope->high_freq_factor;
+  a.orig = static_cast<double>(rope->original_max_position);
+  a.norm_enabled = norm ? 1 : 0;
+  a.norm_offset = norm ? qk_norm->offset : 0;
+  a.norm_eps = norm ? qk_norm->eps : 0.0f;
+  a.w_q = norm ? qk_norm->q_weight : nullptr;
+  a.w_k = norm ? qk_norm->k_weight : nullptr;
+  a.q_in = q_in;
+  a.k_in = k_in;
+  a.v_in = v_in;
+  a.k_dtype = cache->k_dtype;
+  a.v_dtype = cache->v_dtype;
+  a.cap = cache->capacity;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.v_scale = cache->v_scale;
+  a.q_out = q_out;
+  for (int b = 0; b < shape->batch; ++b) a.pos[b] = positions[b];
+  return device_status(fn, uaii::launch_kv_produce(a, static_cast<hipStream_t>(stream)));
+}
+
+uaii_status uaii_decode_attn(const uaii_attn_shape* shape, const uaii_kv_cache* cache, const float* q,
+                             const int32_t* seq_lens, float scale, int32_t window, float softcap,
+                             int32_t split_size, int32_t max_splits, float* part_o, float* part_lse,
+                             void* stream) {
+  const char* fn = "uaii_decode_attn";
+  g_error.clear();
+  uaii_status st = check_shape(fn, shape);
+  if (st != UAII_OK) return st;
+  st = check_cache(fn, cache);
+  if (st != UAII_OK) return st;
+  st = check_lens(fn, shape, seq_lens, cache->capacity, split_size, max_splits, window);
+  if (st != UAII_OK) return st;
+  REQUIRE(std::isfinite(softcap) && softcap >= 0.0f, kInvalid,
+          "softcap=%g is invalid (0 = none, c > 0 applies c*tanh(s/c))", static_cast<double>(softcap));
+  REQUIRE(std::isfinite(scale), kInvalid, "scale=%g is invalid (must be finite)", static_cast<double>(scale));
+  const double want = 1.0 / std::sqrt(static_cast<double>(shape->head_dim));
+  REQUIRE(std::fabs(static_cast<double>(scale) - want) <= 1e-6 * want, kNotImpl,
+          "scale=%.9g is not supported (supported: 1/sqrt(head_dim)=%.9g; a differing "
+          "query_pre_attn_scalar is refused)",
+          static_cast<double>(scale), want);
+  CHECK_PTR("q", q, 16);
+  CHECK_PTR("part_o", part_o, 16);
+  CHECK_PTR("part_lse", part_lse, 4);
+
+  uaii::AttnArgs a{};
+  a.H = shape->n_heads;
+  a.Hkv = shape->n_kv_heads;
+  a.cap = cache->capacity;
+  a.split_size = split_size;
+  a.max_splits = max_splits;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.v_scale = cache->v_dtype == UAII_I8 ? cache->v_scale : nullptr;
+  a.q = q;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  const float log2e = 1.4426950408889634f;
+  const float s = static_cast<float>(want);
+  a.q_mul = softcap > 0.0f ? s : s * log2e;
+  a.softcap = softcap;
+  build_table(shape->batch, seq_lens, window, split_size, &a.t);
+  const int G = shape->n_heads / shape->n_kv_heads;
+  return device_status(fn, uaii::launch_decode_partial(shape->head_dim, G, cache->k_dtype,
+                                                       cache->v_dtype, a,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
+uaii_status uaii_decode_combine(const uaii_attn_shape* shape, const int32_t* seq_lens, int32_t window,
+                                int32_t split_size, int32_t max_splits, const float* part_o,
+                                const float* part_lse, float* out, void* stream) {
+  const char* fn = "uaii_decode_combine";
+  g_error.clear();
+  uaii_status st = check_shape(fn, shape);
+  if (st != UAII_OK) return st;
+  st = check_lens(fn, shape, seq_lens, kMaxCapacity, split_size, max_splits, window);
+  if (st != UAII_OK) return st;
+  CHECK_PTR("part_o", part_o, 16);
+  CHECK_PTR("part_lse", part_lse, 4);
+  CHECK_PTR("out", out, 16);
+
+  uaii::CombineArgs a{};
+  a.H = shape->n_heads;
+  a.max_splits = max_splits;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.out = out;
+  build_table(shape->batch, seq_lens, window, split_size, &a.t);
+  return device_status(fn, uaii::launch_decode_combine(shape->head_dim, shape->batch, a,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

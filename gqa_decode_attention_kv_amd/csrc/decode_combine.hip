@@ -1,0 +1,63 @@
+// Log-sum-exp combine of split-K decode partials: for each (sequence, query
+// head), M = max over valid splits of lse, out = sum e^(lse - M) o / sum
+// e^(lse - M).  Source: "Algenta - Model support matrix" (Conformance CLI:
+// decode_attn=splitk_flash_decoding; Kernel path capabilities: split-K decode
+// partials).  One wave per (b, h); only the splits that hold visible keys
+// are read, so the partial buffer needs no initialisation.
+#include "launch.h"
+
+#include <math.h>
+
+namespace uaii {
+namespace {
+
+__device__ inline float wave_max(float x) {
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_combine_kernel(CombineArgs a) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int s0 = a.t.first_split[b];
+  const int ns = a.t.work_prefix[b + 1] - a.t.work_prefix[b];
+  const int64_t row0 = (static_cast<int64_t>(b) * a.H + h) * a.max_splits + s0;
+  const float* lse = a.part_lse + row0;
+  const float* po = a.part_o + row0 * D;
+
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, lse[s]);
+  M = wave_max(M);
+
+  float den = 0.0f;
+  float num[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) num[e] = 0.0f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = expf(lse[s] - M);
+    den += w;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, po[static_cast<int64_t>(s) * D + lane + 64 * e], num[e]);
+  }
+  float* out = a.out + (static_cast<int64_t>(b) * a.H + h) * D;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) out[lane + 64 * e] = num[e] / den;
+}
+
+}  // namespace
+
+hipError_t launch_decode_combine(int D, int B, const CombineArgs& a, hipStream_t stream) {
+  const dim3 grid(a.H, B);
+  switch (D) {
+    case 64: hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(64), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(64), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(decode_combine_kernel<256>, grid, dim3(64), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace uaii

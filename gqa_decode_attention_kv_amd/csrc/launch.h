@@ -1,0 +1,75 @@
+// Internal interface between the C-ABI host code (api.cpp) and the HIP
+// kernels.  Everything here is passed to kernels by value: the library keeps
+// no device-side state and allocates nothing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace uaii {
+
+constexpr int kMaxBatch = 32;
+
+enum : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
+enum : int { kNeox = 0, kInterleaved = 1 };
+enum : int { kPlain = 0, kLlama3 = 1 };
+
+// Per-sequence schedule of one decode step.  Work item w of the partial
+// kernel belongs to sequence b with work_prefix[b] <= w < work_prefix[b + 1];
+// it is split first_split[b] + (w - work_prefix[b]).  Visible keys of b are
+// [lo[b], len[b]).
+struct SeqTable {
+  int32_t n_seq;
+  int32_t work_prefix[kMaxBatch + 1];
+  int32_t first_split[kMaxBatch];
+  int32_t lo[kMaxBatch];
+  int32_t len[kMaxBatch];
+};
+
+struct ProduceArgs {
+  int32_t B, H, Hkv, D;
+  int32_t pairing, scaling;
+  double theta, factor, low, high, orig;
+  int32_t norm_enabled, norm_offset;
+  float norm_eps;
+  const float* w_q;
+  const float* w_k;
+  const float* q_in;
+  const float* k_in;
+  const float* v_in;
+  int32_t k_dtype, v_dtype, cap;
+  void* k;
+  void* v;
+  float* v_scale;
+  float* q_out;
+  int32_t pos[kMaxBatch];
+};
+
+struct AttnArgs {
+  int32_t H, Hkv, cap, split_size, max_splits;
+  const void* k;
+  const void* v;
+  const float* v_scale;
+  const float* q;
+  float* part_o;
+  float* part_lse;
+  float q_mul;    // multiplies q on load: scale*log2(e), or scale with a softcap
+  float softcap;  // c > 0, or 0 for none
+  SeqTable t;
+};
+
+struct CombineArgs {
+  int32_t H, max_splits;
+  const float* part_o;
+  const float* part_lse;
+  float* out;
+  SeqTable t;
+};
+
+hipError_t launch_kv_produce(const ProduceArgs& a, hipStream_t stream);
+// total_work = t.work_prefix[t.n_seq]; grid = total_work x Hkv work-groups.
+hipError_t launch_decode_partial(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a,
+                                 hipStream_t stream);
+hipError_t launch_decode_combine(int D, int B, const CombineArgs& a, hipStream_t stream);
+
+}  // namespace uaii

@@ -1,0 +1,208 @@
+/*
+ * uaii_decode.h -- C ABI of the MI355X (gfx950) GQA decode-step library.
+ *
+ * One decode step of a grouped-query attention layer, in three calls:
+ *
+ *   uaii_kv_produce      optional per-head QK-RMSNorm, RoPE, append of the new
+ *                        token's K and V to an f32 / bf16 / vq8 cache
+ *   uaii_decode_attn     split-K flash-decoding partials over B <= 32 ragged
+ *                        sequences, with an optional sliding window and
+ *                        attention-logit softcap
+ *   uaii_decode_combine  log-sum-exp combine of the partials
+ *
+ * Sources (page title, then section):
+ *   [UAII]      "Universal AI Inference - Hugging Face decoder completeness"
+ *   [ALGENTA]   "Algenta - Model support matrix"
+ *   [FREETOKEN] "FreeToken PR #722 - serve Llama and Mistral llama-arch GGUF
+ *               checkpoints"
+ *   [LLAMAY]    "llamay - Models and formats"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership.  The caller owns every buffer.  The library never allocates or
+ *   frees memory, keeps no state between calls (except the thread-local error
+ *   text), never synchronises, and enqueues all work on the caller's stream.
+ * Pointers.  "device" pointers address GPU memory of the current device and
+ *   must be 16-byte aligned; "host" arrays are read during the call only.
+ * Layouts (row-major, innermost last):
+ *   q_in, q_out, q           [batch][n_heads][head_dim]            f32
+ *   k_in, v_in               [batch][n_kv_heads][head_dim]         f32
+ *   cache K, V               [batch][n_kv_heads][capacity][head_dim]
+ *                            K: f32 or bf16; V: f32, bf16 or int8 (vq8)
+ *   v_scale (vq8 only)       [batch][n_kv_heads][capacity]         f32
+ *   part_o                   [batch][n_heads][max_splits][head_dim] f32
+ *   part_lse                 [batch][n_heads][max_splits]          f32
+ *   out                      [batch][n_heads][head_dim]            f32
+ *   bf16 is stored as its 16-bit pattern (upper half of an f32); it is
+ *   widened to f32 when read, never reinterpreted ([UAII] P0.1 BF16 ingest).
+ * Query-to-kv-head map.  n_heads is an exact multiple of n_kv_heads and query
+ *   head h reads kv head h / (n_heads / n_kv_heads): consecutive groups
+ *   ([ALGENTA] Structural fact requirements: integral GQA ratio).
+ * Lengths.  seq_lens[b] counts the keys sequence b attends, the new token
+ *   included; the new token sits at slot seq_lens[b] - 1, which is also its
+ *   absolute RoPE position ([UAII] P1.3: positions follow the absolute KV
+ *   index, same as RoPE).
+ * Window.  window = W > 0 keeps the last W keys, the new one included:
+ *   keys [max(0, L - W), L).  W = 0 means no window ([UAII] P1.4).
+ * Errors.  Every argument is checked before any work is enqueued; on error
+ *   nothing is written and the call returns a status, with a message that
+ *   names the fact, its value and the supported range
+ *   ([ALGENTA] Conformance CLI: typed refusals; [UAII] section 6: every
+ *   message says what failed and what to do).  Sizes of caller buffers
+ *   cannot be checked through plain pointers and are the caller's contract.
+ *   UAII_ERR_INVALID_ARGUMENT  malformed input (null pointer, bad range)
+ *   UAII_ERR_NOT_IMPLEMENTED   a valid fact outside the supported ranges
+ *   UAII_ERR_DEVICE            a HIP error when enqueuing (message from HIP)
+ * Supported ranges.  head_dim in {64, 128, 256}; batch in 1..32 ([ALGENTA]
+ *   Kernel path capabilities: batched decode partial, B <= 32);
+ *   n_heads / n_kv_heads in {1, 2, 4, 8}; K dtype f32 or bf16; V dtype f32,
+ *   bf16 or int8 with an f32 scale per token per kv head (vq8: values
+ *   quantised, keys exact; [LLAMAY] The KV cache, in three precisions).
+ * Threads.  Re-entrant; calls on different streams may overlap.  Calls that
+ *   write the same cache slot or partial rows concurrently race.
+ */
+#ifndef UAII_DECODE_H
+#define UAII_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum uaii_status {
+    UAII_OK = 0,
+    UAII_ERR_INVALID_ARGUMENT = 1,
+    UAII_ERR_NOT_IMPLEMENTED = 2,
+    UAII_ERR_DEVICE = 3
+} uaii_status;
+
+/* Cache element types (int32 codes in the structs below). */
+enum { UAII_F32 = 0, UAII_BF16 = 1, UAII_I8 = 2 };
+
+/* RoPE pairing: NeoX rotates (i, i + d/2), interleaved rotates (2i, 2i + 1)
+ * ([UAII] P0.2; [LLAMAY] Architectures; [FREETOKEN] Changes). */
+enum { UAII_ROPE_NEOX = 0, UAII_ROPE_INTERLEAVED = 1 };
+
+/* RoPE frequency scheme: plain theta^(-2i/d), or Llama-3 frequency scaling
+ * ([UAII] P0.2: match Hugging Face's Llama-3 rotary embedding;
+ * [ALGENTA] Structural fact requirements: plain or llama3). */
+enum { UAII_ROPE_PLAIN = 0, UAII_ROPE_LLAMA3 = 1 };
+
+typedef struct uaii_attn_shape {
+    int32_t batch;      /* B, 1..32 */
+    int32_t n_heads;    /* H, query heads */
+    int32_t n_kv_heads; /* Hkv, H % Hkv == 0 */
+    int32_t head_dim;   /* d in {64, 128, 256} */
+} uaii_attn_shape;
+
+/* Rotary embedding of one layer.  A Gemma-style local/global layer pair is
+ * two calls, each with its own theta ([ALGENTA] Decoder families: dual
+ * theta; [LLAMAY] Architectures: a second rotary base on local layers).
+ * Frequencies cover the full head ([ALGENTA]: partial rotary is refused).
+ * Llama-3 scaling, with wavelength lambda_i = 2 pi / f_i and
+ * f_i = theta^(-2i/d):
+ *   lambda < original/high  -> f;    lambda > original/low -> f / factor;
+ *   otherwise mu = (original/lambda - low)/(high - low) and
+ *   (1 - mu) f / factor + mu f   ([FREETOKEN] Changes: low 1, high 4,
+ *   original 8192 for every Llama 3.1-3.3 release). */
+typedef struct uaii_rope {
+    int32_t pairing;               /* UAII_ROPE_NEOX | UAII_ROPE_INTERLEAVED */
+    int32_t scaling;               /* UAII_ROPE_PLAIN | UAII_ROPE_LLAMA3 */
+    double theta;                  /* > 0 */
+    double factor;                 /* llama3: >= 1 */
+    double low_freq_factor;        /* llama3: > 0 */
+    double high_freq_factor;       /* llama3: > low_freq_factor */
+    int32_t original_max_position; /* llama3: > 0 */
+} uaii_rope;
+
+/* Per-head QK-RMSNorm, applied to every q and k head before RoPE
+ * ([UAII] P1.2), y = x (mean x^2 + eps)^-1/2 (w + offset), with offset 0
+ * (gain w) or 1 (gain 1 + w, Gemma; [UAII] P1.1).  One weight vector of
+ * head_dim entries for q and one for k, shared by all heads.  Passing NULL
+ * for the whole struct, or enabled = 0, disables the norm. */
+typedef struct uaii_qk_norm {
+    int32_t enabled;
+    float eps;               /* > 0 */
+    int32_t offset;          /* 0 or 1 */
+    const float *q_weight;   /* device [head_dim] */
+    const float *k_weight;   /* device [head_dim] */
+} uaii_qk_norm;
+
+/* Contiguous per-sequence KV cache of one layer. */
+typedef struct uaii_kv_cache {
+    int32_t k_dtype;   /* UAII_F32 | UAII_BF16 */
+    int32_t v_dtype;   /* UAII_F32 | UAII_BF16 | UAII_I8 (vq8) */
+    int32_t capacity;  /* slots per (sequence, kv head), >= 1 */
+    void *k;           /* device [B][Hkv][capacity][d] */
+    void *v;           /* device [B][Hkv][capacity][d] */
+    float *v_scale;    /* device [B][Hkv][capacity], vq8 only (else ignored) */
+} uaii_kv_cache;
+
+/* Text of the last error on the calling thread ("" if none); valid until the
+ * next call on the same thread. */
+const char *uaii_last_error(void);
+
+/* KV producer.  For every sequence b at position p = positions[b]:
+ *   q' = RoPE(norm_q(q_in[b][h]), p)   -> q_out[b][h]           (f32)
+ *   k' = RoPE(norm_k(k_in[b][u]), p)   -> K[b][u][p]  (f32, or bf16 rounded
+ *                                                       to nearest even)
+ *   v  = v_in[b][u]                    -> V[b][u][p]  (f32; bf16 rounded to
+ *        nearest even; vq8: scale = max|v| / 127 in f32, code =
+ *        clamp(round_half_away(v / scale), -127, 127), all-zero v gives
+ *        scale 0 and codes 0; scale -> v_scale[b][u][p])
+ * The norm and the rotation are evaluated in double precision and rounded
+ * once to the stored format.  Only slot p of each (b, u) is written.
+ *   shape      host, required
+ *   rope       host, required
+ *   qk_norm    host, may be NULL (no norm)
+ *   q_in, k_in, v_in, q_out   device
+ *   positions  host [batch], each in [0, capacity)
+ *   cache      host struct describing device buffers
+ *   stream     hipStream_t (NULL = the null stream) */
+uaii_status uaii_kv_produce(const uaii_attn_shape *shape, const uaii_rope *rope,
+                            const uaii_qk_norm *qk_norm, const float *q_in,
+                            const float *k_in, const float *v_in,
+                            const int32_t *positions, const uaii_kv_cache *cache,
+                            float *q_out, void *stream);
+
+/* Split-K flash-decoding partials ([ALGENTA] Kernel path capabilities:
+ * split-K decode partial, batched decode partial; Conformance CLI:
+ * decode_attn=splitk_flash_decoding).  For every sequence b, query head h
+ * and split sigma that intersects the visible keys [lo_b, L_b), where split
+ * sigma covers keys [sigma * split_size, (sigma + 1) * split_size):
+ *   s_j   = scale * <q[b][h], K[b][h / G][j]>,  then c * tanh(s_j / c) if
+ *           softcap c > 0 ([UAII] P1.4 logit softcap; [ALGENTA] attention
+ *           scale 1/sqrt(head_dim))
+ *   part_o[b][h][sigma]   = sum_j e^(s_j - m) v_j / sum_j e^(s_j - m)
+ *   part_lse[b][h][sigma] = m + ln sum_j e^(s_j - m)
+ * over the split's visible keys, with m their largest score; v_j is the
+ * cached value widened to f32 (vq8: code * scale).  Accumulation is f32.
+ * Entries of splits outside the visible range are not written.
+ *   scale       must equal 1/sqrt(head_dim) (any other value is refused)
+ *   seq_lens    host [batch], each in [1, capacity]
+ *   window      >= 0 (0 = none);  softcap >= 0 and finite (0 = none)
+ *   split_size  >= 1;  max_splits >= ceil(max_b seq_lens[b] / split_size)
+ *   q           device, normally q_out of uaii_kv_produce
+ *   part_o, part_lse  device, sized with max_splits */
+uaii_status uaii_decode_attn(const uaii_attn_shape *shape, const uaii_kv_cache *cache,
+                             const float *q, const int32_t *seq_lens, float scale,
+                             int32_t window, float softcap, int32_t split_size,
+                             int32_t max_splits, float *part_o, float *part_lse,
+                             void *stream);
+
+/* Log-sum-exp combine of the partials written by uaii_decode_attn with the
+ * same seq_lens, window, split_size and max_splits: over the splits that
+ * intersect the visible keys, M = max lse, and
+ *   out[b][h] = sum_sigma e^(lse_sigma - M) part_o_sigma / sum_sigma e^(lse_sigma - M).
+ * Only the valid splits are read. */
+uaii_status uaii_decode_combine(const uaii_attn_shape *shape, const int32_t *seq_lens,
+                                int32_t window, int32_t split_size, int32_t max_splits,
+                                const float *part_o, const float *part_lse, float *out,
+                                void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UAII_DECODE_H */

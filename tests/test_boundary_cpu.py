@@ -1,0 +1,194 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and refuses malformed or unsupported arguments before touching the
+device, with a message that names the fact, its value and the supported
+range.  These tests pass fake (never dereferenced) device addresses, so they
+are skipped where a GPU is visible; the same refusals are exercised with real
+buffers by the GPU tests."""
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gqa_decode_attention_kv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uaii_decode.h")
+
+
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+host_only = pytest.mark.skipif(not _no_gpu(), reason="fake device addresses; host-only test")
+
+FAKE = 0x7F0000000000  # 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uaii_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load()
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert B.last_error() == ""
+
+
+def test_struct_layouts_match_header():
+    import ctypes as C
+    assert C.sizeof(B.Shape) == 16
+    assert C.sizeof(B.Rope) == 48 and B.Rope.theta.offset == 8
+    assert C.sizeof(B.QKNorm) == 32 and B.QKNorm.q_weight.offset == 16
+    assert C.sizeof(B.KVCache) == 40 and B.KVCache.k.offset == 16
+
+
+def shape(b=2, h=8, hkv=2, d=128):
+    return B.Shape(b, h, hkv, d)
+
+
+def cache(kd=B.BF16, vd=B.BF16, cap=64, k=FAKE, v=FAKE, s=None):
+    return B.KVCache(kd, vd, cap, k, v, s)
+
+
+def attn(sh=None, ca=None, q=FAKE, lens=(10, 20), scale=None, window=0, softcap=0.0, split=16,
+         max_splits=4, po=FAKE, pl=FAKE):
+    sh = sh or shape()
+    ca = ca or cache()
+    scale = 1.0 / math.sqrt(sh.head_dim) if scale is None else scale
+    B.decode_attn(sh, ca, q, lens, scale, window, softcap, split, max_splits, po, pl, 0)
+
+
+def produce(sh=None, rope=None, norm=None, ca=None, pos=(3, 4), q_in=FAKE, q_out=FAKE):
+    sh = sh or shape()
+    rope = rope or B.Rope(B.ROPE_NEOX, B.ROPE_PLAIN, 1e4, 1.0, 1.0, 4.0, 8192)
+    B.kv_produce(sh, rope, norm, q_in, FAKE, FAKE, pos, ca or cache(), q_out, 0)
+
+
+def combine(sh=None, lens=(10, 20), window=0, split=16, max_splits=4, out=FAKE):
+    B.decode_combine(sh or shape(), lens, window, split, max_splits, FAKE, FAKE, out, 0)
+
+
+def refused(fn, status, *needles):
+    with pytest.raises(B.UaiiError) as ei:
+        fn()
+    assert ei.value.status == status, ei.value
+    for n in needles:
+        assert n in ei.value.message, (n, ei.value.message)
+    return ei.value.message
+
+
+INV, NI = B.ERR_INVALID_ARGUMENT, B.ERR_NOT_IMPLEMENTED
+
+
+@host_only
+@pytest.mark.parametrize("case", [
+    ("head_dim 96", lambda: attn(sh=shape(d=96)), NI, ["head_dim=96 is not supported", "{64, 128, 256}"]),
+    ("head_dim 32", lambda: attn(sh=shape(d=32)), NI, ["head_dim=32"]),
+    ("batch 40", lambda: attn(sh=shape(b=40), lens=[1] * 40), NI, ["batch=40 is not supported", "1..32"]),
+    ("batch 0", lambda: attn(sh=shape(b=0)), INV, ["batch=0"]),
+    ("gqa not integral", lambda: attn(sh=shape(h=6, hkv=4)), INV, ["n_heads=6", "n_kv_heads=4"]),
+    ("gqa 3", lambda: attn(sh=shape(h=6, hkv=2)), NI, ["n_heads/n_kv_heads=3", "{1, 2, 4, 8}"]),
+    ("scale", lambda: attn(scale=0.1), NI, ["scale=0.1", "1/sqrt(head_dim)=0.0883883"]),
+    ("scale nan", lambda: attn(scale=float("nan")), INV, ["scale="]),
+    ("window", lambda: attn(window=-1), INV, ["window=-1"]),
+    ("softcap neg", lambda: attn(softcap=-1.0), INV, ["softcap=-1"]),
+    ("softcap inf", lambda: attn(softcap=float("inf")), INV, ["softcap=inf"]),
+    ("split 0", lambda: attn(split=0), INV, ["split_size=0"]),
+    ("max_splits", lambda: attn(lens=(10, 40), split=16, max_splits=2), INV,
+     ["max_splits=2", "need 3"]),
+    ("len 0", lambda: attn(lens=(0, 5)), INV, ["seq_lens[0]=0", "[1, 64]"]),
+    ("len > cap", lambda: attn(lens=(65, 5)), INV, ["seq_lens[0]=65"]),
+    ("q8 keys", lambda: attn(ca=cache(kd=B.I8, vd=B.I8, s=FAKE)), NI, ["q8", "vq8"]),
+    ("bad k dtype", lambda: attn(ca=cache(kd=7)), INV, ["k_dtype=7"]),
+    ("bad v dtype", lambda: attn(ca=cache(vd=5)), INV, ["v_dtype=5"]),
+    ("vq8 no scale", lambda: attn(ca=cache(vd=B.I8)), INV, ["v_scale is NULL"]),
+    ("cap 0", lambda: attn(ca=cache(cap=0)), INV, ["capacity=0"]),
+    ("k null", lambda: attn(ca=cache(k=None)), INV, ["cache.k is NULL"]),
+    ("k misaligned", lambda: attn(ca=cache(k=FAKE + 8)), INV, ["cache.k", "16-byte aligned"]),
+    ("q null", lambda: attn(q=None), INV, ["q is NULL"]),
+    ("part_o null", lambda: attn(po=None), INV, ["part_o is NULL"]),
+    ("lens null", lambda: attn(lens=None), INV, ["seq_lens is NULL"]),
+], ids=lambda c: c[0])
+def test_decode_attn_refusals(case):
+    _, fn, status, needles = case
+    msg = refused(fn, status, *needles)
+    assert msg.startswith("uaii_decode_attn: ")
+
+
+@host_only
+@pytest.mark.parametrize("case", [
+    ("rope null", lambda: B.load().uaii_kv_produce(None, None, None, FAKE, FAKE, FAKE, None, None,
+                                                    FAKE, 0), None, []),
+    ("theta 0", lambda: produce(rope=B.Rope(0, 0, 0.0, 1, 1, 4, 8192)), INV, ["rope.theta=0"]),
+    ("pairing 2", lambda: produce(rope=B.Rope(2, 0, 1e4, 1, 1, 4, 8192)), INV, ["rope.pairing=2"]),
+    ("yarn", lambda: produce(rope=B.Rope(0, 2, 1e4, 1, 1, 4, 8192)), NI,
+     ["unsupported rope_scaling.type=2"]),
+    ("llama3 factor", lambda: produce(rope=B.Rope(1, 1, 5e5, 0.5, 1, 4, 8192)), INV, ["rope.factor=0.5"]),
+    ("llama3 high<=low", lambda: produce(rope=B.Rope(1, 1, 5e5, 8, 4, 4, 8192)), INV,
+     ["high_freq_factor=4"]),
+    ("llama3 low", lambda: produce(rope=B.Rope(1, 1, 5e5, 8, 0, 4, 8192)), INV, ["low_freq_factor=0"]),
+    ("llama3 orig", lambda: produce(rope=B.Rope(1, 1, 5e5, 8, 1, 4, 0)), INV,
+     ["original_max_position=0"]),
+    ("norm eps", lambda: produce(norm=B.QKNorm(1, 0.0, 0, FAKE, FAKE)), INV, ["qk_norm.eps=0"]),
+    ("norm offset", lambda: produce(norm=B.QKNorm(1, 1e-6, 2, FAKE, FAKE)), INV, ["qk_norm.offset=2"]),
+    ("norm weight", lambda: produce(norm=B.QKNorm(1, 1e-6, 1, None, FAKE)), INV,
+     ["qk_norm.q_weight is NULL"]),
+    ("position", lambda: produce(pos=(3, 64)), INV, ["positions[1]=64", "capacity=64"]),
+    ("position neg", lambda: produce(pos=(-1, 0)), INV, ["positions[0]=-1"]),
+    ("q_in misaligned", lambda: produce(q_in=FAKE + 4), INV, ["q_in", "16-byte aligned"]),
+    ("q_out null", lambda: produce(q_out=None), INV, ["q_out is NULL"]),
+    ("head_dim", lambda: produce(sh=shape(d=80)), NI, ["head_dim=80"]),
+], ids=lambda c: c[0])
+def test_kv_produce_refusals(case):
+    name, fn, status, needles = case
+    if status is None:
+        assert fn() == INV
+        assert "shape is NULL" in B.last_error()
+        return
+    msg = refused(fn, status, *needles)
+    assert msg.startswith("uaii_kv_produce: ")
+
+
+@host_only
+@pytest.mark.parametrize("case", [
+    ("window", lambda: combine(window=-3), INV, ["window=-3"]),
+    ("split", lambda: combine(split=0), INV, ["split_size=0"]),
+    ("max_splits", lambda: combine(lens=(100, 1), max_splits=3), INV, ["max_splits=3"]),
+    ("out null", lambda: combine(out=None), INV, ["out is NULL"]),
+    ("batch", lambda: combine(sh=shape(b=33), lens=[1] * 33), NI, ["batch=33"]),
+], ids=lambda c: c[0])
+def test_decode_combine_refusals(case):
+    _, fn, status, needles = case
+    msg = refused(fn, status, *needles)
+    assert msg.startswith("uaii_decode_combine: ")
+
+
+@host_only
+def test_valid_call_without_device_reports_device_error():
+    """A fully valid call reaches the launch; with no GPU the HIP error is
+    reported as UAII_ERR_DEVICE with HIP's own text."""
+    with pytest.raises(B.UaiiError) as ei:
+        combine()
+    assert ei.value.status == B.ERR_DEVICE
+    assert "HIP error" in ei.value.message
+
+
+@host_only
+def test_error_text_is_per_call():
+    with pytest.raises(B.UaiiError):
+        attn(sh=shape(d=96))
+    assert "head_dim=96" in B.last_error()
+    assert B.load().uaii_decode_attn(None, None, None, None, 0.0, 0, 0.0, 1, 1, None, None,
+                                     None) == INV
+    assert "shape is NULL" in B.last_error()

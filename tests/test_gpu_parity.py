@@ -1,0 +1,208 @@
+"""GPU parity: the HIP decode step (through the C ABI) against the CPU oracle
+on the same seeded inputs.
+
+* Small cases compare every output element, every produced cache row and
+  every split partial; they span several tiles, multi-chunk splits, ragged
+  tails and the degenerate cases (one key, window 1, split size 1, window
+  larger than the context).
+* The named workloads run at their full sizes in the launch configuration the
+  benchmark times; the oracle checks a sample of (sequence, head) outputs and
+  partials, and every produced cache row.
+Tolerances on the output: f32 cache 1e-5 absolute; bf16 K/V 2e-3 absolute;
+vq8 1e-2 of the output's max-abs; vq8 codes and scales bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import parity as P
+from gqa_decode_attention_kv_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gqa_decode_attention_kv_amd import binding
+    binding.load()
+
+
+def case(name, d, G, Hkv, kdt, vdt, lens, S, window=0, softcap=0.0, pairing=W.NEOX,
+         scaling=W.PLAIN, theta=1e4, factor=8.0, norm=None, cap=None, seed=0):
+    lens = tuple(int(x) for x in lens)
+    cap = cap or max(lens) + 3
+    qn = W.QKNorm(False) if norm is None else W.QKNorm(True, 1e-6, norm, 1.0 - norm, 0.1)
+    w = W.Workload(name, len(lens), Hkv * G, Hkv, d, ("fixed", lens[0]), cap, kdt, vdt,
+                   W.Rope(pairing, scaling, theta, factor, 1.0, 4.0, 8192), qn, window, softcap,
+                   S, (1000 + seed,))
+    return w, np.array(lens, np.int32)
+
+
+SMALL = [
+    case("f32-d64-g2-tiny", 64, 2, 2, W.F32, W.F32, [129], 65, seed=1),
+    case("bf16-d64-g4-llama3", 64, 4, 2, W.BF16, W.BF16, [1000, 1001], 512, pairing=W.INTERLEAVED,
+         scaling=W.LLAMA3, theta=5e5, factor=32.0, seed=2),
+    case("bf16-d128-g4-ragged", 128, 4, 2, W.BF16, W.BF16, [1, 17, 513, 1024, 1500], 512,
+         pairing=W.INTERLEAVED, scaling=W.LLAMA3, theta=5e5, seed=3),
+    case("bf16-d128-g4-multichunk", 128, 4, 2, W.BF16, W.BF16, [1500, 2100], 1000, seed=4),
+    case("vq8-d128-g4-norm0", 128, 4, 2, W.BF16, W.I8, [700, 1025], 512, theta=1e6, norm=0, seed=5),
+    case("vq8-f32keys-d128-g2", 128, 2, 2, W.F32, W.I8, [300, 640], 256, seed=6),
+    case("bf16-d256-g2-window-softcap", 256, 2, 2, W.BF16, W.BF16, [1000, 90], 512, window=100,
+         softcap=50.0, norm=1, seed=7),
+    case("bf16-d256-g2-window1", 256, 2, 1, W.BF16, W.BF16, [300, 5], 128, window=1, seed=8),
+    case("f32-d128-g1", 128, 1, 4, W.F32, W.F32, [200, 333], 64, seed=9),
+    case("bf16-d128-g8", 128, 8, 1, W.BF16, W.BF16, [777], 256, seed=10),
+    case("mixed-f32k-bf16v-d64-g8", 64, 8, 2, W.F32, W.BF16, [450, 3], 128, seed=11),
+    case("f32-d256-g4", 256, 4, 1, W.F32, W.F32, [600], 512, softcap=20.0, seed=12),
+    case("vq8-d64-g1-window", 64, 1, 4, W.BF16, W.I8, [400, 36], 100, window=37, seed=13),
+    case("bf16-d128-split1", 128, 4, 1, W.BF16, W.BF16, [40, 1], 1, seed=14),
+    case("bf16-d128-window-gt-L", 128, 4, 2, W.BF16, W.BF16, [1000, 4999], 512, window=5000, seed=15),
+    case("bf16-d128-b32", 128, 4, 2, W.BF16, W.BF16,
+         np.random.default_rng(16).integers(1, 601, 32), 128, seed=16),
+    case("bf16-d256-g8-window-multichunk", 256, 8, 1, W.BF16, W.BF16, [2600, 1400], 700,
+         window=1500, softcap=30.0, seed=17),
+    case("f32-d64-g2-softcap", 64, 2, 2, W.F32, W.F32, [500], 96, softcap=5.0, norm=1, seed=18),
+    case("vq8-d256-g2-softcap", 256, 2, 2, W.BF16, W.I8, [900, 513], 512, softcap=50.0, seed=19),
+]
+
+
+def run_gpu(inputs, split_size=None):
+    from gqa_decode_attention_kv_amd.step import DeviceStep
+    st = DeviceStep(inputs, split_size=split_size)
+    st.part_o.fill_(float("nan"))
+    st.part_lse.fill_(float("nan"))
+    st.step()
+    torch.cuda.synchronize()
+    return st
+
+
+def compare_partials(st, ref, w, lens, pick=None):
+    po = st.part_o.cpu().numpy()
+    pl = st.part_lse.cpu().numpy()
+    worst = 0.0
+    for b, L in enumerate(lens):
+        valid = P.valid_splits(w, int(L), st.split_size)
+        for h in (range(w.n_heads) if pick is None else pick(b)):
+            for sg in range(st.max_splits):
+                if sg not in valid:
+                    assert np.all(np.isnan(po[b, h, sg])) and np.isnan(pl[b, h, sg]), \
+                        f"partial ({b},{h},{sg}) outside the visible range was written"
+                    continue
+                if pick is not None and sg not in (valid[0], valid[-1]):
+                    continue
+                o, lse, n = ref.partial(b, h, sg, st.split_size)
+                assert n > 0
+                e_o = np.max(np.abs(po[b, h, sg] - o))
+                e_l = abs(pl[b, h, sg] - lse)
+                worst = max(worst, e_o)
+                assert e_o <= P.out_tolerance(w, o)[0], (b, h, sg, e_o)
+                assert e_l <= 1e-4 * max(1.0, abs(lse)), (b, h, sg, e_l, lse)
+    return worst
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[c[0].name for c in SMALL])
+def test_small_case(spec):
+    w, lens = spec
+    P.say(f"case {w.name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} lens={lens.tolist()[:8]} S={w.split_size}")
+    inputs = W.make_inputs(w, seq_lens=lens)
+    ck0, cv0 = inputs.cache_k.copy(), inputs.cache_v.copy()
+    st = run_gpu(inputs)
+    ref = P.OracleStep(inputs)
+    out = st.out.cpu().numpy()
+    want = ref.decode().reshape(out.shape)
+    tol, cls = P.out_tolerance(w, want)
+    err = float(np.max(np.abs(out - want)))
+    P.check_slot(w, st.cache_rows(), ref.slot_rows(), st.q_out.cpu().numpy(), ref.q)
+    compare_partials(st, ref, w, lens)
+    # only the new token's slot of the cache changed
+    mask = np.ones(ck0.shape[:3], bool)
+    mask[np.arange(w.batch), :, inputs.positions] = False
+    for dev, host in ((st.cache_k, ck0), (st.cache_v, cv0)):
+        g = dev.cpu().numpy().view(host.dtype)
+        assert np.array_equal(g[mask].view(np.uint8), host[mask].view(np.uint8))
+    P.say(f"  max abs err {err:.3g} (tol {tol:.3g}, {cls})")
+    assert err <= tol
+
+
+FULL = ["tiny", "llama3.2-1b", "llama3.1-8b-ragged", "qwen3-vq8", "gemma2-local", "gemma2-global",
+        W.HEADLINE]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    w = W.WORKLOADS[name]
+    P.say(f"full-size {name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
+          f"cap={w.capacity} S={w.split_size} window={w.window} softcap={w.softcap}")
+    inputs = W.make_inputs(w)
+    st = run_gpu(inputs)
+    ref = P.OracleStep(inputs, copy_cache=False)  # inputs are on the device already
+    rng = np.random.default_rng(99)
+    H = w.n_heads
+    pairs = []
+    for b in range(w.batch):
+        hs = rng.choice(H, size=min(H, 4 if w.batch > 1 else H), replace=False)
+        pairs += [(b, int(h)) for h in hs]
+    out = st.out.cpu().numpy()
+    want = ref.decode(pairs)
+    got = np.stack([out[b, h] for b, h in pairs])
+    tol, cls = P.out_tolerance(w, want)
+    err = float(np.max(np.abs(got - want)))
+    P.check_slot(w, st.cache_rows(), ref.slot_rows(), st.q_out.cpu().numpy(), ref.q)
+    sel = {b: [h for bb, h in pairs if bb == b][:2] for b in range(w.batch)}
+    compare_partials(st, ref, w, inputs.seq_lens, pick=lambda b: sel[b])
+    assert np.all(np.isfinite(out))
+    P.say(f"  sampled {len(pairs)} outputs: max abs err {err:.3g} (tol {tol:.3g}, {cls})")
+    assert err <= tol
+
+
+def test_deterministic():
+    """Two runs of the same step give bitwise-identical outputs and partials."""
+    w, lens = SMALL[2]
+    inputs = W.make_inputs(w, seq_lens=lens)
+    a = run_gpu(inputs)
+    b = run_gpu(inputs)
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.part_o.nan_to_num(7.0), b.part_o.nan_to_num(7.0))
+    a.step()
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, b.out)
+
+
+def test_refusal_leaves_buffers_untouched():
+    """An invalid call writes nothing (checked on real device buffers)."""
+    from gqa_decode_attention_kv_amd import binding as B
+    w, lens = SMALL[1]
+    inputs = W.make_inputs(w, seq_lens=lens)
+    st = run_gpu(inputs)
+    before = (st.out.clone(), st.part_o.clone(), st.q_out.clone(), st.cache_k.clone())
+    with pytest.raises(B.UaiiError):
+        B.decode_attn(st.shape, st.cache, st.q_out.data_ptr(), st.seq_lens, 0.5, 0, 0.0,
+                      st.split_size, st.max_splits, st.part_o.data_ptr(), st.part_lse.data_ptr(),
+                      st.stream())
+    bad = (np.array(st.positions) + w.capacity).astype(np.int32)
+    with pytest.raises(B.UaiiError):
+        B.kv_produce(st.shape, st.rope, st.qk_norm, st.q_in.data_ptr(), st.k_in.data_ptr(),
+                     st.v_in.data_ptr(), bad, st.cache, st.q_out.data_ptr(), st.stream())
+    with pytest.raises(B.UaiiError):
+        B.decode_combine(st.shape, st.seq_lens, 0, st.split_size, 0, st.part_o.data_ptr(),
+                         st.part_lse.data_ptr(), st.out.data_ptr(), st.stream())
+    torch.cuda.synchronize()
+    after = (st.out, st.part_o, st.q_out, st.cache_k)
+    for x, y in zip(before, after):
+        assert torch.equal(x.nan_to_num(7.0), y.nan_to_num(7.0))
+
+
+def test_split_size_invariance():
+    """The output does not depend on the split size (within f32 rounding)."""
+    w, lens = SMALL[2]
+    inputs = W.make_inputs(w, seq_lens=lens)
+    outs = []
+    for S in (64, 512, 2048):
+        st = run_gpu(inputs, split_size=S)
+        outs.append(st.out.cpu().numpy())
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < 1e-5
