@@ -150,8 +150,10 @@ uaii_status check_lens(const char* fn, const uaii_attn_shape* s, const int32_t* 
     const int64_t lo = (window > 0 && L > window) ? L - window : 0;
     work += (L - 1) / split_size - lo / split_size + 1;
   }
+  work *= s->n_kv_heads;
   REQUIRE(work <= (int64_t{1} << 30), kNotImpl,
-          "%lld split work items are not supported (supported: up to 2^30); use a larger split_size",
+          "%lld (split, kv head) work items are not supported (supported: up to 2^30); use a larger "
+          "split_size",
           static_cast<long long>(work));
   return UAII_OK;
 }

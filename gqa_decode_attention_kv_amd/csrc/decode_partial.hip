@@ -10,26 +10,30 @@
 //
 // Design (gfx950, bandwidth bound, no MFMA: one query row per kv head is a
 // GEMV; arithmetic intensity is 2-5 flop per KV byte, far below the ridge):
-//   * one 256-thread work-group (4 wave64) per (sequence, kv head, split),
-//     taken from a flattened per-sequence work table, so ragged batches and
-//     windows only launch work-groups that hold visible keys;
+//   * one wave64 per (sequence, kv head, split) work item, taken from a
+//     flattened per-sequence work table, so ragged batches and windows only
+//     launch waves that hold visible keys; four independent waves share a
+//     work-group but never synchronise (no barriers, no cross-wave merge);
 //   * the G query heads that share the kv head are held in registers, so
 //     every K and V byte is read from HBM exactly once per group;
-//   * each wave owns a contiguous block of up to 128 rows of the split and
-//     runs two passes over it: K (16-byte coalesced loads, a row spread over
-//     d*sizeof(K)/16 lanes, scores reduced across those lanes with DPP),
-//     scores parked in LDS, then V with the softmax weights broadcast from
-//     LDS; the two passes need no rescaling inside the block;
+//   * a wave walks its split in chunks of up to 512 rows with two passes per
+//     chunk: K (16-byte coalesced loads, a row spread over d*sizeof(K)/16
+//     lanes, scores reduced across those lanes with DPP) with raw scores
+//     parked in LDS, then V with the softmax weights broadcast from LDS; the
+//     running max and sum rescale only between chunks;
 //   * scores live in the log2 domain (q pre-multiplied by scale*log2 e) so the
-//     exponential is a single exp2; with a softcap the tanh clip is applied
-//     to the natural-scale score first;
+//     exponential is one v_exp_f32; with a softcap the tanh clip is applied
+//     in the weights pass (it is monotonic, so the max commutes with it);
 //   * vq8: int8 codes are widened in registers and the per-token scale is
 //     folded into the softmax weight, so dequantisation costs no extra pass;
-//   * the four waves' (max, sum, accumulator) triples are merged through LDS
-//     and the work-group writes one normalised partial and its log-sum-exp
-//     per query head.
-// Rows outside the visible range are never loaded; masked lanes use
-// selects, never multiplications by zero, so poisoned memory cannot leak.
+//   * at the end the wave sums its row groups across lanes and writes one
+//     normalised partial and its log-sum-exp per query head.
+// Loads run as a rolling pipeline (the next tiles are requested as soon as
+// the current one is widened, and the first value tiles before the softmax
+// weights are computed).  Every load addresses a row inside the visible
+// range (rows past a chunk's end are clamped to its last row and masked
+// afterwards), so memory outside the visible keys is never read and masked
+// lanes never touch poisoned values.
 #include "launch.h"
 
 #include <math.h>
@@ -39,9 +43,10 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                  // independent waves per work-group
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 128;  // rows of one wave per chunk (chunk = 512 rows)
+constexpr int kRowsPerChunk = 512;         // rows a wave scores before it reads values
+constexpr int kLoadsInFlight = 8;          // 16-byte loads per lane kept in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -63,6 +68,32 @@ __device__ inline float group_sum(float x) {
   return x;
 }
 
+// group_sum over G independent values, stage by stage, so consecutive DPP
+// operations read registers written G instructions earlier (no hazard stalls).
+template <int N, int G>
+__device__ inline void group_sum_n(float (&x)[G]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) x[g] += dpp<0xB1>(x[g]);
+#pragma unroll
+  for (int g = 0; g < G; ++g) x[g] += dpp<0x4E>(x[g]);
+  if constexpr (N >= 8) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) x[g] += dpp<0x141>(x[g]);
+  }
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) x[g] += dpp<0x140>(x[g]);
+  }
+  if constexpr (N >= 32) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) x[g] += __shfl_xor(x[g], 16);
+  }
+  if constexpr (N >= 64) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) x[g] += __shfl_xor(x[g], 32);
+  }
+}
+
 __device__ inline float wave_max(float x) {
   x = fmaxf(x, dpp<0xB1>(x));
   x = fmaxf(x, dpp<0x4E>(x));
@@ -76,6 +107,13 @@ __device__ inline float wave_max(float x) {
 __device__ inline float wave_sum(float x) { return group_sum<64>(x); }
 
 __device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
+
+// Score in the log2 domain from a raw score: with a softcap c the raw score is
+// the natural-scale s and the result is c*tanh(s/c)*log2(e); without one the
+// raw score already carries the log2(e) factor.  Monotonic in s.
+__device__ inline float capped_log2(float s, bool capped, float c, float c_inv) {
+  return capped ? c * tanhf(s * c_inv) * kLog2e : s;
+}
 
 // Widen the 16 bytes of one lane to E floats.
 template <int DT, int E>
@@ -110,27 +148,27 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
   constexpr int VLPR = D * VB / 16;
   constexpr int VRPL = 64 / VLPR;
   constexpr int VE = 16 / VB;
-  constexpr int UK = (8 * KRPL <= kRowsPerWave) ? 8 : kRowsPerWave / KRPL;  // loads in flight
-  constexpr int UV = (8 * VRPL <= kRowsPerWave) ? 8 : kRowsPerWave / VRPL;
-  static_assert(kRowsPerWave % (UK * KRPL) == 0 && kRowsPerWave % (UV * VRPL) == 0, "tiling");
+  constexpr int UK = (kLoadsInFlight * KRPL <= kRowsPerChunk) ? kLoadsInFlight : kRowsPerChunk / KRPL;
+  constexpr int UV = (kLoadsInFlight * VRPL <= kRowsPerChunk) ? kLoadsInFlight : kRowsPerChunk / VRPL;
+  static_assert(kRowsPerChunk % (UK * KRPL) == 0 && kRowsPerChunk % (UV * VRPL) == 0, "tiling");
   static_assert(KLPR >= 4 && VLPR >= 4, "row must span at least a quad");
 
-  constexpr int kScoreFloats = kWaves * kRowsPerWave * G;
-  constexpr int kCombFloats = kWaves * G * (D + 2);
-  __shared__ __attribute__((aligned(16))) float smem[kScoreFloats > kCombFloats ? kScoreFloats : kCombFloats];
+  __shared__ __attribute__((aligned(16))) float smem[kWaves * kRowsPerChunk * G];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int kvh = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // Which sequence and split this work-group owns.
-  const int w = blockIdx.x;
+  // Work item of this wave: (work index w, kv head); w names (sequence, split).
+  const int item = blockIdx.x * kWaves + wave;
+  const int total = a.t.work_prefix[a.t.n_seq] * a.Hkv;
+  if (item >= total) return;  // no barriers below: idle waves leave at once
+  const int kvh = item % a.Hkv;
+  const int w = item / a.Hkv;
   int b = 0;
   for (int i = 1; i < a.t.n_seq; ++i) b += (w >= a.t.work_prefix[i]) ? 1 : 0;
   const int sigma = a.t.first_split[b] + (w - a.t.work_prefix[b]);
-  const int L = a.t.len[b];
   const int r0 = max(sigma * a.split_size, a.t.lo[b]);
-  const int r1 = min((sigma + 1) * a.split_size, L);
+  const int r1 = min((sigma + 1) * a.split_size, a.t.len[b]);
 
   const int64_t slab = (static_cast<int64_t>(b) * a.Hkv + kvh) * a.cap;  // first row of (b, kvh)
   const char* kbase = static_cast<const char*>(a.k) + slab * (D * KB);
@@ -170,71 +208,106 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
     l_run[g] = 0.0f;
   }
 
-  float* sc = smem + wave * (kRowsPerWave * G);  // this wave's [row][G] scores
+  float* sc = smem + wave * (kRowsPerChunk * G);  // this wave's [row][G] scores / weights
 
-  for (int c0 = r0; c0 < r1; c0 += kWaves * kRowsPerWave) {
-    const int chunk = min(kWaves * kRowsPerWave, r1 - c0);
-    // Even share per wave, rounded to 16 rows (the largest rows-per-load).
-    const int per = min(kRowsPerWave, ((chunk + kWaves - 1) / kWaves + 15) & ~15);
-    const int a0 = c0 + wave * per;
-    const int nrows = max(0, min(per, r1 - a0));  // rows [a0, a0 + nrows)
+  for (int a0 = r0; a0 < r1; a0 += kRowsPerChunk) {
+    const int nrows = min(kRowsPerChunk, r1 - a0);  // rows [a0, a0 + nrows), wave-uniform
 
-    // ---- pass 1: scores of this wave's rows -------------------------------
-    float mloc[G];
+    // Loads address row min(row, nrows - 1): every load is unconditional and
+    // in the visible range; rows past the end are masked after the load.
+    // Addresses are a wave-uniform base plus a 32-bit lane offset.
+    const char* kblk = kbase + static_cast<int64_t>(a0) * (D * KB);
+    const char* vblk = vbase + static_cast<int64_t>(a0) * (D * VB);
+    const int nk = (nrows + KRPL - 1) / KRPL;  // K tiles of KRPL rows
+    const int nv = (nrows + VRPL - 1) / VRPL;  // V tiles of VRPL rows
+    auto koff = [&](int t) -> uint32_t {
+      return static_cast<uint32_t>(min(t * KRPL + kr, nrows - 1) * (D * KB) + kc * 16);
+    };
+    auto voff = [&](int t) -> uint32_t {
+      return static_cast<uint32_t>(min(t * VRPL + vr, nrows - 1) * (D * VB) + vc * 16);
+    };
+
+    // ---- pass 1: raw scores of the chunk's rows (rolling prefetch) ----------
+    // Rows past the chunk's end hold duplicates of its last row; the weights
+    // pass ignores them.  Each tile's registers are reloaded as soon as the
+    // tile has been widened.  The steady-state loop has no branches (every
+    // tile and every reload is in range) so the compiler can count loads in
+    // flight exactly; the last one or two batches run in a guarded tail.
+    u32x4 kd[UK];
+    auto k_scores = [&](const float (&kf)[KE], int r) {
+      float s[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) mloc[g] = -INFINITY;
-    for (int t0 = 0; t0 < nrows; t0 += UK * KRPL) {
-      u32x4 kd[UK];
+      for (int g = 0; g < G; ++g) {
+        float p = q[g][0] * kf[0];
 #pragma unroll
-      for (int u = 0; u < UK; ++u) {
-        const int r = t0 + u * KRPL + kr;
-        kd[u] = (r < nrows) ? load16(kbase + static_cast<int64_t>(a0 + r) * (D * KB) + kc * 16)
-                            : u32x4{0u, 0u, 0u, 0u};
+        for (int e = 1; e < KE; ++e) p = fmaf(q[g][e], kf[e], p);
+        s[g] = p;
       }
+      group_sum_n<KLPR, G>(s);
+      if (kc == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[r * G + g] = s[g];
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < UK; ++u) kd[u] = load16(kblk + koff(min(u, nk - 1)));
+    int t0 = 0;
+    for (; t0 + 2 * UK <= nk; t0 += UK) {
 #pragma unroll
       for (int u = 0; u < UK; ++u) {
-        const int r = t0 + u * KRPL + kr;
         float kf[KE];
         widen<KT, KE>(kd[u], kf);
-        float s[G];
+        kd[u] = load16(kblk + koff(t0 + UK + u));
+        k_scores(kf, (t0 + u) * KRPL + kr);
+      }
+    }
+    for (; t0 < nk; t0 += UK) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float p = 0.0f;
-#pragma unroll
-          for (int e = 0; e < KE; ++e) p = fmaf(q[g][e], kf[e], p);
-          s[g] = group_sum<KLPR>(p);
-          if (capped) s[g] = cap_c * tanhf(s[g] * cap_inv) * kLog2e;
-          s[g] = (r < nrows) ? s[g] : -INFINITY;
-          mloc[g] = fmaxf(mloc[g], s[g]);
-        }
-        if (kc == 0) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) sc[r * G + g] = s[g];
+      for (int u = 0; u < UK; ++u) {
+        if (t0 + u < nk) {
+          float kf[KE];
+          widen<KT, KE>(kd[u], kf);
+          if (t0 + UK + u < nk) kd[u] = load16(kblk + koff(t0 + UK + u));
+          k_scores(kf, (t0 + u) * KRPL + kr);
         }
       }
     }
+    // First value tiles are in flight while the weights are computed.
+    u32x4 vd[UV];
+#pragma unroll
+    for (int u = 0; u < UV; ++u) vd[u] = load16(vblk + voff(min(u, nv - 1)));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- running max and rescale ------------------------------------------
-    float m_new[G];
+    // ---- chunk max (raw scores of valid rows, from LDS), running max, rescale
+    float mloc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) mloc[g] = -INFINITY;
+    for (int r = lane; r < nrows; r += 64) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) mloc[g] = fmaxf(mloc[g], sc[r * G + g]);
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      m_new[g] = fmaxf(m_run[g], wave_max(mloc[g]));
-      const float alpha = (m_run[g] == -INFINITY) ? 0.0f : exp2f(m_run[g] - m_new[g]);
+      const float m_chunk = wave_max(mloc[g]);  // finite: the chunk has >= 1 row
+      const float m_new = fmaxf(m_run[g], capped_log2(m_chunk, capped, cap_c, cap_inv));
+      const float alpha = (m_run[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
       l_run[g] *= alpha;
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
-      m_run[g] = m_new[g];
+      m_run[g] = m_new;
     }
 
-    // ---- weights: p = 2^(s - m); vq8 folds the token's scale into p --------
-    for (int r = lane; r < nrows; r += 64) {
-      const float vs = (VT == kI8) ? sbase[a0 + r] : 1.0f;
+    // ---- weights p = 2^(s - m) for every row the value tiles cover (0 past
+    // the end); vq8 folds the token's scale into p ---------------------------
+    for (int r = lane; r < nv * VRPL; r += 64) {
+      const bool ok = r < nrows;
+      const float vs = (VT == kI8) ? sbase[a0 + min(r, nrows - 1)] : 1.0f;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float p = exp2f(sc[r * G + g] - m_run[g]);
+        const float p =
+            ok ? __builtin_amdgcn_exp2f(capped_log2(sc[r * G + g], capped, cap_c, cap_inv) - m_run[g]) : 0.0f;
         l_run[g] += p;
         sc[r * G + g] = p * vs;
       }
@@ -243,27 +316,35 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- pass 2: weighted sum of values -------------------------------------
-    for (int t0 = 0; t0 < nrows; t0 += UV * VRPL) {
-      u32x4 vd[UV];
+    // ---- pass 2: weighted sum of values (rolling prefetch of UV tiles) ------
+    auto v_accum = [&](const float (&vf)[VE], int r) {
+      float p[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) p[g] = sc[r * G + g];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(p[g], vf[e], acc[g][e]);
+    };
+    t0 = 0;
+    for (; t0 + 2 * UV <= nv; t0 += UV) {
 #pragma unroll
       for (int u = 0; u < UV; ++u) {
-        const int r = t0 + u * VRPL + vr;
-        vd[u] = (r < nrows) ? load16(vbase + static_cast<int64_t>(a0 + r) * (D * VB) + vc * 16)
-                            : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < UV; ++u) {
-        const int r = t0 + u * VRPL + vr;
-        float p[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) p[g] = (r < nrows) ? sc[r * G + g] : 0.0f;
         float vf[VE];
         widen<VT, VE>(vd[u], vf);
+        vd[u] = load16(vblk + voff(t0 + UV + u));
+        v_accum(vf, (t0 + u) * VRPL + vr);
+      }
+    }
+    for (; t0 < nv; t0 += UV) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(p[g], vf[e], acc[g][e]);
+      for (int u = 0; u < UV; ++u) {
+        if (t0 + u < nv) {
+          float vf[VE];
+          widen<VT, VE>(vd[u], vf);
+          if (t0 + UV + u < nv) vd[u] = load16(vblk + voff(t0 + UV + u));
+          v_accum(vf, (t0 + u) * VRPL + vr);
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -271,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- merge the row groups of the wave, then the waves --------------------
+  // ---- merge the wave's row groups and write the split's partial ----------
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     l_run[g] = wave_sum(l_run[g]);
@@ -283,46 +364,29 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
       acc[g][e] = x;
     }
   }
-  __syncthreads();  // every wave is done with its scores
-  float* comb = smem;                          // [wave][G][D]
-  float* ml = smem + kWaves * G * D;           // [wave][G][2]
+  const int64_t row0 = (static_cast<int64_t>(b) * a.H + kvh * G) * a.max_splits + sigma;
   if (vr == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+      const float inv = 1.0f / l_run[g];
+      float* dst = a.part_o + (row0 + static_cast<int64_t>(g) * a.max_splits) * D + vc * VE;
 #pragma unroll
-      for (int e = 0; e < VE; ++e) comb[(wave * G + g) * D + vc * VE + e] = acc[g][e];
+      for (int e = 0; e < VE; e += 4)
+        *reinterpret_cast<float4*>(dst + e) =
+            make_float4(acc[g][e] * inv, acc[g][e + 1] * inv, acc[g][e + 2] * inv, acc[g][e + 3] * inv);
+    }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      ml[(wave * G + g) * 2] = m_run[g];
-      ml[(wave * G + g) * 2 + 1] = l_run[g];
-    }
-  }
-  __syncthreads();
-
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int g = idx / D, dd = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, ml[(wv * G + g) * 2]);
-    float den = 0.0f, num = 0.0f;
-#pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) {
-      const float mw = ml[(wv * G + g) * 2];
-      const float aw = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-      den = fmaf(aw, ml[(wv * G + g) * 2 + 1], den);
-      num = fmaf(aw, comb[(wv * G + g) * D + dd], num);
-    }
-    const int64_t row = (static_cast<int64_t>(b) * a.H + kvh * G + g) * a.max_splits + sigma;
-    a.part_o[row * D + dd] = num / den;
-    if (dd == 0) a.part_lse[row] = (M + log2f(den)) * kLn2;
+    for (int g = 0; g < G; ++g)
+      a.part_lse[row0 + static_cast<int64_t>(g) * a.max_splits] = (m_run[g] + log2f(l_run[g])) * kLn2;
   }
 }
 
 template <int D, int G, int KT, int VT>
 hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid(a.t.work_prefix[a.t.n_seq], a.Hkv);
+  const int items = a.t.work_prefix[a.t.n_seq] * a.Hkv;
+  const dim3 grid((items + kWaves - 1) / kWaves);
   hipLaunchKernelGGL((decode_partial_kernel<D, G, KT, VT>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

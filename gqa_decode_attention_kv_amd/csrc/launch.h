@@ -67,7 +67,7 @@ struct CombineArgs {
 };
 
 hipError_t launch_kv_produce(const ProduceArgs& a, hipStream_t stream);
-// total_work = t.work_prefix[t.n_seq]; grid = total_work x Hkv work-groups.
+// One wave per (work item, kv head): t.work_prefix[t.n_seq] * Hkv waves.
 hipError_t launch_decode_partial(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a,
                                  hipStream_t stream);
 hipError_t launch_decode_combine(int D, int B, const CombineArgs& a, hipStream_t stream);
