@@ -18,7 +18,8 @@ __device__ inline float wave_max(float x) {
 
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(CombineArgs a) {
-  constexpr int EPL = D / 64;
+  constexpr int EPL = D / 64;  // output elements per lane
+  constexpr int U = 8;         // splits whose partial rows are loaded together
   const int lane = threadIdx.x;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineArgs a) {
   const int ns = a.t.work_prefix[b + 1] - a.t.work_prefix[b];
   const int64_t row0 = (static_cast<int64_t>(b) * a.H + h) * a.max_splits + s0;
   const float* lse = a.part_lse + row0;
-  const float* po = a.part_o + row0 * D;
+  const float* po = a.part_o + row0 * D + lane;
 
   float M = -INFINITY;
   for (int s = lane; s < ns; s += 64) M = fmaxf(M, lse[s]);
@@ -36,11 +37,23 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineArgs a) {
   float num[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) num[e] = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = expf(lse[s] - M);
-    den += w;
+  for (int s = 0; s < ns; s += U) {
+    // Issue the loads of up to U splits before using any of them.
+    float w[U], v[U][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, po[static_cast<int64_t>(s) * D + lane + 64 * e], num[e]);
+    for (int u = 0; u < U; ++u) {
+      const int su = min(s + u, ns - 1);
+      w[u] = lse[su];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[u][e] = po[static_cast<int64_t>(su) * D + 64 * e];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wu = (s + u < ns) ? expf(w[u] - M) : 0.0f;
+      den += wu;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) num[e] = fmaf(wu, v[u][e], num[e]);
+    }
   }
   float* out = a.out + (static_cast<int64_t>(b) * a.H + h) * D;
 #pragma unroll

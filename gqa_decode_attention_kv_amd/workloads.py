@@ -135,10 +135,12 @@ WORKLOADS = {
                               Rope(NEOX, PLAIN, 1000000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),
                               window=0, softcap=50.0, split_size=512, seed=(5, 1)),
     # The measured workload: B=32 sequences of 8192 keys, 32/8 heads, d=128, bf16 KV.
+    # Split size 1024 (tuned): 8 splits per sequence, 2048 waves, one per wave slot
+    # of the GPU at the partial kernel's occupancy.
     "llama3.1-8b-b32-ctx8k": Workload("llama3.1-8b-b32-ctx8k", 32, 32, 8, 128, ("fixed", 8192),
                                       8192, BF16, BF16,
                                       Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
-                                      split_size=512, seed=(6,)),
+                                      split_size=1024, seed=(6,)),
 }
 
 HEADLINE = "llama3.1-8b-b32-ctx8k"
