@@ -113,8 +113,10 @@ def cpu_baseline(inputs, min_seconds: float = 10.0, max_rounds: int = 8) -> dict
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--min-warmup-s", type=float, default=0.3,
+                    help="keep warming up until this much wall time has passed (clocks settle)")
     ap.add_argument("--workload", default=None, help="workload name (default: the B=32 ctx-8K one)")
     ap.add_argument("--split-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -154,8 +156,16 @@ def main() -> int:
         print(f"bench: copy probe moved {n * 4} bytes each way", file=sys.stderr, flush=True)
         del src, dst
 
-    for _ in range(args.warmup):
+    # Warm-up: at least --warmup steps and --min-warmup-s seconds.  The first
+    # tens of milliseconds of GPU work in a process can run several times
+    # slower than steady state; they are kept out of the timed region.
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         st.step()
+        n_w += 1
+        if n_w % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -188,7 +198,7 @@ def main() -> int:
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": n_w,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -114,6 +114,9 @@ class Workload:
 
 
 # The workloads of the decode step.  Names give the model shape they follow.
+# Split sizes: 2 splits for the tiny step and 512 for the Llama-3.2-1B shape, as
+# those workloads are defined; elsewhere the size is a tuned launch parameter
+# (measured best on MI355X; the sizes are reported with every result).
 WORKLOADS = {
     # 128 cached tokens plus the new one at position 128; two splits of 65 keys.
     "tiny": Workload("tiny", 1, 4, 2, 64, ("fixed", 129), 129, F32, F32,
@@ -124,16 +127,16 @@ WORKLOADS = {
     "llama3.1-8b-ragged": Workload("llama3.1-8b-ragged", 32, 32, 8, 128, ("uniform", 512, 8192),
                                    8192, BF16, BF16,
                                    Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
-                                   split_size=512, seed=(3,)),
+                                   split_size=384, seed=(3,)),
     "qwen3-vq8": Workload("qwen3-vq8", 16, 32, 8, 128, ("fixed", 16384), 16384, BF16, I8,
                           Rope(NEOX, PLAIN, 1000000.0),
-                          QKNorm(True, 1e-6, 0, 1.0, 0.1), split_size=512, seed=(4,)),
+                          QKNorm(True, 1e-6, 0, 1.0, 0.1), split_size=1024, seed=(4,)),
     "gemma2-local": Workload("gemma2-local", 8, 16, 8, 256, ("fixed", 32768), 32768, BF16, BF16,
                              Rope(NEOX, PLAIN, 10000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),
-                             window=4096, softcap=50.0, split_size=512, seed=(5, 0)),
+                             window=4096, softcap=50.0, split_size=128, seed=(5, 0)),
     "gemma2-global": Workload("gemma2-global", 8, 16, 8, 256, ("fixed", 32768), 32768, BF16, BF16,
                               Rope(NEOX, PLAIN, 1000000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),
-                              window=0, softcap=50.0, split_size=512, seed=(5, 1)),
+                              window=0, softcap=50.0, split_size=1024, seed=(5, 1)),
     # The measured workload: B=32 sequences of 8192 keys, 32/8 heads, d=128, bf16 KV.
     # Split size 1024 (tuned): 8 splits per sequence, 2048 waves, one per wave slot
     # of the GPU at the partial kernel's occupancy.
