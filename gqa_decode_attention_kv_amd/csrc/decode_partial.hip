@@ -132,9 +132,11 @@ __device__ inline void widen(const u32x4& w, float (&out)[E]) {
       out[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
     }
   } else {
+    // vq8 codes are widened as code + 128 (one v_cvt_f32_ubyte per code after
+    // flipping the sign bits); the caller removes 128 * sum(p) at the end.
 #pragma unroll
     for (int e = 0; e < 16; ++e)
-      out[e] = static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(w[e >> 2] >> (8 * (e & 3)))));
+      out[e] = static_cast<float>(((w[e >> 2] ^ 0x80808080u) >> (8 * (e & 3))) & 0xFFu);
   }
 }
 
@@ -143,8 +145,12 @@ struct Elem {
   static constexpr int bytes = DT == kF32 ? 4 : (DT == kBF16 ? 2 : 1);
 };
 
+// amdgpu_waves_per_eu(2, 8): at least two waves per SIMD.  Without the hint
+// the allocator spends registers freely (the vq8 kernel spilled into AGPRs at
+// one wave per SIMD); with it the bf16 d128 kernel fits three waves per SIMD.
 template <int D, int G, int KT, int VT>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void
+decode_partial_kernel(AttnArgs a) {
   constexpr int KB = Elem<KT>::bytes, VB = Elem<VT>::bytes;
   constexpr int KLPR = D * KB / 16;  // lanes per K row
   constexpr int KRPL = 64 / KLPR;    // K rows per wave load
@@ -152,8 +158,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
   constexpr int VLPR = D * VB / 16;
   constexpr int VRPL = 64 / VLPR;
   constexpr int VE = 16 / VB;
-  constexpr int UK = (kLoadsInFlight * KRPL <= kRowsPerChunk) ? kLoadsInFlight : kRowsPerChunk / KRPL;
-  constexpr int UV = (kLoadsInFlight * VRPL <= kRowsPerChunk) ? kLoadsInFlight : kRowsPerChunk / VRPL;
+  // Eight 16-byte loads per lane in flight; four for G = 8, whose query and
+  // accumulator registers would otherwise leave room for one wave per SIMD.
+  constexpr int LF = G >= 8 ? kLoadsInFlight / 2 : kLoadsInFlight;
+  constexpr int UK = (LF * KRPL <= kRowsPerChunk) ? LF : kRowsPerChunk / KRPL;
+  constexpr int UV = (LF * VRPL <= kRowsPerChunk) ? LF : kRowsPerChunk / VRPL;
+  constexpr int kScaleRegs = (VT == kI8) ? kRowsPerChunk / 64 : 1;
   static_assert(kRowsPerChunk % (UK * KRPL) == 0 && kRowsPerChunk % (UV * VRPL) == 0, "tiling");
   static_assert(KLPR >= 4 && VLPR >= 4, "row must span at least a quad");
 
@@ -206,10 +216,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
   float m_run[G], l_run[G];
+  float psum[G];  // vq8: sum of this lane's scaled weights (removes the +128 of the codes)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m_run[g] = -INFINITY;
     l_run[g] = 0.0f;
+    psum[g] = 0.0f;
   }
 
   float* sc = smem + wave * (kRowsPerChunk * G);  // this wave's [row][G] scores / weights
@@ -230,6 +242,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
     auto voff = [&](int t) -> uint32_t {
       return static_cast<uint32_t>(min(t * VRPL + vr, nrows - 1) * (D * VB) + vc * 16);
     };
+
+    // vq8: the chunk's per-token scales are requested now and used by the
+    // weights pass; row r = lane + 64 i sits in register i.
+    float sreg[kScaleRegs];
+    if constexpr (VT == kI8) {
+#pragma unroll
+      for (int i = 0; i < kScaleRegs; ++i) sreg[i] = sbase[a0 + min(lane + 64 * i, nrows - 1)];
+    }
 
     // ---- pass 1: raw scores of the chunk's rows (rolling prefetch) ----------
     // Rows past the chunk's end hold duplicates of its last row; the weights
@@ -300,20 +320,26 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
       l_run[g] *= alpha;
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
+      psum[g] *= alpha;
       m_run[g] = m_new;
     }
 
     // ---- weights p = 2^(s - m) for every row the value tiles cover (0 past
     // the end); vq8 folds the token's scale into p ---------------------------
-    for (int r = lane; r < nv * VRPL; r += 64) {
-      const bool ok = r < nrows;
-      const float vs = (VT == kI8) ? sbase[a0 + min(r, nrows - 1)] : 1.0f;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p =
-            ok ? __builtin_amdgcn_exp2f(capped_log2(sc[r * G + g], capped, cap_c, cap_inv) - m_run[g]) : 0.0f;
-        l_run[g] += p;
-        sc[r * G + g] = p * vs;
+    for (int i = 0; i < kRowsPerChunk / 64; ++i) {
+      const int r = lane + 64 * i;
+      if (64 * i >= nv * VRPL) break;  // wave-uniform
+      if (r < nv * VRPL) {
+        const bool ok = r < nrows;
+        const float vs = (VT == kI8) ? sreg[VT == kI8 ? i : 0] : 1.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p =
+              ok ? __builtin_amdgcn_exp2f(capped_log2(sc[r * G + g], capped, cap_c, cap_inv) - m_run[g]) : 0.0f;
+          l_run[g] += p;
+          sc[r * G + g] = p * vs;
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -326,9 +352,11 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
 #pragma unroll
       for (int g = 0; g < G; ++g) p[g] = sc[r * G + g];
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(p[g], vf[e], acc[g][e]);
+        if constexpr (VT == kI8) psum[g] += p[g];
+      }
     };
     t0 = 0;
     for (; t0 + 2 * UV <= nv; t0 += UV) {
@@ -360,12 +388,18 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(AttnArgs a) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     l_run[g] = wave_sum(l_run[g]);
+    if constexpr (VT == kI8) {
+      // Each row's weight sits in every lane of the row; summing one lane
+      // per row group counts it once.
+#pragma unroll
+      for (int m = VLPR; m < 64; m <<= 1) psum[g] += __shfl_xor(psum[g], m);
+    }
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       float x = acc[g][e];
 #pragma unroll
       for (int m = VLPR; m < 64; m <<= 1) x += __shfl_xor(x, m);
-      acc[g][e] = x;
+      acc[g][e] = (VT == kI8) ? fmaf(-128.0f, psum[g], x) : x;
     }
   }
   const int64_t row0 = (static_cast<int64_t>(b) * a.H + kvh * G) * a.max_splits + sigma;
