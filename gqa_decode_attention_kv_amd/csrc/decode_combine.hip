@@ -11,11 +11,6 @@
 namespace uaii {
 namespace {
 
-__device__ inline float wave_max(float x) {
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
-
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(CombineArgs a) {
   constexpr int EPL = D / 64;  // output elements per lane
@@ -29,16 +24,13 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineArgs a) {
   const float* lse = a.part_lse + row0;
   const float* po = a.part_o + row0 * D + lane;
 
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, lse[s]);
-  M = wave_max(M);
-
-  float den = 0.0f;
+  // One pass with a running max: the loads of U splits are issued together,
+  // and for up to U splits no cross-lane reduction is needed at all.
+  float M = -INFINITY, den = 0.0f;
   float num[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) num[e] = 0.0f;
   for (int s = 0; s < ns; s += U) {
-    // Issue the loads of up to U splits before using any of them.
     float w[U], v[U][EPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -47,13 +39,22 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) v[u][e] = po[static_cast<int64_t>(su) * D + 64 * e];
     }
+    float bm = w[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) bm = fmaxf(bm, w[u]);  // clamped duplicates do not change it
+    const float m_new = fmaxf(M, bm);
+    const float alpha = (M == -INFINITY) ? 0.0f : expf(M - m_new);
+    den *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) num[e] *= alpha;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float wu = (s + u < ns) ? expf(w[u] - M) : 0.0f;
+      const float wu = (s + u < ns) ? expf(w[u] - m_new) : 0.0f;
       den += wu;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) num[e] = fmaf(wu, v[u][e], num[e]);
     }
+    M = m_new;
   }
   float* out = a.out + (static_cast<int64_t>(b) * a.H + h) * D;
 #pragma unroll

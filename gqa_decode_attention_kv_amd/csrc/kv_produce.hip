@@ -66,7 +66,8 @@ __device__ inline double rope_freq(const ProduceArgs& a, int i) {
 
 template <int D>
 __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
-  constexpr int EPL = D / 64;  // elements per lane
+  constexpr int EPL = D / 64;                     // elements per lane
+  constexpr int NP = (D / 2 + 63) / 64;           // rotation pairs per lane
   __shared__ double sx[D];
   const int lane = threadIdx.x;
   const int x = blockIdx.x;
@@ -75,12 +76,31 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
   const bool is_q = x < a.H;
   const int u = x - a.H;
 
+  // Loads first; the data-independent angles below overlap with them.
   const float* src = is_q ? a.q_in + (static_cast<int64_t>(b) * a.H + x) * D
                           : a.k_in + (static_cast<int64_t>(b) * a.Hkv + u) * D;
+  float xin[EPL], v[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) xin[e] = src[lane + 64 * e];
+  if (!is_q) {
+    const float* vsrc = a.v_in + (static_cast<int64_t>(b) * a.Hkv + u) * D;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] = vsrc[lane + 64 * e];
+  }
+
+  // cos/sin of pos * g_i for this lane's pairs i = lane + 64 j.
+  double cs[NP], sn[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int i = lane + 64 * j;
+    cs[j] = 1.0;
+    sn[j] = 0.0;
+    if (i < D / 2) sincos(static_cast<double>(pos) * rope_freq(a, i), &sn[j], &cs[j]);
+  }
+
   double xv[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) xv[e] = static_cast<double>(src[lane + 64 * e]);
-
+  for (int e = 0; e < EPL; ++e) xv[e] = static_cast<double>(xin[e]);
   if (a.norm_enabled) {
     const float* w = is_q ? a.w_q : a.w_k;
     double ss = 0.0;
@@ -97,15 +117,16 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
   __syncthreads();
 
   const int64_t slot = (is_q ? 0 : ((static_cast<int64_t>(b) * a.Hkv + u) * a.cap + pos)) * D;
-  for (int i = lane; i < D / 2; i += 64) {
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int i = lane + 64 * j;
+    if (i >= D / 2) break;
     const int ia = (a.pairing == kNeox) ? i : 2 * i;
     const int ib = (a.pairing == kNeox) ? i + D / 2 : 2 * i + 1;
-    const double t = static_cast<double>(pos) * rope_freq(a, i);
-    double s, c;
-    sincos(t, &s, &c);
+    const double c = cs[j], sv = sn[j];
     const double xa = sx[ia], xb = sx[ib];
-    const double ya = xa * c - xb * s;
-    const double yb = xa * s + xb * c;
+    const double ya = xa * c - xb * sv;
+    const double yb = xa * sv + xb * c;
     if (is_q) {
       float* q = a.q_out + (static_cast<int64_t>(b) * a.H + x) * D;
       q[ia] = static_cast<float>(ya);
@@ -123,10 +144,6 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
   if (is_q) return;
 
   // Value of (b, u): stored as given (f32), rounded to bf16, or quantised.
-  const float* vsrc = a.v_in + (static_cast<int64_t>(b) * a.Hkv + u) * D;
-  float v[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) v[e] = vsrc[lane + 64 * e];
   if (a.v_dtype == kF32) {
     float* dst = static_cast<float*>(a.v) + slot;
 #pragma unroll

@@ -124,3 +124,77 @@ def check_slot(w: W.Workload, gpu: dict, ref: dict, q_gpu: np.ndarray, q_ref: np
         assert np.array_equal(gpu["scale"].view(np.uint32), ref["scale"].view(np.uint32)), \
             "vq8 scales differ (must be bit-exact)"
     return res
+
+
+def run_gpu(inputs, split_size=None):
+    """One step on the GPU with NaN-filled partial buffers (so unwritten
+    entries stay detectable)."""
+    import torch
+    from gqa_decode_attention_kv_amd.step import DeviceStep
+    st = DeviceStep(inputs, split_size=split_size)
+    st.part_o.fill_(float("nan"))
+    st.part_lse.fill_(float("nan"))
+    st.step()
+    torch.cuda.synchronize()
+    return st
+
+
+def compare_partials(st, ref, w, lens, pick=None, max_per_seq=None, rng=None):
+    """Every valid split partial (or a sample) against the oracle's; splits
+    outside the visible range must stay unwritten (NaN)."""
+    po = st.part_o.cpu().numpy()
+    pl = st.part_lse.cpu().numpy()
+    worst = 0.0
+    for b, L in enumerate(lens):
+        valid = valid_splits(w, int(L), st.split_size)
+        vset = set(valid)
+        invalid = [sg for sg in range(st.max_splits) if sg not in vset]
+        heads = range(w.n_heads) if pick is None else pick(b)
+        for h in heads:
+            if invalid:
+                assert np.all(np.isnan(po[b, h, invalid])) and np.all(np.isnan(pl[b, h, invalid])), \
+                    f"partial ({b},{h}) outside the visible range was written"
+            chk = valid
+            if pick is not None:
+                chk = sorted({valid[0], valid[-1]})
+            elif max_per_seq is not None and len(valid) > max_per_seq:
+                chk = sorted({valid[0], valid[-1], *rng.choice(valid, max_per_seq - 2, replace=False).tolist()})
+            for sg in chk:
+                o, lse, n = ref.partial(b, h, sg, st.split_size)
+                assert n > 0
+                e_o = float(np.max(np.abs(po[b, h, sg] - o)))
+                e_l = abs(float(pl[b, h, sg]) - lse)
+                worst = max(worst, e_o)
+                assert e_o <= out_tolerance(w, o)[0], (b, h, sg, e_o)
+                assert e_l <= 1e-4 * max(1.0, abs(lse)), (b, h, sg, e_l, lse)
+    return worst
+
+
+def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0):
+    """Run one step on the GPU and in the oracle; compare every output element,
+    the produced cache rows (and that nothing else in the caches changed) and
+    the split partials.  Returns (max abs error, tolerance, class)."""
+    lens = np.asarray(lens, dtype=np.int32)
+    say(f"case {w.name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
+        f"K/V={w.k_dtype}/{w.v_dtype} lens={lens.tolist()[:8]} S={w.split_size} W={w.window} "
+        f"cap={w.softcap} rope={w.rope.pairing}/{w.rope.scaling} norm={w.qk_norm.enabled}")
+    inputs = W.make_inputs(w, seq_lens=lens)
+    ck0, cv0 = inputs.cache_k.copy(), inputs.cache_v.copy()
+    st = run_gpu(inputs)
+    ref = OracleStep(inputs)
+    out = st.out.cpu().numpy()
+    want = ref.decode().reshape(out.shape)
+    tol, cls = out_tolerance(w, want)
+    err = float(np.max(np.abs(out - want)))
+    check_slot(w, st.cache_rows(), ref.slot_rows(), st.q_out.cpu().numpy(), ref.q)
+    compare_partials(st, ref, w, lens, max_per_seq=max_partials_per_seq,
+                     rng=np.random.default_rng(seed))
+    mask = np.ones(ck0.shape[:3], bool)
+    mask[np.arange(w.batch), :, inputs.positions] = False
+    for dev, host in ((st.cache_k, ck0), (st.cache_v, cv0)):
+        g = dev.cpu().numpy().view(host.dtype)
+        assert np.array_equal(g[mask].view(np.uint8), host[mask].view(np.uint8)), \
+            "cache rows other than the new token's slot changed"
+    say(f"  max abs err {err:.3g} (tol {tol:.3g}, {cls})")
+    assert err <= tol, (err, tol)
+    return err, tol, cls

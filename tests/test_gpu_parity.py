@@ -70,62 +70,14 @@ SMALL = [
 ]
 
 
-def run_gpu(inputs, split_size=None):
-    from gqa_decode_attention_kv_amd.step import DeviceStep
-    st = DeviceStep(inputs, split_size=split_size)
-    st.part_o.fill_(float("nan"))
-    st.part_lse.fill_(float("nan"))
-    st.step()
-    torch.cuda.synchronize()
-    return st
-
-
-def compare_partials(st, ref, w, lens, pick=None):
-    po = st.part_o.cpu().numpy()
-    pl = st.part_lse.cpu().numpy()
-    worst = 0.0
-    for b, L in enumerate(lens):
-        valid = P.valid_splits(w, int(L), st.split_size)
-        for h in (range(w.n_heads) if pick is None else pick(b)):
-            for sg in range(st.max_splits):
-                if sg not in valid:
-                    assert np.all(np.isnan(po[b, h, sg])) and np.isnan(pl[b, h, sg]), \
-                        f"partial ({b},{h},{sg}) outside the visible range was written"
-                    continue
-                if pick is not None and sg not in (valid[0], valid[-1]):
-                    continue
-                o, lse, n = ref.partial(b, h, sg, st.split_size)
-                assert n > 0
-                e_o = np.max(np.abs(po[b, h, sg] - o))
-                e_l = abs(pl[b, h, sg] - lse)
-                worst = max(worst, e_o)
-                assert e_o <= P.out_tolerance(w, o)[0], (b, h, sg, e_o)
-                assert e_l <= 1e-4 * max(1.0, abs(lse)), (b, h, sg, e_l, lse)
-    return worst
+run_gpu = P.run_gpu
+compare_partials = P.compare_partials
 
 
 @pytest.mark.parametrize("spec", SMALL, ids=[c[0].name for c in SMALL])
 def test_small_case(spec):
     w, lens = spec
-    P.say(f"case {w.name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} lens={lens.tolist()[:8]} S={w.split_size}")
-    inputs = W.make_inputs(w, seq_lens=lens)
-    ck0, cv0 = inputs.cache_k.copy(), inputs.cache_v.copy()
-    st = run_gpu(inputs)
-    ref = P.OracleStep(inputs)
-    out = st.out.cpu().numpy()
-    want = ref.decode().reshape(out.shape)
-    tol, cls = P.out_tolerance(w, want)
-    err = float(np.max(np.abs(out - want)))
-    P.check_slot(w, st.cache_rows(), ref.slot_rows(), st.q_out.cpu().numpy(), ref.q)
-    compare_partials(st, ref, w, lens)
-    # only the new token's slot of the cache changed
-    mask = np.ones(ck0.shape[:3], bool)
-    mask[np.arange(w.batch), :, inputs.positions] = False
-    for dev, host in ((st.cache_k, ck0), (st.cache_v, cv0)):
-        g = dev.cpu().numpy().view(host.dtype)
-        assert np.array_equal(g[mask].view(np.uint8), host[mask].view(np.uint8))
-    P.say(f"  max abs err {err:.3g} (tol {tol:.3g}, {cls})")
-    assert err <= tol
+    P.run_and_compare(w, lens)
 
 
 FULL = ["tiny", "llama3.2-1b", "llama3.1-8b-ragged", "qwen3-vq8", "gemma2-local", "gemma2-global",
