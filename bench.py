@@ -119,6 +119,8 @@ def main() -> int:
                     help="keep warming up until this much wall time has passed (clocks settle)")
     ap.add_argument("--workload", default=None, help="workload name (default: the B=32 ctx-8K one)")
     ap.add_argument("--split-size", type=int, default=None)
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK_SIZE",
+                    help="use the paged cache layout with this block size (0: contiguous)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -144,7 +146,8 @@ def main() -> int:
     inputs = W.make_inputs(w)
     t_gen = time.perf_counter() - t_gen
     print(f"bench: {name} inputs generated in {t_gen:.1f} s", file=sys.stderr, flush=True)
-    st = DeviceStep(inputs, split_size=args.split_size)
+    paged = W.make_paged(inputs, args.paged) if args.paged else None
+    st = DeviceStep(inputs, split_size=args.split_size, paged=paged)
     kv_bytes = w.kv_bytes()
 
     if args.copy_probe:
@@ -198,7 +201,7 @@ def main() -> int:
 
     step_gbs = kv_bytes / (ms_step * 1e-3) / 1e9
     attn_gbs = kv_bytes / (attn_mean * 1e-3) / 1e9
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name) if not args.paged else None
     result = {
         "metric": METRIC,
         "value": round(step_gbs, 2),
@@ -217,6 +220,7 @@ def main() -> int:
                    "kv_cache": {0: "f32", 1: "bf16", 2: "int8"}[w.k_dtype] + "/" +
                    {0: "f32", 1: "bf16", 2: "int8(vq8)"}[w.v_dtype],
                    "split_size": st.split_size, "window": w.window, "softcap": w.softcap,
+                   "layout": f"paged(block_size={args.paged})" if args.paged else "contiguous",
                    "parallelism": "single-gpu"},
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(w.batch / (ms_step * 1e-3), 1),

@@ -49,7 +49,9 @@ class QKNorm(C.Structure):
 
 class KVCache(C.Structure):
     _fields_ = [("k_dtype", C.c_int32), ("v_dtype", C.c_int32), ("capacity", C.c_int32),
-                ("k", C.c_void_p), ("v", C.c_void_p), ("v_scale", C.c_void_p)]
+                ("k", C.c_void_p), ("v", C.c_void_p), ("v_scale", C.c_void_p),
+                ("block_table", C.c_void_p), ("block_size", C.c_int32),
+                ("max_blocks", C.c_int32), ("num_blocks", C.c_int32)]
 
 
 _lib = None

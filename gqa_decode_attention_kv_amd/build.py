@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libuaii_decode.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "kv_produce.hip", "decode_partial.hip", "decode_combine.hip"]
+SOURCES = ["api.cpp", "kv_produce.hip", "decode_partial.hip", "decode_partial_paged.hip",
+           "decode_combine.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -90,6 +90,17 @@ uaii_status check_cache(const char* fn, const uaii_kv_cache* c) {
   REQUIRE(c->capacity >= 1, kInvalid, "capacity=%d is invalid (must be >= 1)", c->capacity);
   REQUIRE(c->capacity <= kMaxCapacity, kNotImpl, "capacity=%d is not supported (supported: 1..%d)",
           c->capacity, kMaxCapacity);
+  if (c->block_table != nullptr) {
+    const int32_t bs = c->block_size;
+    REQUIRE(bs >= 16 && bs <= 1024 && (bs & (bs - 1)) == 0, kNotImpl,
+            "block_size=%d is not supported (supported: a power of two in [16, 1024])", bs);
+    REQUIRE(c->max_blocks >= 1, kInvalid, "max_blocks=%d is invalid (must be >= 1)", c->max_blocks);
+    REQUIRE(c->num_blocks >= 1, kInvalid, "num_blocks=%d is invalid (must be >= 1)", c->num_blocks);
+    REQUIRE(static_cast<int64_t>(c->max_blocks) * bs == c->capacity, kInvalid,
+            "capacity=%d must equal max_blocks*block_size=%lld for a paged cache", c->capacity,
+            static_cast<long long>(c->max_blocks) * bs);
+    CHECK_PTR("cache.block_table", c->block_table, 4);
+  }
   CHECK_PTR("cache.k", c->k, 16);
   CHECK_PTR("cache.v", c->v, 16);
   if (c->v_dtype == UAII_I8) {
@@ -238,6 +249,10 @@ uaii_status uaii_kv_produce(const uaii_attn_shape* shape, const uaii_rope* rope,
   a.v = cache->v;
   a.v_scale = cache->v_scale;
   a.q_out = q_out;
+  a.block_table = cache->block_table;
+  a.block_size = cache->block_table ? cache->block_size : 0;
+  a.max_blocks = cache->block_table ? cache->max_blocks : 0;
+  a.num_blocks = cache->block_table ? cache->num_blocks : 0;
   for (int b = 0; b < shape->batch; ++b) a.pos[b] = positions[b];
   return device_status(fn, uaii::launch_kv_produce(a, static_cast<hipStream_t>(stream)));
 }
@@ -284,6 +299,17 @@ uaii_status uaii_decode_attn(const uaii_attn_shape* shape, const uaii_kv_cache* 
   a.softcap = softcap;
   build_table(shape->batch, seq_lens, window, split_size, &a.t);
   const int G = shape->n_heads / shape->n_kv_heads;
+  if (cache->block_table != nullptr) {
+    a.block_table = cache->block_table;
+    a.block_size = cache->block_size;
+    a.log2_bs = 0;
+    while ((1 << a.log2_bs) < cache->block_size) ++a.log2_bs;
+    a.max_blocks = cache->max_blocks;
+    a.num_blocks = cache->num_blocks;
+    return device_status(fn, uaii::launch_decode_partial_paged(shape->head_dim, G, cache->k_dtype,
+                                                               cache->v_dtype, a,
+                                                               static_cast<hipStream_t>(stream)));
+  }
   return device_status(fn, uaii::launch_decode_partial(shape->head_dim, G, cache->k_dtype,
                                                        cache->v_dtype, a,
                                                        static_cast<hipStream_t>(stream)));

@@ -1,466 +1,12 @@
-// Split-K flash-decoding partials for grouped-query attention, one query
-// token per sequence, over B <= 32 ragged sequences.
-//
-// Sources: "Algenta - Model support matrix" (Kernel path capabilities:
-// split-K decode partials, batched decode partial with B <= 32; Structural
-// fact requirements: GQA ratio, attention scale 1/sqrt(head_dim));
-// "Universal AI Inference - Hugging Face decoder completeness" (P1.4:
-// sliding window and attention-logit softcap as a tanh clip); "llamay -
-// Models and formats" (The KV cache, in three precisions: vq8 values).
-//
-// Design (gfx950, bandwidth bound, no MFMA: one query row per kv head is a
-// GEMV; arithmetic intensity is 2-5 flop per KV byte, far below the ridge):
-//   * one wave64 per (sequence, kv head, split) work item, taken from a
-//     flattened per-sequence work table, so ragged batches and windows only
-//     launch waves that hold visible keys; four independent waves share a
-//     work-group but never synchronise (no barriers, no cross-wave merge);
-//   * the G query heads that share the kv head are held in registers, so
-//     every K and V byte is read from HBM exactly once per group;
-//   * a wave walks its split in chunks of up to 512 rows with two passes per
-//     chunk: K (16-byte coalesced loads, a row spread over d*sizeof(K)/16
-//     lanes, scores reduced across those lanes with DPP) with raw scores
-//     parked in LDS, then V with the softmax weights broadcast from LDS; the
-//     running max and sum rescale only between chunks;
-//   * scores live in the log2 domain (q pre-multiplied by scale*log2 e) so the
-//     exponential is one v_exp_f32; with a softcap the tanh clip is applied
-//     in the weights pass (it is monotonic, so the max commutes with it);
-//   * vq8: int8 codes are widened in registers and the per-token scale is
-//     folded into the softmax weight, so dequantisation costs no extra pass;
-//   * at the end the wave sums its row groups across lanes and writes one
-//     normalised partial and its log-sum-exp per query head.
-// Loads run as a rolling pipeline (the next tiles are requested as soon as
-// the current one is widened, and the first value tiles before the softmax
-// weights are computed).  Every load addresses a row inside the visible
-// range (rows past a chunk's end are clamped to its last row and masked
-// afterwards), so memory outside the visible keys is never read and masked
-// lanes never touch poisoned values.
-#include "launch.h"
-
-#include <math.h>
+// Split-K decode partials over contiguous per-sequence caches
+// [B][Hkv][capacity][d]; the kernel itself is in decode_partial_kernel.h.
+#include "decode_partial_kernel.h"
 
 namespace uaii {
-namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWaves = 4;                  // independent waves per work-group
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerChunk = 512;         // rows a wave scores before it reads values
-constexpr int kLoadsInFlight = 8;          // 16-byte loads per lane kept in flight
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-template <int CTRL>
-__device__ inline float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over aligned groups of N lanes (N in {4, 8, 16, 32, 64}); every lane of
-// a group receives the group's sum.
-template <int N>
-__device__ inline float group_sum(float x) {
-  x += dpp<0xB1>(x);                        // quad_perm [1,0,3,2]: lane ^ 1
-  x += dpp<0x4E>(x);                        // quad_perm [2,3,0,1]: lane ^ 2
-  if constexpr (N >= 8) x += dpp<0x141>(x);   // row_half_mirror: pairs the quads of 8
-  if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror: pairs the halves of 16
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
-  return x;
-}
-
-// group_sum over G independent values, stage by stage, so consecutive DPP
-// operations read registers written G instructions earlier (no hazard stalls).
-template <int N, int G>
-__device__ inline void group_sum_n(float (&x)[G]) {
-#pragma unroll
-  for (int g = 0; g < G; ++g) x[g] += dpp<0xB1>(x[g]);
-#pragma unroll
-  for (int g = 0; g < G; ++g) x[g] += dpp<0x4E>(x[g]);
-  if constexpr (N >= 8) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) x[g] += dpp<0x141>(x[g]);
-  }
-  if constexpr (N >= 16) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) x[g] += dpp<0x140>(x[g]);
-  }
-  if constexpr (N >= 32) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) x[g] += __shfl_xor(x[g], 16);
-  }
-  if constexpr (N >= 64) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) x[g] += __shfl_xor(x[g], 32);
-  }
-}
-
-__device__ inline float wave_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));
-  x = fmaxf(x, dpp<0x4E>(x));
-  x = fmaxf(x, dpp<0x141>(x));
-  x = fmaxf(x, dpp<0x140>(x));
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-
-__device__ inline float wave_sum(float x) { return group_sum<64>(x); }
-
-// KV rows are read once per step: non-temporal loads stream them past the
-// caches instead of evicting reusable lines (worth about 8% of bandwidth).
-__device__ inline u32x4 load16(const void* p) {
-  return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
-}
-
-// Score in the log2 domain from a raw score: with a softcap c the raw score is
-// the natural-scale s and the result is c*tanh(s/c)*log2(e); without one the
-// raw score already carries the log2(e) factor.  Monotonic in s.
-__device__ inline float capped_log2(float s, bool capped, float c, float c_inv) {
-  return capped ? c * tanhf(s * c_inv) * kLog2e : s;
-}
-
-// Widen the 16 bytes of one lane to E floats.
-template <int DT, int E>
-__device__ inline void widen(const u32x4& w, float (&out)[E]) {
-  if constexpr (DT == kF32) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = __uint_as_float(w[e]);
-  } else if constexpr (DT == kBF16) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      out[2 * e] = __uint_as_float(w[e] << 16);
-      out[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-    }
-  } else {
-    // vq8 codes are widened as code + 128 (one v_cvt_f32_ubyte per code after
-    // flipping the sign bits); the caller removes 128 * sum(p) at the end.
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      out[e] = static_cast<float>(((w[e >> 2] ^ 0x80808080u) >> (8 * (e & 3))) & 0xFFu);
-  }
-}
-
-template <int DT>
-struct Elem {
-  static constexpr int bytes = DT == kF32 ? 4 : (DT == kBF16 ? 2 : 1);
-};
-
-// amdgpu_waves_per_eu(2, 8): at least two waves per SIMD.  Without the hint
-// the allocator spends registers freely (the vq8 kernel spilled into AGPRs at
-// one wave per SIMD); with it the bf16 d128 kernel fits three waves per SIMD.
-template <int D, int G, int KT, int VT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void
-decode_partial_kernel(AttnArgs a) {
-  constexpr int KB = Elem<KT>::bytes, VB = Elem<VT>::bytes;
-  constexpr int KLPR = D * KB / 16;  // lanes per K row
-  constexpr int KRPL = 64 / KLPR;    // K rows per wave load
-  constexpr int KE = 16 / KB;        // K elements per lane
-  constexpr int VLPR = D * VB / 16;
-  constexpr int VRPL = 64 / VLPR;
-  constexpr int VE = 16 / VB;
-  // Eight 16-byte loads per lane in flight; four for G = 8, whose query and
-  // accumulator registers would otherwise leave room for one wave per SIMD.
-  constexpr int LF = G >= 8 ? kLoadsInFlight / 2 : kLoadsInFlight;
-  constexpr int UK = (LF * KRPL <= kRowsPerChunk) ? LF : kRowsPerChunk / KRPL;
-  constexpr int UV = (LF * VRPL <= kRowsPerChunk) ? LF : kRowsPerChunk / VRPL;
-  constexpr int kScaleRegs = (VT == kI8) ? kRowsPerChunk / 64 : 1;
-  static_assert(kRowsPerChunk % (UK * KRPL) == 0 && kRowsPerChunk % (UV * VRPL) == 0, "tiling");
-  static_assert(KLPR >= 4 && VLPR >= 4, "row must span at least a quad");
-
-  __shared__ __attribute__((aligned(16))) float smem[kWaves * kRowsPerChunk * G];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  // Work item of this wave: (work index w, kv head); w names (sequence, split).
-  const int item = blockIdx.x * kWaves + wave;
-  const int total = a.t.work_prefix[a.t.n_seq] * a.Hkv;
-  if (item >= total) return;  // no barriers below: idle waves leave at once
-  const int kvh = item % a.Hkv;
-  const int w = item / a.Hkv;
-  int b = 0;
-  for (int i = 1; i < a.t.n_seq; ++i) b += (w >= a.t.work_prefix[i]) ? 1 : 0;
-  const int sigma = a.t.first_split[b] + (w - a.t.work_prefix[b]);
-  const int r0 = max(sigma * a.split_size, a.t.lo[b]);
-  const int r1 = min((sigma + 1) * a.split_size, a.t.len[b]);
-
-  const int64_t slab = (static_cast<int64_t>(b) * a.Hkv + kvh) * a.cap;  // first row of (b, kvh)
-  const char* kbase = static_cast<const char*>(a.k) + slab * (D * KB);
-  const char* vbase = static_cast<const char*>(a.v) + slab * (D * VB);
-  const float* sbase = (VT == kI8) ? a.v_scale + slab : nullptr;
-
-  // Query group in registers: lane holds q[h][kc*KE .. kc*KE + KE) for its K segment.
-  const int kr = lane / KLPR, kc = lane % KLPR;
-  float q[G][KE];
-  {
-    const float* qb = a.q + (static_cast<int64_t>(b) * a.H + kvh * G) * D + kc * KE;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < KE; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(qb + g * D + e);
-        q[g][e] = v.x * a.q_mul;
-        q[g][e + 1] = v.y * a.q_mul;
-        q[g][e + 2] = v.z * a.q_mul;
-        q[g][e + 3] = v.w * a.q_mul;
-      }
-    }
-  }
-  const bool capped = a.softcap > 0.0f;
-  const float cap_c = a.softcap, cap_inv = capped ? 1.0f / a.softcap : 0.0f;
-
-  const int vr = lane / VLPR, vc = lane % VLPR;
-  float acc[G][VE];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
-  float m_run[G], l_run[G];
-  float psum[G];  // vq8: sum of this lane's scaled weights (removes the +128 of the codes)
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.0f;
-    psum[g] = 0.0f;
-  }
-
-  float* sc = smem + wave * (kRowsPerChunk * G);  // this wave's [row][G] scores / weights
-
-  for (int a0 = r0; a0 < r1; a0 += kRowsPerChunk) {
-    const int nrows = min(kRowsPerChunk, r1 - a0);  // rows [a0, a0 + nrows), wave-uniform
-
-    // Loads address row min(row, nrows - 1): every load is unconditional and
-    // in the visible range; rows past the end are masked after the load.
-    // Addresses are a wave-uniform base plus a 32-bit lane offset.
-    const char* kblk = kbase + static_cast<int64_t>(a0) * (D * KB);
-    const char* vblk = vbase + static_cast<int64_t>(a0) * (D * VB);
-    const int nk = (nrows + KRPL - 1) / KRPL;  // K tiles of KRPL rows
-    const int nv = (nrows + VRPL - 1) / VRPL;  // V tiles of VRPL rows
-    auto koff = [&](int t) -> uint32_t {
-      return static_cast<uint32_t>(min(t * KRPL + kr, nrows - 1) * (D * KB) + kc * 16);
-    };
-    auto voff = [&](int t) -> uint32_t {
-      return static_cast<uint32_t>(min(t * VRPL + vr, nrows - 1) * (D * VB) + vc * 16);
-    };
-
-    // vq8: the chunk's per-token scales are requested now and used by the
-    // weights pass; row r = lane + 64 i sits in register i.
-    float sreg[kScaleRegs];
-    if constexpr (VT == kI8) {
-#pragma unroll
-      for (int i = 0; i < kScaleRegs; ++i) sreg[i] = sbase[a0 + min(lane + 64 * i, nrows - 1)];
-    }
-
-    // ---- pass 1: raw scores of the chunk's rows (rolling prefetch) ----------
-    // Rows past the chunk's end hold duplicates of its last row; the weights
-    // pass ignores them.  Each tile's registers are reloaded as soon as the
-    // tile has been widened.  The steady-state loop has no branches (every
-    // tile and every reload is in range) so the compiler can count loads in
-    // flight exactly; the last one or two batches run in a guarded tail.
-    u32x4 kd[UK];
-    auto k_scores = [&](const float (&kf)[KE], int r) {
-      float s[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float p = q[g][0] * kf[0];
-#pragma unroll
-        for (int e = 1; e < KE; ++e) p = fmaf(q[g][e], kf[e], p);
-        s[g] = p;
-      }
-      group_sum_n<KLPR, G>(s);
-      if (kc == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) sc[r * G + g] = s[g];
-      }
-    };
-#pragma unroll
-    for (int u = 0; u < UK; ++u) kd[u] = load16(kblk + koff(min(u, nk - 1)));
-    int t0 = 0;
-    for (; t0 + 2 * UK <= nk; t0 += UK) {
-#pragma unroll
-      for (int u = 0; u < UK; ++u) {
-        float kf[KE];
-        widen<KT, KE>(kd[u], kf);
-        kd[u] = load16(kblk + koff(t0 + UK + u));
-        k_scores(kf, (t0 + u) * KRPL + kr);
-      }
-    }
-    for (; t0 < nk; t0 += UK) {
-#pragma unroll
-      for (int u = 0; u < UK; ++u) {
-        if (t0 + u < nk) {
-          float kf[KE];
-          widen<KT, KE>(kd[u], kf);
-          if (t0 + UK + u < nk) kd[u] = load16(kblk + koff(t0 + UK + u));
-          k_scores(kf, (t0 + u) * KRPL + kr);
-        }
-      }
-    }
-    // First value tiles are in flight while the weights are computed.
-    u32x4 vd[UV];
-#pragma unroll
-    for (int u = 0; u < UV; ++u) vd[u] = load16(vblk + voff(min(u, nv - 1)));
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- chunk max (raw scores of valid rows, from LDS), running max, rescale
-    float mloc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) mloc[g] = -INFINITY;
-    for (int r = lane; r < nrows; r += 64) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) mloc[g] = fmaxf(mloc[g], sc[r * G + g]);
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m_chunk = wave_max(mloc[g]);  // finite: the chunk has >= 1 row
-      const float m_new = fmaxf(m_run[g], capped_log2(m_chunk, capped, cap_c, cap_inv));
-      const float alpha = (m_run[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
-      l_run[g] *= alpha;
-#pragma unroll
-      for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
-      psum[g] *= alpha;
-      m_run[g] = m_new;
-    }
-
-    // ---- weights p = 2^(s - m) for every row the value tiles cover (0 past
-    // the end); vq8 folds the token's scale into p ---------------------------
-#pragma unroll
-    for (int i = 0; i < kRowsPerChunk / 64; ++i) {
-      const int r = lane + 64 * i;
-      if (64 * i >= nv * VRPL) break;  // wave-uniform
-      if (r < nv * VRPL) {
-        const bool ok = r < nrows;
-        const float vs = (VT == kI8) ? sreg[VT == kI8 ? i : 0] : 1.0f;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float p =
-              ok ? __builtin_amdgcn_exp2f(capped_log2(sc[r * G + g], capped, cap_c, cap_inv) - m_run[g]) : 0.0f;
-          l_run[g] += p;
-          sc[r * G + g] = p * vs;
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- pass 2: weighted sum of values (rolling prefetch of UV tiles) ------
-    auto v_accum = [&](const float (&vf)[VE], int r) {
-      float p[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) p[g] = sc[r * G + g];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(p[g], vf[e], acc[g][e]);
-        if constexpr (VT == kI8) psum[g] += p[g];
-      }
-    };
-    t0 = 0;
-    for (; t0 + 2 * UV <= nv; t0 += UV) {
-#pragma unroll
-      for (int u = 0; u < UV; ++u) {
-        float vf[VE];
-        widen<VT, VE>(vd[u], vf);
-        vd[u] = load16(vblk + voff(t0 + UV + u));
-        v_accum(vf, (t0 + u) * VRPL + vr);
-      }
-    }
-    for (; t0 < nv; t0 += UV) {
-#pragma unroll
-      for (int u = 0; u < UV; ++u) {
-        if (t0 + u < nv) {
-          float vf[VE];
-          widen<VT, VE>(vd[u], vf);
-          if (t0 + UV + u < nv) vd[u] = load16(vblk + voff(t0 + UV + u));
-          v_accum(vf, (t0 + u) * VRPL + vr);
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-
-  // ---- merge the wave's row groups and write the split's partial ----------
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    l_run[g] = wave_sum(l_run[g]);
-    if constexpr (VT == kI8) {
-      // Each row's weight sits in every lane of the row; summing one lane
-      // per row group counts it once.
-#pragma unroll
-      for (int m = VLPR; m < 64; m <<= 1) psum[g] += __shfl_xor(psum[g], m);
-    }
-#pragma unroll
-    for (int e = 0; e < VE; ++e) {
-      float x = acc[g][e];
-#pragma unroll
-      for (int m = VLPR; m < 64; m <<= 1) x += __shfl_xor(x, m);
-      acc[g][e] = (VT == kI8) ? fmaf(-128.0f, psum[g], x) : x;
-    }
-  }
-  const int64_t row0 = (static_cast<int64_t>(b) * a.H + kvh * G) * a.max_splits + sigma;
-  if (vr == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float inv = 1.0f / l_run[g];
-      float* dst = a.part_o + (row0 + static_cast<int64_t>(g) * a.max_splits) * D + vc * VE;
-#pragma unroll
-      for (int e = 0; e < VE; e += 4)
-        *reinterpret_cast<float4*>(dst + e) =
-            make_float4(acc[g][e] * inv, acc[g][e + 1] * inv, acc[g][e + 2] * inv, acc[g][e + 3] * inv);
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      a.part_lse[row0 + static_cast<int64_t>(g) * a.max_splits] = (m_run[g] + log2f(l_run[g])) * kLn2;
-  }
-}
-
-template <int D, int G, int KT, int VT>
-hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
-  const int items = a.t.work_prefix[a.t.n_seq] * a.Hkv;
-  const dim3 grid((items + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL((decode_partial_kernel<D, G, KT, VT>), grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
-template <int D, int G>
-hipError_t by_dtype(int kt, int vt, const AttnArgs& a, hipStream_t s) {
-  if (kt == kF32 && vt == kF32) return launch_one<D, G, kF32, kF32>(a, s);
-  if (kt == kF32 && vt == kBF16) return launch_one<D, G, kF32, kBF16>(a, s);
-  if (kt == kF32 && vt == kI8) return launch_one<D, G, kF32, kI8>(a, s);
-  if (kt == kBF16 && vt == kF32) return launch_one<D, G, kBF16, kF32>(a, s);
-  if (kt == kBF16 && vt == kBF16) return launch_one<D, G, kBF16, kBF16>(a, s);
-  if (kt == kBF16 && vt == kI8) return launch_one<D, G, kBF16, kI8>(a, s);
-  return hipErrorInvalidValue;
-}
-
-template <int D>
-hipError_t by_group(int G, int kt, int vt, const AttnArgs& a, hipStream_t s) {
-  switch (G) {
-    case 1: return by_dtype<D, 1>(kt, vt, a, s);
-    case 2: return by_dtype<D, 2>(kt, vt, a, s);
-    case 4: return by_dtype<D, 4>(kt, vt, a, s);
-    case 8: return by_dtype<D, 8>(kt, vt, a, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-}  // namespace
 
 hipError_t launch_decode_partial(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a,
                                  hipStream_t stream) {
-  switch (D) {
-    case 64: return by_group<64>(G, k_dtype, v_dtype, a, stream);
-    case 128: return by_group<128>(G, k_dtype, v_dtype, a, stream);
-    case 256: return by_group<256>(G, k_dtype, v_dtype, a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return dispatch<false>(D, G, k_dtype, v_dtype, a, stream);
 }
 
 }  // namespace uaii

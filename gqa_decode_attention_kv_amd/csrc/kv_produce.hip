@@ -116,7 +116,19 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
   for (int e = 0; e < EPL; ++e) sx[lane + 64 * e] = xv[e];
   __syncthreads();
 
-  const int64_t slot = (is_q ? 0 : ((static_cast<int64_t>(b) * a.Hkv + u) * a.cap + pos)) * D;
+  // Element offset of the new token's row: contiguous [B][Hkv][cap][D], or
+  // paged [num_blocks][Hkv][bs][D] through the block table (ids outside the
+  // pool are clamped, so a bad table cannot write outside it).
+  int64_t slot = 0;
+  if (!is_q) {
+    if (a.block_table != nullptr) {
+      int pid = a.block_table[static_cast<int64_t>(b) * a.max_blocks + pos / a.block_size];
+      pid = min(max(pid, 0), a.num_blocks - 1);
+      slot = ((static_cast<int64_t>(pid) * a.Hkv + u) * a.block_size + pos % a.block_size) * D;
+    } else {
+      slot = ((static_cast<int64_t>(b) * a.Hkv + u) * a.cap + pos) * D;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const int i = lane + 64 * j;

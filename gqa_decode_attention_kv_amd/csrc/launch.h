@@ -42,6 +42,10 @@ struct ProduceArgs {
   void* v;
   float* v_scale;
   float* q_out;
+  // Paged cache (block_table != nullptr): slot p of (b, u) is row p % bs of
+  // physical block block_table[b][p / bs], pools [num_blocks][Hkv][bs][D].
+  const int32_t* block_table;
+  int32_t block_size, max_blocks, num_blocks;
   int32_t pos[kMaxBatch];
 };
 
@@ -55,6 +59,9 @@ struct AttnArgs {
   float* part_lse;
   float q_mul;    // multiplies q on load: scale*log2(e), or scale with a softcap
   float softcap;  // c > 0, or 0 for none
+  // Paged cache only (see ProduceArgs); log2_bs = log2(block_size).
+  const int32_t* block_table;
+  int32_t block_size, log2_bs, max_blocks, num_blocks;
   SeqTable t;
 };
 
@@ -70,6 +77,8 @@ hipError_t launch_kv_produce(const ProduceArgs& a, hipStream_t stream);
 // One wave per (work item, kv head): t.work_prefix[t.n_seq] * Hkv waves.
 hipError_t launch_decode_partial(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a,
                                  hipStream_t stream);
+hipError_t launch_decode_partial_paged(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a,
+                                       hipStream_t stream);
 hipError_t launch_decode_combine(int D, int B, const CombineArgs& a, hipStream_t stream);
 
 }  // namespace uaii

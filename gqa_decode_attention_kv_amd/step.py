@@ -11,7 +11,7 @@ import numpy as np
 import torch
 
 from . import binding as B
-from .workloads import BF16, F32, I8, Inputs, Workload
+from .workloads import BF16, F32, I8, Inputs, PagedInputs, Workload
 
 _TORCH = {F32: torch.float32, BF16: torch.int16, I8: torch.int8}
 
@@ -25,7 +25,8 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 class DeviceStep:
     """Device buffers of one layer's decode step and the calls that run it."""
 
-    def __init__(self, inputs: Inputs, device: str = "cuda", split_size: int | None = None):
+    def __init__(self, inputs: Inputs, device: str = "cuda", split_size: int | None = None,
+                 paged: PagedInputs | None = None):
         if not torch.cuda.is_available():
             raise RuntimeError("DeviceStep needs a GPU (torch.cuda.is_available() is False)")
         w: Workload = inputs.workload
@@ -40,9 +41,14 @@ class DeviceStep:
         self.q_in = _dev(inputs.q_in, device)
         self.k_in = _dev(inputs.k_in, device)
         self.v_in = _dev(inputs.v_in, device)
-        self.cache_k = _dev(inputs.cache_k, device)
-        self.cache_v = _dev(inputs.cache_v, device)
-        self.v_scale = _dev(inputs.v_scale, device) if inputs.v_scale is not None else None
+        self.paged = paged
+        src_k = paged.pool_k if paged else inputs.cache_k
+        src_v = paged.pool_v if paged else inputs.cache_v
+        src_s = paged.pool_scale if paged else inputs.v_scale
+        self.cache_k = _dev(src_k, device)
+        self.cache_v = _dev(src_v, device)
+        self.v_scale = _dev(src_s, device) if src_s is not None else None
+        self.block_table = _dev(paged.block_table, device) if paged else None
         self.w_q = _dev(inputs.w_q, device) if inputs.w_q is not None else None
         self.w_k = _dev(inputs.w_k, device) if inputs.w_k is not None else None
         self.q_out = torch.empty((Bn, H, d), dtype=torch.float32, device=device)
@@ -56,9 +62,14 @@ class DeviceStep:
         n = w.qk_norm
         self.qk_norm = (B.QKNorm(1, n.eps, n.offset, self.w_q.data_ptr(), self.w_k.data_ptr())
                         if n.enabled else None)
-        self.cache = B.KVCache(w.k_dtype, w.v_dtype, w.capacity, self.cache_k.data_ptr(),
-                               self.cache_v.data_ptr(),
-                               self.v_scale.data_ptr() if self.v_scale is not None else None)
+        vs_ptr = self.v_scale.data_ptr() if self.v_scale is not None else None
+        if paged:
+            self.cache = B.KVCache(w.k_dtype, w.v_dtype, paged.capacity, self.cache_k.data_ptr(),
+                                   self.cache_v.data_ptr(), vs_ptr, self.block_table.data_ptr(),
+                                   paged.block_size, paged.max_blocks, paged.num_blocks)
+        else:
+            self.cache = B.KVCache(w.k_dtype, w.v_dtype, w.capacity, self.cache_k.data_ptr(),
+                                   self.cache_v.data_ptr(), vs_ptr, None, 0, 0, 0)
         self.scale = 1.0 / math.sqrt(d)
 
     @staticmethod
@@ -92,11 +103,21 @@ class DeviceStep:
             a = a.view(dtype)
         return a
 
+    def slot_index(self):
+        """(first index, row index) of each sequence's new-token slot: (b, p)
+        for a contiguous cache, (physical block, p % block_size) for a paged one."""
+        p = self.positions.astype(np.int64)
+        if self.paged:
+            bs = self.paged.block_size
+            blk = self.paged.block_table[np.arange(self.w.batch), p // bs].astype(np.int64)
+            return blk, p % bs
+        return np.arange(self.w.batch), p
+
     def cache_rows(self) -> dict:
         """The produced slot of every (b, kv head): K, V and (vq8) scale rows."""
-        Bn = self.w.batch
-        idx = torch.as_tensor(self.positions.astype(np.int64), device=self.device)
-        bi = torch.arange(Bn, device=self.device)
+        first, row = self.slot_index()
+        bi = torch.as_tensor(first, device=self.device)
+        idx = torch.as_tensor(row, device=self.device)
         k = self.cache_k[bi, :, idx].cpu().numpy()
         v = self.cache_v[bi, :, idx].cpu().numpy()
         if self.w.k_dtype == BF16:

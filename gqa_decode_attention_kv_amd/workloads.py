@@ -22,6 +22,12 @@ standard normal float32 unless stated):
 
 Blocks are filled from a thread pool; each block has its own seed, so the
 result does not depend on the number of threads.
+
+Paged caches (``make_paged``) hold the same logical rows: logical block j of
+sequence b is copied to physical block table[b][j] of a pool
+[num_blocks][Hkv][block_size][d], where the table is a seeded random
+permutation of the pool (stream 8) and a few blocks stay unused.  Every pool
+row that no logical row maps to is NaN-poisoned, like the invisible rows.
 """
 from __future__ import annotations
 
@@ -245,3 +251,59 @@ def make_inputs(w: Workload, seq_lens=None) -> Inputs:
         list(ex.map(fill, jobs))
     return Inputs(w, lens, (lens - 1).astype(np.int32), q_in, k_in, v_in, w_q, w_k,
                   cache_k, cache_v, v_scale)
+
+
+@dataclass
+class PagedInputs:
+    block_size: int
+    max_blocks: int
+    num_blocks: int
+    block_table: np.ndarray     # [B][max_blocks] int32
+    pool_k: np.ndarray          # [num_blocks][Hkv][block_size][d]
+    pool_v: np.ndarray
+    pool_scale: np.ndarray | None  # [num_blocks][Hkv][block_size] (vq8)
+
+    @property
+    def capacity(self) -> int:
+        return self.max_blocks * self.block_size
+
+
+def _poison_like(dtype) -> object:
+    return {np.dtype(np.float32): np.float32(np.nan), np.dtype(np.uint16): BF16_NAN,
+            np.dtype(np.int8): np.int8(0)}[np.dtype(dtype)]
+
+
+def make_paged(inputs: Inputs, block_size: int, spare_blocks: int = 3) -> PagedInputs:
+    """Scatter the contiguous caches of ``inputs`` into block pools."""
+    w = inputs.workload
+    B, Hkv, d, cap = w.batch, w.n_kv_heads, w.head_dim, w.capacity
+    bs = int(block_size)
+    mb = -(-cap // bs)
+    nblk = B * mb + spare_blocks
+    rng = np.random.default_rng([*w.seed, 8])
+    table = rng.permutation(nblk)[: B * mb].astype(np.int32).reshape(B, mb)
+
+    def scatter(cache, trailing):
+        # cache [B][Hkv][cap]+trailing -> pool [nblk][Hkv][bs]+trailing
+        pad = mb * bs - cap
+        if pad:
+            fill = np.full((B, Hkv, pad) + trailing, _poison_like(cache.dtype), dtype=cache.dtype)
+            cache = np.concatenate([cache, fill], axis=2)
+        blocks = cache.reshape((B, Hkv, mb, bs) + trailing)
+        blocks = np.moveaxis(blocks, 2, 1).reshape((B * mb, Hkv, bs) + trailing)
+        pool = np.full((nblk, Hkv, bs) + trailing, _poison_like(cache.dtype), dtype=cache.dtype)
+        pool[table.reshape(-1)] = blocks
+        return pool
+
+    pk = scatter(inputs.cache_k, (d,))
+    pv = scatter(inputs.cache_v, (d,))
+    ps = None
+    if inputs.v_scale is not None:
+        vs = inputs.v_scale
+        pad = mb * bs - cap
+        if pad:
+            vs = np.concatenate([vs, np.full((B, Hkv, pad), np.nan, np.float32)], axis=2)
+        blocks = np.moveaxis(vs.reshape(B, Hkv, mb, bs), 2, 1).reshape(B * mb, Hkv, bs)
+        ps = np.full((nblk, Hkv, bs), np.nan, np.float32)
+        ps[table.reshape(-1)] = blocks
+    return PagedInputs(bs, mb, nblk, table, pk, pv, ps)

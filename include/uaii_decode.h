@@ -27,7 +27,8 @@
  * Layouts (row-major, innermost last):
  *   q_in, q_out, q           [batch][n_heads][head_dim]            f32
  *   k_in, v_in               [batch][n_kv_heads][head_dim]         f32
- *   cache K, V               [batch][n_kv_heads][capacity][head_dim]
+ *   cache K, V               [batch][n_kv_heads][capacity][head_dim] (contiguous;
+ *                            the paged layout is described at uaii_kv_cache)
  *                            K: f32 or bf16; V: f32, bf16 or int8 (vq8)
  *   v_scale (vq8 only)       [batch][n_kv_heads][capacity]         f32
  *   part_o                   [batch][n_heads][max_splits][head_dim] f32
@@ -129,14 +130,40 @@ typedef struct uaii_qk_norm {
     const float *k_weight;   /* device [head_dim] */
 } uaii_qk_norm;
 
-/* Contiguous per-sequence KV cache of one layer. */
+/* KV cache of one layer, in one of two layouts.
+ *
+ * Contiguous (block_table == NULL): one slab per (sequence, kv head),
+ *   k, v     device [B][Hkv][capacity][d]
+ *   v_scale  device [B][Hkv][capacity]          (vq8 only)
+ *
+ * Paged (block_table != NULL): pools of fixed-size blocks shared by all
+ * sequences, and a table that maps each sequence's logical blocks to
+ * physical ones.  Slot p of (sequence b, kv head u) is row p % block_size of
+ * physical block block_table[b][p / block_size]:
+ *   k, v         device [num_blocks][Hkv][block_size][d]
+ *   v_scale      device [num_blocks][Hkv][block_size]   (vq8 only)
+ *   block_table  device [B][max_blocks] int32
+ *   capacity     must equal max_blocks * block_size (logical slots per
+ *                sequence)
+ * The table must hold an id in [0, num_blocks) for every logical block that
+ * covers a visible key or the new token's slot; the kernels clamp ids
+ * outside the pool (so a bad table cannot reach memory outside it) but the
+ * result is then undefined.  Blocks may be shared between sequences for
+ * reading; the producer writes only the new token's slot, so two sequences
+ * must not share the block that receives it.
+ * (Paged KV pages: "llamay - Models and formats", What is refused: a KV
+ * page, the paged allocator, copy-on-write fork.) */
 typedef struct uaii_kv_cache {
     int32_t k_dtype;   /* UAII_F32 | UAII_BF16 */
     int32_t v_dtype;   /* UAII_F32 | UAII_BF16 | UAII_I8 (vq8) */
     int32_t capacity;  /* slots per (sequence, kv head), >= 1 */
-    void *k;           /* device [B][Hkv][capacity][d] */
-    void *v;           /* device [B][Hkv][capacity][d] */
-    float *v_scale;    /* device [B][Hkv][capacity], vq8 only (else ignored) */
+    void *k;           /* device, see the layouts above */
+    void *v;           /* device */
+    float *v_scale;    /* device, vq8 only (else ignored) */
+    const int32_t *block_table; /* device [B][max_blocks], or NULL (contiguous) */
+    int32_t block_size; /* paged: rows per block, a power of two in [16, 1024] */
+    int32_t max_blocks; /* paged: table entries per sequence, >= 1 */
+    int32_t num_blocks; /* paged: blocks in each pool, >= 1 */
 } uaii_kv_cache;
 
 /* Text of the last error on the calling thread ("" if none); valid until the

@@ -126,12 +126,12 @@ def check_slot(w: W.Workload, gpu: dict, ref: dict, q_gpu: np.ndarray, q_ref: np
     return res
 
 
-def run_gpu(inputs, split_size=None):
+def run_gpu(inputs, split_size=None, paged=None):
     """One step on the GPU with NaN-filled partial buffers (so unwritten
     entries stay detectable)."""
     import torch
     from gqa_decode_attention_kv_amd.step import DeviceStep
-    st = DeviceStep(inputs, split_size=split_size)
+    st = DeviceStep(inputs, split_size=split_size, paged=paged)
     st.part_o.fill_(float("nan"))
     st.part_lse.fill_(float("nan"))
     st.step()
@@ -170,7 +170,7 @@ def compare_partials(st, ref, w, lens, pick=None, max_per_seq=None, rng=None):
     return worst
 
 
-def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0):
+def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0, block_size=None):
     """Run one step on the GPU and in the oracle; compare every output element,
     the produced cache rows (and that nothing else in the caches changed) and
     the split partials.  Returns (max abs error, tolerance, class)."""
@@ -179,8 +179,14 @@ def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0):
         f"K/V={w.k_dtype}/{w.v_dtype} lens={lens.tolist()[:8]} S={w.split_size} W={w.window} "
         f"cap={w.softcap} rope={w.rope.pairing}/{w.rope.scaling} norm={w.qk_norm.enabled}")
     inputs = W.make_inputs(w, seq_lens=lens)
-    ck0, cv0 = inputs.cache_k.copy(), inputs.cache_v.copy()
-    st = run_gpu(inputs)
+    paged = W.make_paged(inputs, block_size) if block_size else None
+    if paged:
+        say(f"  paged: block_size={paged.block_size} max_blocks={paged.max_blocks} "
+            f"num_blocks={paged.num_blocks}")
+        ck0, cv0 = paged.pool_k.copy(), paged.pool_v.copy()
+    else:
+        ck0, cv0 = inputs.cache_k.copy(), inputs.cache_v.copy()
+    st = run_gpu(inputs, paged=paged)
     ref = OracleStep(inputs)
     out = st.out.cpu().numpy()
     want = ref.decode().reshape(out.shape)
@@ -190,7 +196,8 @@ def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0):
     compare_partials(st, ref, w, lens, max_per_seq=max_partials_per_seq,
                      rng=np.random.default_rng(seed))
     mask = np.ones(ck0.shape[:3], bool)
-    mask[np.arange(w.batch), :, inputs.positions] = False
+    first, row = st.slot_index()
+    mask[first, :, row] = False
     for dev, host in ((st.cache_k, ck0), (st.cache_v, cv0)):
         g = dev.cpu().numpy().view(host.dtype)
         assert np.array_equal(g[mask].view(np.uint8), host[mask].view(np.uint8)), \

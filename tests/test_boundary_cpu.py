@@ -50,7 +50,8 @@ def test_struct_layouts_match_header():
     assert C.sizeof(B.Shape) == 16
     assert C.sizeof(B.Rope) == 48 and B.Rope.theta.offset == 8
     assert C.sizeof(B.QKNorm) == 32 and B.QKNorm.q_weight.offset == 16
-    assert C.sizeof(B.KVCache) == 40 and B.KVCache.k.offset == 16
+    assert C.sizeof(B.KVCache) == 64 and B.KVCache.k.offset == 16
+    assert B.KVCache.block_table.offset == 40 and B.KVCache.num_blocks.offset == 56
 
 
 def shape(b=2, h=8, hkv=2, d=128):
@@ -192,3 +193,22 @@ def test_error_text_is_per_call():
     assert B.load().uaii_decode_attn(None, None, None, None, 0.0, 0, 0.0, 1, 1, None, None,
                                      None) == INV
     assert "shape is NULL" in B.last_error()
+
+
+@host_only
+@pytest.mark.parametrize("case", [
+    ("block size 8", dict(block_size=8), NI, ["block_size=8 is not supported"]),
+    ("block size 48", dict(block_size=48), NI, ["block_size=48"]),
+    ("block size 2048", dict(block_size=2048), NI, ["block_size=2048"]),
+    ("max_blocks 0", dict(max_blocks=0), INV, ["max_blocks=0"]),
+    ("num_blocks 0", dict(num_blocks=0), INV, ["num_blocks=0"]),
+    ("capacity mismatch", dict(capacity=100), INV, ["capacity=100 must equal max_blocks*block_size=64"]),
+    ("table misaligned", dict(table=FAKE + 2), INV, ["cache.block_table", "4-byte aligned"]),
+], ids=lambda c: c[0])
+def test_paged_cache_refusals(case):
+    _, kw, status, needles = case
+    c = B.KVCache(B.BF16, B.BF16, kw.get("capacity", 64), FAKE, FAKE, None,
+                  kw.get("table", FAKE), kw.get("block_size", 16), kw.get("max_blocks", 4),
+                  kw.get("num_blocks", 10))
+    refused(lambda: attn(ca=c), status, *needles)
+    refused(lambda: produce(ca=c, pos=(3, 4)), status, *needles)
