@@ -18,7 +18,7 @@ from . import build as _build
 
 F32, BF16, I8 = 0, 1, 2
 NEOX, INTERLEAVED = 0, 1
-PLAIN, LLAMA3 = 0, 1
+PLAIN, LLAMA3, LINEAR = 0, 1, 2
 
 _dp = C.POINTER(C.c_double)
 _fp = C.POINTER(C.c_float)
@@ -70,19 +70,20 @@ class Oracle:
         lib.oracle_kv_produce.argtypes = (
             [C.c_int] * 4 + [C.c_int, C.c_int] + [C.c_double] * 5
             + [C.c_int, C.c_double, C.c_int, _fp, _fp, _fp, _fp, _fp, _ip,
-               C.c_int, C.c_int, C.c_int, _vp, _vp, _fp, _dp])
+               C.c_int, C.c_int, C.c_int, _vp, _vp, _fp, _fp, _dp])
         lib.oracle_scores.restype = None
-        lib.oracle_scores.argtypes = ([C.c_int] * 5 + [_vp, _dp, C.c_int, C.c_int, C.c_int64,
+        lib.oracle_scores.argtypes = ([C.c_int] * 5 + [_vp, _fp, _dp, C.c_int, C.c_int, C.c_int64,
                                                        C.c_int64, C.c_double, _dp])
         lib.oracle_decode_pairs.restype = C.c_int
-        lib.oracle_decode_pairs.argtypes = ([C.c_int] * 7 + [_vp, _vp, _fp, _dp, _ip, C.c_int32,
-                                                            C.c_double, _ip, C.c_int, _dp])
+        lib.oracle_decode_pairs.argtypes = ([C.c_int] * 7 + [_vp, _vp, _fp, _fp, _dp, _ip, C.c_int32,
+                                                            C.c_double, _dp, _ip, C.c_int, _dp])
         lib.oracle_split_partial.restype = C.c_int64
-        lib.oracle_split_partial.argtypes = ([C.c_int] * 6 + [_vp, _vp, _fp, _dp, C.c_int, C.c_int]
+        lib.oracle_split_partial.argtypes = ([C.c_int] * 6 + [_vp, _vp, _fp, _fp, _dp, C.c_int,
+                                                              C.c_int]
                                              + [C.c_int64, C.c_int64, C.c_double, C.c_int64,
                                                 C.c_int64, _dp, _dp])
         lib.oracle_combine.restype = C.c_int
-        lib.oracle_combine.argtypes = [C.c_int, C.c_int, _dp, _dp, _dp]
+        lib.oracle_combine.argtypes = [C.c_int, C.c_int, _dp, _dp, C.c_int, C.c_double, _dp]
         self.lib = lib
 
     # -- codecs -----------------------------------------------------------
@@ -135,7 +136,7 @@ class Oracle:
         return y
 
     def kv_produce(self, *, rope: dict, norm: dict | None, q_in, k_in, v_in, positions,
-                   k_dtype: int, v_dtype: int, cache_k, cache_v, v_scale=None):
+                   k_dtype: int, v_dtype: int, cache_k, cache_v, v_scale=None, k_scale=None):
         """Run the producer; writes slot positions[b] of the caches in place and
         returns q' as double [B][H][d]."""
         B, H, d = q_in.shape
@@ -161,37 +162,44 @@ class Oracle:
             ne, eps, off, _ptr(w_q, C.c_float), _ptr(w_k, C.c_float),
             _ptr(q_in, C.c_float), _ptr(k_in, C.c_float), _ptr(v_in, C.c_float),
             _ptr(positions, C.c_int32), k_dtype, v_dtype, cap, _ptr(cache_k), _ptr(cache_v),
-            _ptr(v_scale, C.c_float), _ptr(q_out, C.c_double))
+            _ptr(k_scale, C.c_float), _ptr(v_scale, C.c_float), _ptr(q_out, C.c_double))
         if rc != 0:
             raise ValueError("oracle_kv_produce rejected its arguments")
         return q_out
 
     # -- attention -----------------------------------------------------------
-    def _cache_args(self, cache_k, cache_v, v_scale, k_dtype, v_dtype):
+    def _cache_args(self, cache_k, cache_v, v_scale, k_dtype, v_dtype, k_scale=None):
         _need(cache_k, _STORAGE[k_dtype], "cache_k")
         _need(cache_v, _STORAGE[v_dtype], "cache_v")
         if v_dtype == I8:
             _need(v_scale, np.float32, "v_scale")
+        if k_dtype == I8:
+            _need(k_scale, np.float32, "k_scale")
         return cache_k.shape[2]
 
-    def scores(self, *, q, cache_k, k_dtype, n_heads, b, h, L, window=0, softcap=0.0):
+    def scores(self, *, q, cache_k, k_dtype, n_heads, b, h, L, window=0, softcap=0.0,
+               k_scale=None):
         Hkv, cap, d = cache_k.shape[1], cache_k.shape[2], cache_k.shape[3]
         _need(cache_k, _STORAGE[k_dtype], "cache_k")
+        if k_dtype == I8:
+            _need(k_scale, np.float32, "k_scale")
         qv = np.ascontiguousarray(q, dtype=np.float64)
         s = np.zeros(int(L), dtype=np.float64)
-        self.lib.oracle_scores(n_heads, Hkv, d, k_dtype, cap, _ptr(cache_k), _ptr(qv, C.c_double),
+        self.lib.oracle_scores(n_heads, Hkv, d, k_dtype, cap, _ptr(cache_k),
+                               _ptr(k_scale, C.c_float), _ptr(qv, C.c_double),
                                int(b), int(h), int(L), int(window), float(softcap),
                                _ptr(s, C.c_double))
         return s
 
     def decode(self, *, q, cache_k, cache_v, v_scale=None, k_dtype, v_dtype, seq_lens,
-               window=0, softcap=0.0, pairs=None):
+               window=0, softcap=0.0, pairs=None, sinks=None, k_scale=None):
         """Single-pass attention; q is [B][H][d] (any float dtype, widened to
-        double).  Returns [B][H][d] double, or [len(pairs)][d] for a list of
-        (b, h) pairs."""
+        double); sinks is an optional per-head attention-sink logit [H].
+        Returns [B][H][d] double, or [len(pairs)][d] for a list of (b, h)
+        pairs."""
         B, H, d = q.shape
         Hkv = cache_k.shape[1]
-        cap = self._cache_args(cache_k, cache_v, v_scale, k_dtype, v_dtype)
+        cap = self._cache_args(cache_k, cache_v, v_scale, k_dtype, v_dtype, k_scale)
         qd = np.ascontiguousarray(q, dtype=np.float64)
         lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
         if pairs is None:
@@ -199,37 +207,44 @@ class Oracle:
         else:
             pr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
         out = np.zeros((len(pr), d), dtype=np.float64)
+        sk = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float64)
+        if sk is not None and sk.shape != (H,):
+            raise ValueError(f"sinks must have shape ({H},)")
         rc = self.lib.oracle_decode_pairs(B, H, Hkv, d, k_dtype, v_dtype, cap, _ptr(cache_k),
-                                          _ptr(cache_v), _ptr(v_scale, C.c_float),
+                                          _ptr(cache_v), _ptr(k_scale, C.c_float),
+                                          _ptr(v_scale, C.c_float),
                                           _ptr(qd, C.c_double), _ptr(lens, C.c_int32),
-                                          int(window), float(softcap), _ptr(pr, C.c_int32),
-                                          len(pr), _ptr(out, C.c_double))
+                                          int(window), float(softcap), _ptr(sk, C.c_double),
+                                          _ptr(pr, C.c_int32), len(pr), _ptr(out, C.c_double))
         if rc != 0:
             raise ValueError("oracle_decode_pairs rejected its arguments")
         return out.reshape(B, H, d) if pairs is None else out
 
     def split_partial(self, *, q_bh, cache_k, cache_v, v_scale=None, k_dtype, v_dtype,
-                      n_heads, b, h, L, window, softcap, split_size, sigma):
+                      n_heads, b, h, L, window, softcap, split_size, sigma, k_scale=None):
         """(o[d], lse, n_keys) of split sigma for one (b, h); q_bh is [d]."""
         Hkv, d = cache_k.shape[1], cache_k.shape[3]
-        cap = self._cache_args(cache_k, cache_v, v_scale, k_dtype, v_dtype)
+        cap = self._cache_args(cache_k, cache_v, v_scale, k_dtype, v_dtype, k_scale)
         qv = np.ascontiguousarray(q_bh, dtype=np.float64)
         o = np.zeros(d, dtype=np.float64)
         lse = np.zeros(1, dtype=np.float64)
         n = self.lib.oracle_split_partial(n_heads, Hkv, d, k_dtype, v_dtype, cap, _ptr(cache_k),
-                                          _ptr(cache_v), _ptr(v_scale, C.c_float),
+                                          _ptr(cache_v), _ptr(k_scale, C.c_float),
+                                          _ptr(v_scale, C.c_float),
                                           _ptr(qv, C.c_double), int(b), int(h), int(L),
                                           int(window), float(softcap), int(split_size),
                                           int(sigma), _ptr(o, C.c_double),
                                           _ptr(lse, C.c_double))
         return o, float(lse[0]), int(n)
 
-    def combine(self, o, lse):
+    def combine(self, o, lse, sink=None):
         o = np.ascontiguousarray(o, dtype=np.float64)
         lse = np.ascontiguousarray(lse, dtype=np.float64)
         out = np.zeros(o.shape[1], dtype=np.float64)
         used = self.lib.oracle_combine(o.shape[0], o.shape[1], _ptr(o, C.c_double),
-                                       _ptr(lse, C.c_double), _ptr(out, C.c_double))
+                                       _ptr(lse, C.c_double), 0 if sink is None else 1,
+                                       0.0 if sink is None else float(sink),
+                                       _ptr(out, C.c_double))
         return out, int(used)
 
 

@@ -39,6 +39,7 @@
 
 #define OR_PLAIN 0
 #define OR_LLAMA3 1
+#define OR_LINEAR 2
 
 static const double OR_PI = 3.14159265358979323846264338327950288;
 
@@ -131,7 +132,8 @@ static double load_elem(int dtype, const void *base, int64_t row, int d, int i,
         return (double)((const float *)base)[idx];
     case OR_BF16:
         return oracle_bf16_to_double(((const uint16_t *)base)[idx]);
-    default: /* OR_I8: code * scale, the double product of the stored values */
+    default: /* OR_I8 (vq8 values, q8 keys and values): code * scale, the
+              * double product of the stored values */
         return (double)((const int8_t *)base)[idx] * (double)scale[row];
     }
 }
@@ -156,7 +158,9 @@ void oracle_rms_norm(const double *x, int d, const float *w, int offset,
 
 /* Rotary frequencies g_i, i in [0, d/2), over the full head
  * ([ALGENTA] Structural fact requirements: rotary coverage is the full head).
- * Plain: g_i = theta^(-2i/d).  Llama-3 scaling ([UAII] P0.2 RoPE scaling,
+ * Plain: g_i = theta^(-2i/d).  Linear scaling divides every frequency by
+ * factor, i.e. positions are divided by factor ([ALGENTA] Decoder families:
+ * linear global scaling; [UAII] P0.2).  Llama-3 scaling ([UAII] P0.2 RoPE scaling,
  * matching Hugging Face's Llama-3 rotary embedding; [FREETOKEN] Changes:
  * factor, low 1, high 4, original 8192): with wavelength lambda = 2*pi/f,
  *   lambda < orig/high           -> keep f
@@ -178,6 +182,8 @@ void oracle_rope_freqs(int d, int scaling, double theta, double factor,
                 double mu = (orig / lambda - low) / (high - low);
                 g[i] = (1.0 - mu) * f / factor + mu * f;
             }
+        } else if (scaling == OR_LINEAR) {
+            g[i] = f / factor;
         } else {
             g[i] = f;
         }
@@ -233,7 +239,8 @@ static void store_row_double(int dtype, void *base, int64_t row, int d,
 /* The producer for a batch.  Position of sequence b is positions[b]; the
  * same absolute position rotates q and k ([UAII] P1.3: positions follow the
  * absolute KV index, same as RoPE).  Writes q_out (double, [B][H][d]) and
- * slot positions[b] of the caches ([B][Hkv][cap][d]; v_scale [B][Hkv][cap]).
+ * slot positions[b] of the caches ([B][Hkv][cap][d]; k_scale and v_scale
+ * [B][Hkv][cap] for int8 keys and values).
  * Returns 0, or -1 for an argument outside what the oracle handles. */
 int oracle_kv_produce(int B, int H, int Hkv, int d,
                       int pairing, int scaling, double theta, double factor,
@@ -243,8 +250,8 @@ int oracle_kv_produce(int B, int H, int Hkv, int d,
                       const float *q_in, const float *k_in, const float *v_in,
                       const int32_t *positions,
                       int k_dtype, int v_dtype, int cap,
-                      void *cache_k, void *cache_v, float *v_scale,
-                      double *q_out)
+                      void *cache_k, void *cache_v, float *k_scale,
+                      float *v_scale, double *q_out)
 {
     if (d > 256 || d < 2 || (d & 1) || H % Hkv != 0)
         return -1;
@@ -265,7 +272,17 @@ int oracle_kv_produce(int B, int H, int Hkv, int d,
             int64_t row = slab * cap + pos;
             norm_rope(k_in + slab * d, d, norm_enabled, w_k, offset, eps, pairing,
                       g, pos, tmp);
-            store_row_double(k_dtype, cache_k, row, d, tmp);
+            if (k_dtype == OR_I8) {
+                /* q8 keys: the rotated key rounded to f32, then the same
+                 * quantiser as the values ([LLAMAY] The KV cache, in three
+                 * precisions: q8 quantises both keys and values). */
+                float kf[256];
+                for (int i = 0; i < d; ++i)
+                    kf[i] = (float)tmp[i];
+                oracle_quantize_v(kf, d, (int8_t *)cache_k + row * d, &k_scale[row]);
+            } else {
+                store_row_double(k_dtype, cache_k, row, d, tmp);
+            }
             const float *v = v_in + slab * d;
             if (v_dtype == OR_I8) {
                 oracle_quantize_v(v, d, (int8_t *)cache_v + row * d, &v_scale[row]);
@@ -296,12 +313,12 @@ static int64_t visible_lo(int64_t L, int64_t W)
  * fact requirements: n_heads is an exact multiple of n_kv_heads; attention
  * scale is 1/sqrt(head_dim)), then the logit softcap c * tanh(s / c) when
  * c > 0 ([UAII] P1.4: logit softcapping as a tanh clip). */
-static double score(int d, int k_dtype, const void *cache_k, int64_t krow,
-                    const double *q, double scale, double softcap)
+static double score(int d, int k_dtype, const void *cache_k, const float *k_scale,
+                    int64_t krow, const double *q, double scale, double softcap)
 {
     double acc = 0.0;
     for (int i = 0; i < d; ++i)
-        acc += q[i] * load_elem(k_dtype, cache_k, krow, d, i, NULL);
+        acc += q[i] * load_elem(k_dtype, cache_k, krow, d, i, k_scale);
     double s = scale * acc;
     if (softcap > 0.0)
         s = softcap * tanh(s / softcap);
@@ -311,7 +328,7 @@ static double score(int d, int k_dtype, const void *cache_k, int64_t krow,
 /* Scores of one (b, h) over all L keys: visible keys get their (capped)
  * score, the rest -inf.  s_out has L entries. */
 void oracle_scores(int H, int Hkv, int d, int k_dtype, int cap,
-                   const void *cache_k, const double *q /* [d] */,
+                   const void *cache_k, const float *k_scale, const double *q /* [d] */,
                    int b, int h, int64_t L, int64_t W, double softcap,
                    double *s_out)
 {
@@ -322,19 +339,24 @@ void oracle_scores(int H, int Hkv, int d, int k_dtype, int cap,
     double scale = 1.0 / sqrt((double)d);
     for (int64_t j = 0; j < L; ++j)
         s_out[j] = (j >= lo)
-                       ? score(d, k_dtype, cache_k, slab * cap + j, q, scale, softcap)
+                       ? score(d, k_dtype, cache_k, k_scale, slab * cap + j, q, scale, softcap)
                        : -INFINITY;
 }
 
 /* Softmax attention of one (b, h) over the keys [j0, j1) intersected with
  * the visible range.  out = sum_j e^(s_j - m) v_j / sum_j e^(s_j - m),
- * m = max s_j.  Returns the number of keys used; when it is > 0 and lse is
- * not NULL, *lse = m + ln(sum_j e^(s_j - m)). */
+ * m = max s_j.  With an attention sink (a per-head logit sink that enters
+ * the softmax denominator only; [LLAMAY] Architectures: gpt-oss) the
+ * denominator gains e^(sink - m); has_sink = 0 means no sink.  Returns the
+ * number of keys used; when it is > 0 and lse is not NULL,
+ * *lse = m + ln(sum_j e^(s_j - m)) (over the keys only). */
 static int64_t attend_range(int H, int Hkv, int d, int k_dtype, int v_dtype,
                             int cap, const void *cache_k, const void *cache_v,
-                            const float *v_scale, const double *q, int b, int h,
+                            const float *k_scale, const float *v_scale,
+                            const double *q, int b, int h,
                             int64_t L, int64_t W, double softcap, int64_t j0,
-                            int64_t j1, double *out, double *lse)
+                            int64_t j1, int has_sink, double sink, double *out,
+                            double *lse)
 {
     int G = H / Hkv;
     int u = h / G;
@@ -351,20 +373,21 @@ static int64_t attend_range(int H, int Hkv, int d, int k_dtype, int v_dtype,
     double scale = 1.0 / sqrt((double)d);
     double m = -INFINITY;
     for (int64_t j = j0; j < j1; ++j) {
-        double s = score(d, k_dtype, cache_k, slab * cap + j, q, scale, softcap);
+        double s = score(d, k_dtype, cache_k, k_scale, slab * cap + j, q, scale, softcap);
         if (s > m)
             m = s;
     }
     double l = 0.0;
     for (int64_t j = j0; j < j1; ++j) {
         int64_t row = slab * cap + j;
-        double w = exp(score(d, k_dtype, cache_k, row, q, scale, softcap) - m);
+        double w = exp(score(d, k_dtype, cache_k, k_scale, row, q, scale, softcap) - m);
         l += w;
         for (int i = 0; i < d; ++i)
             out[i] += w * load_elem(v_dtype, cache_v, row, d, i, v_scale);
     }
+    double z = l + (has_sink ? exp(sink - m) : 0.0);
     for (int i = 0; i < d; ++i)
-        out[i] /= l;
+        out[i] /= z;
     if (lse)
         *lse = m + log(l);
     return j1 - j0;
@@ -375,8 +398,9 @@ static int64_t attend_range(int H, int Hkv, int d, int k_dtype, int v_dtype,
  * [n_pairs][d] double.  pairs holds 2*n_pairs ints (b, h). */
 int oracle_decode_pairs(int B, int H, int Hkv, int d, int k_dtype, int v_dtype,
                         int cap, const void *cache_k, const void *cache_v,
-                        const float *v_scale, const double *q,
+                        const float *k_scale, const float *v_scale, const double *q,
                         const int32_t *seq_lens, int32_t window, double softcap,
+                        const double *sinks /* [H] or NULL */,
                         const int32_t *pairs, int n_pairs, double *out)
 {
     if (H % Hkv != 0 || d > 256)
@@ -388,9 +412,9 @@ int oracle_decode_pairs(int B, int H, int Hkv, int d, int k_dtype, int v_dtype,
         int64_t L = seq_lens[b];
         if (L < 1 || L > cap)
             return -1;
-        attend_range(H, Hkv, d, k_dtype, v_dtype, cap, cache_k, cache_v, v_scale,
-                     q + ((int64_t)b * H + h) * d, b, h, L, window, softcap, 0, L,
-                     out + (int64_t)n * d, NULL);
+        attend_range(H, Hkv, d, k_dtype, v_dtype, cap, cache_k, cache_v, k_scale,
+                     v_scale, q + ((int64_t)b * H + h) * d, b, h, L, window, softcap, 0, L,
+                     sinks != NULL, sinks ? sinks[h] : 0.0, out + (int64_t)n * d, NULL);
     }
     return 0;
 }
@@ -404,13 +428,14 @@ int oracle_decode_pairs(int B, int H, int Hkv, int d, int k_dtype, int v_dtype,
  * partials; Conformance CLI: decode_attn=splitk_flash_decoding). */
 int64_t oracle_split_partial(int H, int Hkv, int d, int k_dtype, int v_dtype,
                              int cap, const void *cache_k, const void *cache_v,
-                             const float *v_scale, const double *q /* [d] */,
+                             const float *k_scale, const float *v_scale,
+                             const double *q /* [d] */,
                              int b, int h, int64_t L, int64_t W, double softcap,
                              int64_t S, int64_t sigma, double *o, double *lse)
 {
     int64_t n = attend_range(H, Hkv, d, k_dtype, v_dtype, cap, cache_k, cache_v,
-                             v_scale, q, b, h, L, W, softcap, sigma * S,
-                             (sigma + 1) * S, o, lse);
+                             k_scale, v_scale, q, b, h, L, W, softcap, sigma * S,
+                             (sigma + 1) * S, 0, 0.0, o, lse);
     if (n == 0)
         *lse = -INFINITY;
     return n;
@@ -418,19 +443,23 @@ int64_t oracle_split_partial(int H, int Hkv, int d, int k_dtype, int v_dtype,
 
 /* Log-sum-exp combine of n partials: M = max lse_s over non-empty splits,
  * out = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M).  Splits whose lse is
- * -inf are skipped.  Returns the number of splits used. */
+ * -inf are skipped.  With an attention sink the denominator gains
+ * e^(sink - M) (the sink belongs to no split).
+ * Returns the number of splits used. */
 int oracle_combine(int n, int d, const double *o /* [n][d] */,
-                   const double *lse /* [n] */, double *out)
+                   const double *lse /* [n] */, int has_sink, double sink,
+                   double *out)
 {
     double M = -INFINITY;
     for (int s = 0; s < n; ++s)
         if (lse[s] > M)
             M = lse[s];
+
     for (int i = 0; i < d; ++i)
         out[i] = 0.0;
     if (M == -INFINITY)
         return 0;
-    double den = 0.0;
+    double den = has_sink ? exp(sink - M) : 0.0;
     int used = 0;
     for (int s = 0; s < n; ++s) {
         if (lse[s] == -INFINITY)

@@ -162,6 +162,35 @@ def pin_freqs_llama3_factor_one(o):
     assert np.allclose(f, g, rtol=1e-15, atol=0)
 
 
+def pin_freqs_linear(o):
+    """Linear scaling divides every frequency by the factor (ALGENTA Decoder
+    families: gemma3 linear global scaling; UAII P0.2): g_i * factor equals
+    exp(-2i ln(theta) / d), and the rotation angle at position p is that of
+    plain RoPE at position p / factor.  Factor 1 is plain RoPE; and when
+    every wavelength is past original/low, llama3 scaling degenerates to the
+    same division, so the two branches agree there."""
+    for d, theta, factor in ((64, 1e4, 2.0), (128, 1e6, 8.0), (256, 1e6, 40.0)):
+        g = o.rope_freqs(d, O.LINEAR, theta, factor)
+        i = np.arange(d // 2)
+        assert np.allclose(g * factor, np.exp(-2.0 * i * math.log(theta) / d), rtol=1e-13,
+                           atol=0)
+        one = o.rope_freqs(d, O.LINEAR, theta, 1.0)
+        assert np.array_equal(one, o.rope_freqs(d, O.PLAIN, theta))
+        # llama3 with a tiny original context: every lambda > orig / low.
+        l3 = o.rope_freqs(d, O.LLAMA3, theta, factor, 1.0, 4.0, 1e-3)
+        assert np.array_equal(l3, g)
+        x = _rng(17, d).standard_normal(d)
+        p = 37
+        y = o.rope_apply(x, O.NEOX, g, p)
+        # plain rotation by angle (p / factor) * f_i written out
+        z = x.copy()
+        t = (p / factor) * np.exp(-2.0 * i * math.log(theta) / d)
+        h = d // 2
+        z[:h] = x[:h] * np.cos(t) - x[h:] * np.sin(t)
+        z[h:] = x[:h] * np.sin(t) + x[h:] * np.cos(t)
+        assert np.allclose(y, z, rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------------------
 # RoPE rotation  (UAII P0.2; LLAMAY Architectures; FREETOKEN Changes)
 # ---------------------------------------------------------------------------
@@ -510,6 +539,107 @@ def pin_attention_storage_formats(o):
     assert np.array_equal(c, e)
 
 
+def pin_attention_sink_zero_query(o):
+    """Attention sink (LLAMAY Architectures: gpt-oss; a per-head logit in the
+    softmax denominator only).  With q = 0 every visible score is 0, so the
+    weights are 1 / (n + e^sink) for each of the n visible keys and the output
+    is mean(v) * n / (n + e^sink); the sink itself contributes no value."""
+    B, H, Hkv, d, cap = 2, 4, 2, 64, 40
+    K, _ = _cache(B, Hkv, cap, d, 71)
+    V = np.zeros((B, Hkv, cap, d), np.float32)
+    V[..., 0] = np.arange(cap, dtype=np.float32)
+    V[..., 1] = 1.0
+    q = np.zeros((B, H, d))
+    lens = np.array([40, 9], np.int32)
+    sinks = np.array([-3.0, 0.0, 1.5, 4.0])
+    for W in (0, 5):
+        out = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                       seq_lens=lens, window=W, sinks=sinks)
+        for b, L in enumerate(lens):
+            lo = L - W if (W > 0 and L > W) else 0
+            n = L - lo
+            for h in range(H):
+                frac = n / (n + math.exp(sinks[h]))
+                assert abs(out[b, h, 1] - frac) < 1e-14, (W, b, h)
+                assert abs(out[b, h, 0] - frac * (lo + L - 1) / 2.0) < 1e-12, (W, b, h)
+
+
+def pin_attention_sink_denominator(o):
+    """With a sink the output is the sink-free output times Z / (Z + e^sink),
+    Z = sum of e^s over the visible (capped) scores, computed here in long
+    double from the scores; a very negative sink leaves the output unchanged."""
+    B, H, Hkv, d, cap = 1, 4, 2, 64, 33
+    K, V = _cache(B, Hkv, cap, d, 72)
+    q = 2.0 * _rng(73).standard_normal((B, H, d))
+    lens = np.array([33], np.int32)
+    sinks = np.array([-1.0, 0.5, 2.0, 6.0])
+    for W, c in ((0, 0.0), (12, 0.0), (0, 3.0)):
+        base = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens,
+                        window=W, softcap=c)
+        out = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens,
+                       window=W, softcap=c, sinks=sinks)
+        gone = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens,
+                        window=W, softcap=c, sinks=np.full(H, -1e4))
+        assert np.array_equal(gone, base)
+        for h in range(H):
+            s = o.scores(q=q[0, h], cache_k=K, k_dtype=O.F32, n_heads=H, b=0, h=h, L=33,
+                         window=W, softcap=c)
+            z = np.sum(np.exp(s[s > -np.inf].astype(np.longdouble)))
+            ratio = float(z / (z + np.exp(np.longdouble(sinks[h]))))
+            assert np.allclose(out[0, h], base[0, h] * ratio, rtol=1e-12, atol=1e-14), (W, c, h)
+
+
+def pin_combine_sink(o):
+    """The sink belongs to no split: combining the split partials with the
+    sink in the combine's denominator equals single-pass attention with the
+    sink, and equals a combine with one more split that has o = 0 and
+    lse = sink."""
+    H, Hkv, d, L = 4, 2, 64, 61
+    K, V = _cache(1, Hkv, L, d, 74)
+    q = 2.0 * _rng(75).standard_normal((1, H, d))
+    sinks = np.array([0.0, 3.0, -2.0, 8.0])
+    for W in (0, 20):
+        single = o.decode(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                          seq_lens=np.array([L], np.int32), window=W, sinks=sinks)
+        for S in (7, 32, L):
+            n = -(-L // S)
+            for h in range(H):
+                os_, ls = np.zeros((n, d)), np.zeros(n)
+                for sg in range(n):
+                    os_[sg], ls[sg], _ = o.split_partial(
+                        q_bh=q[0, h], cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                        n_heads=H, b=0, h=h, L=L, window=W, softcap=0.0, split_size=S, sigma=sg)
+                out, _ = o.combine(os_, ls, sink=sinks[h])
+                assert np.allclose(out, single[0, h], rtol=1e-12, atol=1e-13), (W, S, h)
+                ext, _ = o.combine(np.vstack([os_, np.zeros((1, d))]), np.append(ls, sinks[h]))
+                assert np.allclose(out, ext, rtol=1e-13, atol=1e-15), (W, S, h)
+
+
+def pin_q8_keys(o):
+    """q8 (LLAMAY The KV cache, in three precisions: keys and values both
+    quantised): int8 keys with a per-token scale score like f32 keys holding
+    code * scale (power-of-two scales keep that product exact in f32)."""
+    B, H, Hkv, d, cap = 2, 4, 2, 64, 30
+    rng = _rng(76)
+    kc = rng.integers(-127, 128, (B, Hkv, cap, d)).astype(np.int8)
+    ks = np.exp2(-rng.integers(3, 9, (B, Hkv, cap))).astype(np.float32)
+    vc = rng.integers(-127, 128, (B, Hkv, cap, d)).astype(np.int8)
+    vs = np.exp2(-rng.integers(3, 9, (B, Hkv, cap))).astype(np.float32)
+    kd = kc.astype(np.float32) * ks[..., None]
+    vd = vc.astype(np.float32) * vs[..., None]
+    q = 3.0 * rng.standard_normal((B, H, d))
+    lens = np.array([30, 13], np.int32)
+    for W, c in ((0, 0.0), (7, 0.0), (0, 4.0)):
+        a = o.decode(q=q, cache_k=kc, k_scale=ks, cache_v=vc, v_scale=vs, k_dtype=O.I8,
+                     v_dtype=O.I8, seq_lens=lens, window=W, softcap=c)
+        b = o.decode(q=q, cache_k=kd, cache_v=vd, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens,
+                     window=W, softcap=c)
+        assert np.array_equal(a, b), (W, c)
+    s8 = o.scores(q=q[0, 1], cache_k=kc, k_scale=ks, k_dtype=O.I8, n_heads=H, b=0, h=1, L=30)
+    sf = o.scores(q=q[0, 1], cache_k=kd, k_dtype=O.F32, n_heads=H, b=0, h=1, L=30)
+    assert np.array_equal(s8, sf)
+
+
 # ---------------------------------------------------------------------------
 # Split-K flash decoding  (ALGENTA Kernel path capabilities: split-K decode
 # partials; Conformance CLI: decode_attn=splitk_flash_decoding)
@@ -641,6 +771,41 @@ def pin_produce_norm_before_rope(o):
     xr = o.rope_apply(x, O.NEOX, g, 5)
     other = xr / math.sqrt(np.mean(xr * xr) + 1e-6) * w
     assert not np.allclose(qo[0, 0], other, rtol=1e-6)
+
+
+def pin_produce_q8_keys(o):
+    """The q8 producer stores, for each key, the quantiser applied to the
+    rotated key rounded to f32: the same codes and scale as quantising the
+    row an f32-key producer writes for the same inputs."""
+    B, H, Hkv, d, cap = 2, 4, 2, 64, 12
+    rng = _rng(77)
+    qi = rng.standard_normal((B, H, d)).astype(np.float32)
+    ki = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+    vi = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    pos = np.array([5, 11], np.int32)
+    rope = dict(pairing=O.INTERLEAVED, scaling=O.LLAMA3, theta=5e5, factor=8.0, low=1.0,
+                high=4.0, orig=8192.0)
+    norm = dict(enabled=True, eps=1e-6, offset=0, w_q=w, w_k=w)
+    kf = np.zeros((B, Hkv, cap, d), np.float32)
+    vf = np.zeros((B, Hkv, cap, d), np.float32)
+    qa = o.kv_produce(rope=rope, norm=norm, q_in=qi, k_in=ki, v_in=vi, positions=pos,
+                      k_dtype=O.F32, v_dtype=O.F32, cache_k=kf, cache_v=vf)
+    k8 = np.zeros((B, Hkv, cap, d), np.int8)
+    v8 = np.zeros((B, Hkv, cap, d), np.int8)
+    ks = np.zeros((B, Hkv, cap), np.float32)
+    vs = np.zeros((B, Hkv, cap), np.float32)
+    qb = o.kv_produce(rope=rope, norm=norm, q_in=qi, k_in=ki, v_in=vi, positions=pos,
+                      k_dtype=O.I8, v_dtype=O.I8, cache_k=k8, cache_v=v8, k_scale=ks,
+                      v_scale=vs)
+    assert np.array_equal(qa, qb)
+    for b in range(B):
+        for u in range(Hkv):
+            codes, sc = o.quantize_v(kf[b, u, pos[b]])
+            assert np.array_equal(k8[b, u, pos[b]], codes) and ks[b, u, pos[b]] == sc
+            codes, sc = o.quantize_v(vi[b, u])
+            assert np.array_equal(v8[b, u, pos[b]], codes) and vs[b, u, pos[b]] == sc
+    assert np.count_nonzero(k8) == np.count_nonzero(k8[np.arange(B), :, pos])
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

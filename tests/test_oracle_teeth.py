@@ -37,7 +37,17 @@ MUTANTS = [
     ("bf16_truncates", "double r = nearbyint(x / quantum) * quantum;", "double r = trunc(x / quantum) * quantum;"),
     ("softcap_unscaled", "s = softcap * tanh(s / softcap);", "s = softcap * tanh(s);"),
     ("score_unscaled", "double s = scale * acc;", "double s = acc;"),
-    ("softmax_unnormalised", "    for (int i = 0; i < d; ++i)\n        out[i] /= l;\n", "\n"),
+    ("linear_multiplies", "} else if (scaling == OR_LINEAR) {\n            g[i] = f / factor;",
+     "} else if (scaling == OR_LINEAR) {\n            g[i] = f * factor;"),
+    ("sink_unshifted", "double z = l + (has_sink ? exp(sink - m) : 0.0);",
+     "double z = l + (has_sink ? exp(sink) : 0.0);"),
+    ("sink_ignored_in_decode", "double z = l + (has_sink ? exp(sink - m) : 0.0);\n    for (int i = 0; i < d; ++i)\n        out[i] /= z;",
+     "double z = l + (has_sink ? exp(sink - m) : 0.0);\n    for (int i = 0; i < d; ++i)\n        out[i] /= l;"),
+    ("combine_sink_dropped", "double den = has_sink ? exp(sink - M) : 0.0;", "double den = 0.0;"),
+    ("q8_key_unrotated", "kf[i] = (float)tmp[i];", "kf[i] = k_in[slab * d + i];"),
+    ("q8_key_scale_ignored", "acc += q[i] * load_elem(k_dtype, cache_k, krow, d, i, k_scale);",
+     "acc += q[i] * load_elem(k_dtype == OR_I8 ? OR_F32 : k_dtype, cache_k, krow, d, i, k_scale);"),
+    ("softmax_unnormalised", "    for (int i = 0; i < d; ++i)\n        out[i] /= z;\n", "\n"),
     ("combine_unnormalised", "    for (int i = 0; i < d; ++i)\n        out[i] /= den;\n", "\n"),
     ("lse_missing_max", "*lse = m + log(l);", "*lse = log(l);"),
     ("vq8_scale_ignored", "return (double)((const int8_t *)base)[idx] * (double)scale[row];",
