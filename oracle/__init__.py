@@ -18,7 +18,7 @@ from . import build as _build
 
 F32, BF16, I8 = 0, 1, 2
 NEOX, INTERLEAVED = 0, 1
-PLAIN, LLAMA3, LINEAR = 0, 1, 2
+PLAIN, LLAMA3, LINEAR, YARN = 0, 1, 2, 3
 
 _dp = C.POINTER(C.c_double)
 _fp = C.POINTER(C.c_float)
@@ -63,12 +63,14 @@ class Oracle:
         lib.oracle_rms_norm.restype = None
         lib.oracle_rms_norm.argtypes = [_dp, C.c_int, _fp, C.c_int, C.c_double, _dp]
         lib.oracle_rope_freqs.restype = None
-        lib.oracle_rope_freqs.argtypes = [C.c_int, C.c_int] + [C.c_double] * 5 + [_dp]
+        lib.oracle_rope_freqs.argtypes = [C.c_int, C.c_int] + [C.c_double] * 5 + [C.c_int, _dp]
+        lib.oracle_yarn_attn_factor.restype = C.c_double
+        lib.oracle_yarn_attn_factor.argtypes = [C.c_double]
         lib.oracle_rope_apply.restype = None
         lib.oracle_rope_apply.argtypes = [_dp, C.c_int, C.c_int, _dp, C.c_int64]
         lib.oracle_kv_produce.restype = C.c_int
         lib.oracle_kv_produce.argtypes = (
-            [C.c_int] * 4 + [C.c_int, C.c_int] + [C.c_double] * 5
+            [C.c_int] * 4 + [C.c_int, C.c_int] + [C.c_double] * 5 + [C.c_int, C.c_double]
             + [C.c_int, C.c_double, C.c_int, _fp, _fp, _fp, _fp, _fp, _ip,
                C.c_int, C.c_int, C.c_int, _vp, _vp, _fp, _fp, _dp])
         lib.oracle_scores.restype = None
@@ -123,10 +125,14 @@ class Oracle:
 
     def rope_freqs(self, d: int, scaling: int = PLAIN, theta: float = 10000.0,
                    factor: float = 1.0, low: float = 1.0, high: float = 4.0,
-                   orig: float = 8192.0):
+                   orig: float = 8192.0, truncate: bool = True):
         g = np.zeros(d // 2, dtype=np.float64)
-        self.lib.oracle_rope_freqs(d, scaling, theta, factor, low, high, orig, _ptr(g, C.c_double))
+        self.lib.oracle_rope_freqs(d, scaling, theta, factor, low, high, orig, int(truncate),
+                                   _ptr(g, C.c_double))
         return g
+
+    def yarn_attn_factor(self, factor: float) -> float:
+        return float(self.lib.oracle_yarn_attn_factor(float(factor)))
 
     def rope_apply(self, x, pairing: int, g, pos: int):
         y = np.array(x, dtype=np.float64, copy=True)
@@ -159,6 +165,8 @@ class Oracle:
             B, H, Hkv, d, int(rope["pairing"]), int(rope["scaling"]), float(rope["theta"]),
             float(rope.get("factor", 1.0)), float(rope.get("low", 1.0)),
             float(rope.get("high", 4.0)), float(rope.get("orig", 8192.0)),
+            int(rope.get("truncate", True)),
+            float(rope.get("attn_factor") or self.yarn_attn_factor(rope.get("factor", 1.0))),
             ne, eps, off, _ptr(w_q, C.c_float), _ptr(w_k, C.c_float),
             _ptr(q_in, C.c_float), _ptr(k_in, C.c_float), _ptr(v_in, C.c_float),
             _ptr(positions, C.c_int32), k_dtype, v_dtype, cap, _ptr(cache_k), _ptr(cache_v),

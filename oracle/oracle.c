@@ -40,6 +40,7 @@
 #define OR_PLAIN 0
 #define OR_LLAMA3 1
 #define OR_LINEAR 2
+#define OR_YARN 3
 
 static const double OR_PI = 3.14159265358979323846264338327950288;
 
@@ -166,10 +167,36 @@ void oracle_rms_norm(const double *x, int d, const float *w, int offset,
  *   lambda < orig/high           -> keep f
  *   lambda > orig/low            -> f / factor
  *   otherwise, mu = (orig/lambda - low)/(high - low),
- *                                   (1 - mu) * f / factor + mu * f. */
+ *                                   (1 - mu) * f / factor + mu * f.
+ * YaRN ([UAII] P0.2 names YaRN beside Llama-3 scaling; [LLAMAY]
+ * Architectures: gpt-oss uses YaRN), as Hugging Face computes it (the
+ * reading the Llama-3 resolution sets): low and high are beta_slow and
+ * beta_fast, the rotation counts over the original context that bound the
+ * blend.  The pair index at which a frequency makes n turns over orig is
+ * c(n) = d ln(orig / (2 pi n)) / (2 ln theta); the blend runs over pair
+ * indices from c(beta_fast) to c(beta_slow) (rounded outwards to whole
+ * indices when truncate is set, then clamped to [0, d - 1]), with weight
+ * t_i = clamp((i - c_lo) / (c_hi - c_lo), 0, 1) on the divided frequency:
+ *   g_i = t_i * f / factor + (1 - t_i) * f. */
 void oracle_rope_freqs(int d, int scaling, double theta, double factor,
-                       double low, double high, double orig, double *g)
+                       double low, double high, double orig, int truncate,
+                       double *g)
 {
+    double c_lo = 0.0, c_hi = 1.0;
+    if (scaling == OR_YARN) {
+        c_lo = (double)d * log(orig / (2.0 * OR_PI * high)) / (2.0 * log(theta));
+        c_hi = (double)d * log(orig / (2.0 * OR_PI * low)) / (2.0 * log(theta));
+        if (truncate) {
+            c_lo = floor(c_lo);
+            c_hi = ceil(c_hi);
+        }
+        if (c_lo < 0.0)
+            c_lo = 0.0;
+        if (c_hi > (double)(d - 1))
+            c_hi = (double)(d - 1);
+        if (c_hi == c_lo)
+            c_hi += 0.001; /* a zero-width band still ramps */
+    }
     for (int i = 0; i < d / 2; ++i) {
         double f = pow(theta, -2.0 * (double)i / (double)d);
         if (scaling == OR_LLAMA3) {
@@ -184,6 +211,13 @@ void oracle_rope_freqs(int d, int scaling, double theta, double factor,
             }
         } else if (scaling == OR_LINEAR) {
             g[i] = f / factor;
+        } else if (scaling == OR_YARN) {
+            double t = ((double)i - c_lo) / (c_hi - c_lo);
+            if (t < 0.0)
+                t = 0.0;
+            if (t > 1.0)
+                t = 1.0;
+            g[i] = t * f / factor + (1.0 - t) * f;
         } else {
             g[i] = f;
         }
@@ -208,10 +242,11 @@ void oracle_rope_apply(double *x, int d, int pairing, const double *g, int64_t p
 }
 
 /* One head vector through the producer: optional RMSNorm, then RoPE
- * ([UAII] P1.2: the norm sits before RoPE). */
+ * ([UAII] P1.2: the norm sits before RoPE), then the rotary attention factor
+ * (1 except for YaRN, whose cos and sin carry it, so q and k both scale). */
 static void norm_rope(const float *in, int d, int norm_enabled, const float *w,
                       int offset, double eps, int pairing, const double *g,
-                      int64_t pos, double *out)
+                      int64_t pos, double attn_factor, double *out)
 {
     double x[256];
     for (int i = 0; i < d; ++i)
@@ -221,6 +256,16 @@ static void norm_rope(const float *in, int d, int norm_enabled, const float *w,
     else
         memcpy(out, x, sizeof(double) * (size_t)d);
     oracle_rope_apply(out, d, pairing, g, pos);
+    if (attn_factor != 1.0)
+        for (int i = 0; i < d; ++i)
+            out[i] *= attn_factor;
+}
+
+/* YaRN's attention factor: 0.1 ln(factor) + 1 for factor > 1, else 1
+ * (Hugging Face's default when the config gives none). */
+double oracle_yarn_attn_factor(double factor)
+{
+    return factor <= 1.0 ? 1.0 : 0.1 * log(factor) + 1.0;
 }
 
 /* Store one row (double values) in the cache's storage format. */
@@ -244,7 +289,8 @@ static void store_row_double(int dtype, void *base, int64_t row, int d,
  * Returns 0, or -1 for an argument outside what the oracle handles. */
 int oracle_kv_produce(int B, int H, int Hkv, int d,
                       int pairing, int scaling, double theta, double factor,
-                      double low, double high, double orig,
+                      double low, double high, double orig, int truncate,
+                      double attn_factor,
                       int norm_enabled, double eps, int offset,
                       const float *w_q, const float *w_k,
                       const float *q_in, const float *k_in, const float *v_in,
@@ -256,7 +302,9 @@ int oracle_kv_produce(int B, int H, int Hkv, int d,
     if (d > 256 || d < 2 || (d & 1) || H % Hkv != 0)
         return -1;
     double g[128];
-    oracle_rope_freqs(d, scaling, theta, factor, low, high, orig, g);
+    oracle_rope_freqs(d, scaling, theta, factor, low, high, orig, truncate, g);
+    if (scaling != OR_YARN)
+        attn_factor = 1.0;
     double tmp[256];
     for (int b = 0; b < B; ++b) {
         int64_t pos = positions[b];
@@ -265,13 +313,13 @@ int oracle_kv_produce(int B, int H, int Hkv, int d,
         for (int h = 0; h < H; ++h) {
             const float *src = q_in + ((int64_t)b * H + h) * d;
             norm_rope(src, d, norm_enabled, w_q, offset, eps, pairing, g, pos,
-                      q_out + ((int64_t)b * H + h) * d);
+                      attn_factor, q_out + ((int64_t)b * H + h) * d);
         }
         for (int u = 0; u < Hkv; ++u) {
             int64_t slab = (int64_t)b * Hkv + u;
             int64_t row = slab * cap + pos;
             norm_rope(k_in + slab * d, d, norm_enabled, w_k, offset, eps, pairing,
-                      g, pos, tmp);
+                      g, pos, attn_factor, tmp);
             if (k_dtype == OR_I8) {
                 /* q8 keys: the rotated key rounded to f32, then the same
                  * quantiser as the values ([LLAMAY] The KV cache, in three

@@ -191,6 +191,88 @@ def pin_freqs_linear(o):
         assert np.allclose(y, z, rtol=1e-12, atol=1e-13)
 
 
+def _turns(d, theta, orig):
+    """Turns each rotary pair makes over the original context: orig / wavelength."""
+    f = np.exp(-2.0 * np.arange(d // 2) * math.log(theta) / d)
+    return f, orig * f / (2.0 * math.pi)
+
+
+YARN_CASES = (  # (d, theta, factor, beta_slow, beta_fast, original context)
+    (64, 150000.0, 32.0, 1.0, 32.0, 4096),     # gpt-oss (LLAMAY Architectures)
+    (128, 10000.0, 16.0, 1.0, 32.0, 4096),
+    (256, 1e6, 4.0, 2.0, 64.0, 32768),
+)
+
+
+def pin_freqs_yarn_bands_by_turns(o):
+    """YaRN keeps the frequency of every pair that turns at least beta_fast
+    times over the original context and divides by the factor every pair that
+    turns at most beta_slow times; the pairs between are blended, with a
+    divisor strictly inside (1, factor).  Integer pair indices make this hold
+    with and without rounding of the band edges."""
+    for d, theta, factor, a, b, orig in YARN_CASES:
+        f, turns = _turns(d, theta, orig)
+        for trunc in (False, True):
+            g = o.rope_freqs(d, O.YARN, theta, factor, a, b, orig, trunc)
+            keep, scaled = turns >= b, turns <= a
+            assert np.allclose(g[keep], f[keep], rtol=1e-14, atol=0), (d, trunc)
+            assert np.allclose(g[scaled], f[scaled] / factor, rtol=1e-14, atol=0), (d, trunc)
+            mid = ~(keep | scaled)
+            assert mid.sum() >= 2
+            div = f[mid] / g[mid]
+            assert np.all((div > 1.0 + 1e-9) & (div < factor - 1e-9)), (d, trunc)
+
+
+def pin_freqs_yarn_ramp_in_index(o):
+    """Between the band edges the weight t of the divided frequency,
+    g = (1 - t) f + t f / factor, is affine in the pair index (constant first
+    differences); with rounded edges t steps by 1 / (whole number of pairs)."""
+    for d, theta, factor, a, b, orig in YARN_CASES:
+        f, turns = _turns(d, theta, orig)
+        for trunc in (False, True):
+            g = o.rope_freqs(d, O.YARN, theta, factor, a, b, orig, trunc)
+            t = (1.0 - g / f) / (1.0 - 1.0 / factor)
+            inside = np.nonzero((t > 1e-12) & (t < 1.0 - 1e-12))[0]
+            assert np.array_equal(inside, np.arange(inside[0], inside[-1] + 1))
+            step = np.diff(t[inside])
+            assert np.allclose(step, step[0], rtol=1e-9, atol=1e-13), (d, trunc)
+            if trunc:
+                n = 1.0 / step[0]
+                assert abs(n - round(n)) < 1e-9, (d, n)
+                # first blended pair sits one step above 0
+                assert abs(t[inside[0]] - step[0]) < 1e-12
+
+
+def pin_yarn_factor_one_and_attention_factor(o):
+    """Factor 1 gives plain frequencies and attention factor 1; the attention
+    factor is 1 + 0.1 ln(factor) (gpt-oss, factor 32: 1.3465735902799727),
+    and at position 0 (no rotation) the producer scales q and k by it."""
+    d = 64
+    assert np.allclose(o.rope_freqs(d, O.YARN, 150000.0, 1.0, 1.0, 32.0, 4096, False),
+                       o.rope_freqs(d, O.PLAIN, 150000.0), rtol=1e-15, atol=0)
+    assert o.yarn_attn_factor(1.0) == 1.0
+    assert abs(o.yarn_attn_factor(32.0) - 1.3465735902799727) < 1e-15
+    rng = _rng(78)
+    qi = rng.standard_normal((1, 2, d)).astype(np.float32)
+    ki = rng.standard_normal((1, 1, d)).astype(np.float32)
+    ck = np.zeros((1, 1, 4, d), np.float32)
+    cv = np.zeros((1, 1, 4, d), np.float32)
+    rope = dict(pairing=O.NEOX, scaling=O.YARN, theta=150000.0, factor=32.0, low=1.0,
+                high=32.0, orig=4096.0, truncate=False)
+    qo = o.kv_produce(rope=rope, norm=None, q_in=qi, k_in=ki, v_in=ki,
+                      positions=np.array([0], np.int32), k_dtype=O.F32, v_dtype=O.F32,
+                      cache_k=ck, cache_v=cv)
+    m = 1.0 + 0.1 * math.log(32.0)
+    assert np.allclose(qo[0], qi[0].astype(np.float64) * m, rtol=1e-15, atol=0)
+    assert np.array_equal(ck[0, 0, 0], (ki[0, 0].astype(np.float64) * m).astype(np.float32))
+    assert np.array_equal(cv[0, 0, 0], ki[0, 0])      # values are not rotated or scaled
+    # an explicit attention factor replaces the default
+    qo2 = o.kv_produce(rope=dict(rope, attn_factor=2.0), norm=None, q_in=qi, k_in=ki, v_in=ki,
+                       positions=np.array([0], np.int32), k_dtype=O.F32, v_dtype=O.F32,
+                       cache_k=ck, cache_v=cv)
+    assert np.allclose(qo2[0], 2.0 * qi[0].astype(np.float64), rtol=1e-15, atol=0)
+
+
 # ---------------------------------------------------------------------------
 # RoPE rotation  (UAII P0.2; LLAMAY Architectures; FREETOKEN Changes)
 # ---------------------------------------------------------------------------

@@ -39,6 +39,13 @@ MUTANTS = [
     ("score_unscaled", "double s = scale * acc;", "double s = acc;"),
     ("linear_multiplies", "} else if (scaling == OR_LINEAR) {\n            g[i] = f / factor;",
      "} else if (scaling == OR_LINEAR) {\n            g[i] = f * factor;"),
+    ("yarn_ramp_reversed", "g[i] = t * f / factor + (1.0 - t) * f;",
+     "g[i] = (1.0 - t) * f / factor + t * f;"),
+    ("yarn_edges_swapped", "log(orig / (2.0 * OR_PI * high))", "log(orig / (2.0 * OR_PI * low))"),
+    ("yarn_truncate_inward", "c_lo = floor(c_lo);\n            c_hi = ceil(c_hi);",
+     "c_lo = ceil(c_lo);\n            c_hi = floor(c_hi);"),
+    ("yarn_attn_factor_dropped", "    if (attn_factor != 1.0)\n        for", "    if (0)\n        for"),
+    ("yarn_attn_factor_log2", "0.1 * log(factor) + 1.0", "0.1 * log2(factor) + 1.0"),
     ("sink_unshifted", "double z = l + (has_sink ? exp(sink - m) : 0.0);",
      "double z = l + (has_sink ? exp(sink) : 0.0);"),
     ("sink_ignored_in_decode", "double z = l + (has_sink ? exp(sink - m) : 0.0);\n    for (int i = 0; i < d; ++i)\n        out[i] /= z;",
