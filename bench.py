@@ -29,13 +29,19 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn KV GB/s & % of HBM peak; seq-steps/s at B=32, ctx 8K, d128"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "gqa_decode_attention_kv_amd", "csrc", "decode_partial.hip")
+CSRC = os.path.join(ROOT, "gqa_decode_attention_kv_amd", "csrc")
+# The partial kernel's template and the contiguous-cache instantiation.
+KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("decode_partial_kernel.h", "decode_partial.hip",
+                                               "launch.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -74,11 +80,11 @@ def cpu_baseline(inputs, min_seconds: float = 10.0, max_rounds: int = 8) -> dict
         norm = dict(enabled=True, eps=w.qk_norm.eps, offset=w.qk_norm.offset, w_q=inputs.w_q,
                     w_k=inputs.w_k)
     ck, cv = inputs.cache_k, inputs.cache_v
-    vs = inputs.v_scale
+    vs, ks = inputs.v_scale, inputs.k_scale
     t0 = time.perf_counter()
     q = o.kv_produce(rope=w.rope.as_dict(), norm=norm, q_in=inputs.q_in, k_in=inputs.k_in,
                      v_in=inputs.v_in, positions=inputs.positions, k_dtype=w.k_dtype,
-                     v_dtype=w.v_dtype, cache_k=ck, cache_v=cv, v_scale=vs)
+                     v_dtype=w.v_dtype, cache_k=ck, cache_v=cv, v_scale=vs, k_scale=ks)
     t_produce = time.perf_counter() - t0
     seqs_done, kv_bytes, elapsed = 0, 0, t_produce
     order = list(range(w.batch))
@@ -89,9 +95,9 @@ def cpu_baseline(inputs, min_seconds: float = 10.0, max_rounds: int = 8) -> dict
 
         def one(b):
             pairs = [(b, h) for h in range(w.n_heads)]
-            o.decode(q=q, cache_k=ck, cache_v=cv, v_scale=vs, k_dtype=w.k_dtype,
+            o.decode(q=q, cache_k=ck, cache_v=cv, v_scale=vs, k_scale=ks, k_dtype=w.k_dtype,
                      v_dtype=w.v_dtype, seq_lens=inputs.seq_lens, window=w.window,
-                     softcap=w.softcap, pairs=pairs)
+                     softcap=w.softcap, pairs=pairs, sinks=inputs.sinks)
 
         t0 = time.perf_counter()
         with ThreadPoolExecutor(per_round) as ex:
@@ -217,9 +223,12 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": name, "batch": w.batch, "ctx": int(inputs.seq_lens.max()),
                    "n_heads": w.n_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
-                   "kv_cache": {0: "f32", 1: "bf16", 2: "int8"}[w.k_dtype] + "/" +
-                   {0: "f32", 1: "bf16", 2: "int8(vq8)"}[w.v_dtype],
+                   "kv_cache": ("q8" if w.k_dtype == 2 else
+                                {0: "f32", 1: "bf16"}[w.k_dtype] + "/" +
+                                {0: "f32", 1: "bf16", 2: "int8(vq8)"}[w.v_dtype]),
                    "split_size": st.split_size, "window": w.window, "softcap": w.softcap,
+                   "rope_scaling": {0: "plain", 1: "llama3", 2: "linear", 3: "yarn"}[w.rope.scaling],
+                   "attention_sink": w.sink,
                    "layout": f"paged(block_size={args.paged})" if args.paged else "contiguous",
                    "parallelism": "single-gpu"},
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),

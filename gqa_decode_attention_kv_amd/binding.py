@@ -19,9 +19,10 @@ LIBRARY = os.path.join(HERE, "libuaii_decode.so")
 OK, ERR_INVALID_ARGUMENT, ERR_NOT_IMPLEMENTED, ERR_DEVICE = 0, 1, 2, 3
 F32, BF16, I8 = 0, 1, 2
 ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
-ROPE_PLAIN, ROPE_LLAMA3 = 0, 1
+ROPE_PLAIN, ROPE_LLAMA3, ROPE_LINEAR, ROPE_YARN = 0, 1, 2, 3
 
-EXPORTS = ("uaii_last_error", "uaii_kv_produce", "uaii_decode_attn", "uaii_decode_combine")
+EXPORTS = ("uaii_last_error", "uaii_kv_produce", "uaii_decode_attn", "uaii_decode_combine",
+           "uaii_decode_combine_sink")
 
 
 class UaiiError(RuntimeError):
@@ -39,7 +40,8 @@ class Shape(C.Structure):
 class Rope(C.Structure):
     _fields_ = [("pairing", C.c_int32), ("scaling", C.c_int32), ("theta", C.c_double),
                 ("factor", C.c_double), ("low_freq_factor", C.c_double),
-                ("high_freq_factor", C.c_double), ("original_max_position", C.c_int32)]
+                ("high_freq_factor", C.c_double), ("original_max_position", C.c_int32),
+                ("truncate", C.c_int32), ("attention_factor", C.c_double)]
 
 
 class QKNorm(C.Structure):
@@ -51,7 +53,7 @@ class KVCache(C.Structure):
     _fields_ = [("k_dtype", C.c_int32), ("v_dtype", C.c_int32), ("capacity", C.c_int32),
                 ("k", C.c_void_p), ("v", C.c_void_p), ("v_scale", C.c_void_p),
                 ("block_table", C.c_void_p), ("block_size", C.c_int32),
-                ("max_blocks", C.c_int32), ("num_blocks", C.c_int32)]
+                ("max_blocks", C.c_int32), ("num_blocks", C.c_int32), ("k_scale", C.c_void_p)]
 
 
 _lib = None
@@ -77,6 +79,9 @@ def load() -> C.CDLL:
         lib.uaii_decode_combine.restype = C.c_int
         lib.uaii_decode_combine.argtypes = [C.POINTER(Shape), ip, C.c_int32, C.c_int32, C.c_int32,
                                             vp, vp, vp, vp]
+        lib.uaii_decode_combine_sink.restype = C.c_int
+        lib.uaii_decode_combine_sink.argtypes = [C.POINTER(Shape), ip, C.c_int32, C.c_int32,
+                                                 C.c_int32, vp, vp, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -120,3 +125,10 @@ def decode_combine(shape: Shape, seq_lens, window: int, split_size: int, max_spl
     arr, p = _host_i32(seq_lens, shape.batch)
     _check(load().uaii_decode_combine(C.byref(shape), p, window, split_size, max_splits, part_o,
                                       part_lse, out, stream))
+
+
+def decode_combine_sink(shape: Shape, seq_lens, window: int, split_size: int, max_splits: int,
+                        part_o: int, part_lse: int, sinks: int, out: int, stream: int = 0) -> None:
+    arr, p = _host_i32(seq_lens, shape.batch)
+    _check(load().uaii_decode_combine_sink(C.byref(shape), p, window, split_size, max_splits,
+                                           part_o, part_lse, sinks, out, stream))

@@ -10,6 +10,7 @@
 // closed with InvalidArgument / NotImplemented).
 #include "uaii_decode.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -80,13 +81,14 @@ uaii_status check_shape(const char* fn, const uaii_attn_shape* s) {
 
 uaii_status check_cache(const char* fn, const uaii_kv_cache* c) {
   REQUIRE(c != nullptr, kInvalid, "cache is NULL; pass a uaii_kv_cache");
-  REQUIRE(c->k_dtype != UAII_I8, kNotImpl,
-          "k_dtype=int8 (a q8 cache, int8 keys) is not supported; keys stay exact: use k_dtype f32 or "
-          "bf16, with v_dtype int8 for the vq8 cache");
-  REQUIRE(c->k_dtype == UAII_F32 || c->k_dtype == UAII_BF16, kInvalid,
-          "k_dtype=%d is not a dtype code (f32=0, bf16=1)", c->k_dtype);
+  REQUIRE(c->k_dtype == UAII_F32 || c->k_dtype == UAII_BF16 || c->k_dtype == UAII_I8, kInvalid,
+          "k_dtype=%d is not a dtype code (f32=0, bf16=1, int8=2)", c->k_dtype);
   REQUIRE(c->v_dtype == UAII_F32 || c->v_dtype == UAII_BF16 || c->v_dtype == UAII_I8, kInvalid,
           "v_dtype=%d is not a dtype code (f32=0, bf16=1, int8=2)", c->v_dtype);
+  REQUIRE(c->k_dtype != UAII_I8 || c->v_dtype == UAII_I8, kNotImpl,
+          "k_dtype=int8 with v_dtype=%d is not supported (supported: int8 keys only in the q8 cache, "
+          "with int8 values); use f32 or bf16 keys, or v_dtype int8",
+          c->v_dtype);
   REQUIRE(c->capacity >= 1, kInvalid, "capacity=%d is invalid (must be >= 1)", c->capacity);
   REQUIRE(c->capacity <= kMaxCapacity, kNotImpl, "capacity=%d is not supported (supported: 1..%d)",
           c->capacity, kMaxCapacity);
@@ -107,6 +109,11 @@ uaii_status check_cache(const char* fn, const uaii_kv_cache* c) {
     REQUIRE(c->v_scale != nullptr, kInvalid,
             "cache.v_scale is NULL but v_dtype is int8 (vq8 needs one f32 scale per token per kv head)");
     CHECK_PTR("cache.v_scale", c->v_scale, 4);
+  }
+  if (c->k_dtype == UAII_I8) {
+    REQUIRE(c->k_scale != nullptr, kInvalid,
+            "cache.k_scale is NULL but k_dtype is int8 (q8 needs one f32 key scale per token per kv head)");
+    CHECK_PTR("cache.k_scale", c->k_scale, 4);
   }
   return UAII_OK;
 }
@@ -188,10 +195,29 @@ uaii_status uaii_kv_produce(const uaii_attn_shape* shape, const uaii_rope* rope,
   REQUIRE(rope != nullptr, kInvalid, "rope is NULL; pass a uaii_rope");
   REQUIRE(rope->pairing == UAII_ROPE_NEOX || rope->pairing == UAII_ROPE_INTERLEAVED, kInvalid,
           "rope.pairing=%d is not a pairing code (neox=0, interleaved=1)", rope->pairing);
-  REQUIRE(rope->scaling == UAII_ROPE_PLAIN || rope->scaling == UAII_ROPE_LLAMA3, kNotImpl,
-          "unsupported rope_scaling.type=%d (supported: plain=0, llama3=1)", rope->scaling);
+  REQUIRE(rope->scaling >= UAII_ROPE_PLAIN && rope->scaling <= UAII_ROPE_YARN, kNotImpl,
+          "unsupported rope_scaling.type=%d (supported: plain=0, llama3=1, linear=2, yarn=3)",
+          rope->scaling);
   REQUIRE(finite_pos(rope->theta), kInvalid, "rope.theta=%g is invalid (must be finite and > 0)",
           rope->theta);
+  if (rope->scaling == UAII_ROPE_LINEAR)
+    REQUIRE(finite_pos(rope->factor), kInvalid,
+            "rope.factor=%g is invalid for linear scaling (must be finite and > 0)", rope->factor);
+  if (rope->scaling == UAII_ROPE_YARN) {
+    REQUIRE(std::isfinite(rope->factor) && rope->factor >= 1.0, kInvalid,
+            "rope.factor=%g is invalid for yarn scaling (must be finite and >= 1)", rope->factor);
+    REQUIRE(finite_pos(rope->low_freq_factor), kInvalid,
+            "rope.low_freq_factor (yarn beta_slow)=%g is invalid (must be finite and > 0)",
+            rope->low_freq_factor);
+    REQUIRE(std::isfinite(rope->high_freq_factor) && rope->high_freq_factor > rope->low_freq_factor,
+            kInvalid, "rope.high_freq_factor (yarn beta_fast)=%g must be finite and > beta_slow=%g",
+            rope->high_freq_factor, rope->low_freq_factor);
+    REQUIRE(rope->original_max_position > 0, kInvalid,
+            "rope.original_max_position=%d is invalid (must be > 0)", rope->original_max_position);
+    REQUIRE(std::isfinite(rope->attention_factor) && rope->attention_factor >= 0.0, kInvalid,
+            "rope.attention_factor=%g is invalid (must be finite and > 0, or 0 for the default)",
+            rope->attention_factor);
+  }
   if (rope->scaling == UAII_ROPE_LLAMA3) {
     REQUIRE(std::isfinite(rope->factor) && rope->factor >= 1.0, kInvalid,
             "rope.factor=%g is invalid for llama3 scaling (must be finite and >= 1)", rope->factor);
@@ -234,6 +260,27 @@ uaii_status uaii_kv_produce(const uaii_attn_shape* shape, const uaii_rope* rope,
   a.low = rope->low_freq_factor;
   a.high = rope->high_freq_factor;
   a.orig = static_cast<double>(rope->original_max_position);
+  a.attn_factor = 1.0;
+  if (rope->scaling == UAII_ROPE_YARN) {
+    // Blend band in pair indices; the same quantities for every pair, so
+    // they are computed once here (host double precision).
+    const double pi = 3.14159265358979323846;
+    const double d = static_cast<double>(shape->head_dim);
+    double lo = d * std::log(a.orig / (2.0 * pi * rope->high_freq_factor)) / (2.0 * std::log(rope->theta));
+    double hi = d * std::log(a.orig / (2.0 * pi * rope->low_freq_factor)) / (2.0 * std::log(rope->theta));
+    if (rope->truncate) {
+      lo = std::floor(lo);
+      hi = std::ceil(hi);
+    }
+    lo = std::max(lo, 0.0);
+    hi = std::min(hi, d - 1.0);
+    if (hi == lo) hi += 0.001;
+    a.c_lo = lo;
+    a.c_hi = hi;
+    a.attn_factor = rope->attention_factor > 0.0
+                        ? rope->attention_factor
+                        : (rope->factor <= 1.0 ? 1.0 : 0.1 * std::log(rope->factor) + 1.0);
+  }
   a.norm_enabled = norm ? 1 : 0;
   a.norm_offset = norm ? qk_norm->offset : 0;
   a.norm_eps = norm ? qk_norm->eps : 0.0f;
@@ -247,7 +294,8 @@ uaii_status uaii_kv_produce(const uaii_attn_shape* shape, const uaii_rope* rope,
   a.cap = cache->capacity;
   a.k = cache->k;
   a.v = cache->v;
-  a.v_scale = cache->v_scale;
+  a.k_scale = cache->k_dtype == UAII_I8 ? cache->k_scale : nullptr;
+  a.v_scale = cache->v_dtype == UAII_I8 ? cache->v_scale : nullptr;
   a.q_out = q_out;
   a.block_table = cache->block_table;
   a.block_size = cache->block_table ? cache->block_size : 0;
@@ -289,6 +337,7 @@ uaii_status uaii_decode_attn(const uaii_attn_shape* shape, const uaii_kv_cache* 
   a.max_splits = max_splits;
   a.k = cache->k;
   a.v = cache->v;
+  a.k_scale = cache->k_dtype == UAII_I8 ? cache->k_scale : nullptr;
   a.v_scale = cache->v_dtype == UAII_I8 ? cache->v_scale : nullptr;
   a.q = q;
   a.part_o = part_o;
@@ -315,10 +364,13 @@ uaii_status uaii_decode_attn(const uaii_attn_shape* shape, const uaii_kv_cache* 
                                                        static_cast<hipStream_t>(stream)));
 }
 
-uaii_status uaii_decode_combine(const uaii_attn_shape* shape, const int32_t* seq_lens, int32_t window,
-                                int32_t split_size, int32_t max_splits, const float* part_o,
-                                const float* part_lse, float* out, void* stream) {
-  const char* fn = "uaii_decode_combine";
+}  // extern "C"
+
+namespace {
+
+uaii_status combine(const char* fn, const uaii_attn_shape* shape, const int32_t* seq_lens, int32_t window,
+                    int32_t split_size, int32_t max_splits, const float* part_o, const float* part_lse,
+                    const float* sinks, float* out, void* stream) {
   g_error.clear();
   uaii_status st = check_shape(fn, shape);
   if (st != UAII_OK) return st;
@@ -333,10 +385,33 @@ uaii_status uaii_decode_combine(const uaii_attn_shape* shape, const int32_t* seq
   a.max_splits = max_splits;
   a.part_o = part_o;
   a.part_lse = part_lse;
+  a.sinks = sinks;
   a.out = out;
   build_table(shape->batch, seq_lens, window, split_size, &a.t);
   return device_status(fn, uaii::launch_decode_combine(shape->head_dim, shape->batch, a,
                                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+uaii_status uaii_decode_combine(const uaii_attn_shape* shape, const int32_t* seq_lens, int32_t window,
+                                int32_t split_size, int32_t max_splits, const float* part_o,
+                                const float* part_lse, float* out, void* stream) {
+  return combine("uaii_decode_combine", shape, seq_lens, window, split_size, max_splits, part_o, part_lse,
+                 nullptr, out, stream);
+}
+
+uaii_status uaii_decode_combine_sink(const uaii_attn_shape* shape, const int32_t* seq_lens,
+                                     int32_t window, int32_t split_size, int32_t max_splits,
+                                     const float* part_o, const float* part_lse, const float* sinks,
+                                     float* out, void* stream) {
+  const char* fn = "uaii_decode_combine_sink";
+  g_error.clear();
+  CHECK_PTR("sinks", sinks, 4);
+  return combine(fn, shape, seq_lens, window, split_size, max_splits, part_o, part_lse, sinks, out,
+                 stream);
 }
 
 }  // extern "C"

@@ -4,6 +4,11 @@
 // decode_attn=splitk_flash_decoding; Kernel path capabilities: split-K decode
 // partials).  One wave per (b, h); only the splits that hold visible keys
 // are read, so the partial buffer needs no initialisation.
+//
+// With an attention sink ("llamay - Models and formats", Architectures:
+// gpt-oss), the head's sink logit joins the denominator as a term
+// e^(sink - M) that carries no value: the running max starts at the sink
+// with a denominator of 1 and no numerator.
 #include "launch.h"
 
 #include <math.h>
@@ -27,6 +32,10 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineArgs a) {
   // One pass with a running max: the loads of U splits are issued together,
   // and for up to U splits no cross-lane reduction is needed at all.
   float M = -INFINITY, den = 0.0f;
+  if (a.sinks != nullptr) {
+    M = a.sinks[h];
+    den = 1.0f;
+  }
   float num[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) num[e] = 0.0f;

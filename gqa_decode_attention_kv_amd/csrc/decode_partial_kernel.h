@@ -10,7 +10,8 @@
 // fact requirements: GQA ratio, attention scale 1/sqrt(head_dim));
 // "Universal AI Inference - Hugging Face decoder completeness" (P1.4:
 // sliding window and attention-logit softcap as a tanh clip); "llamay -
-// Models and formats" (The KV cache, in three precisions: vq8 values).
+// Models and formats" (The KV cache, in three precisions: vq8 values, q8
+// keys and values).
 //
 // Design (gfx950, bandwidth bound, no MFMA: one query row per kv head is a
 // GEMV; arithmetic intensity is 2-5 flop per KV byte, far below the ridge):
@@ -21,8 +22,8 @@
 //   * the G query heads that share the kv head are held in registers, so
 //     every K and V byte is read from HBM exactly once per group;
 //   * a wave walks its split in chunks of up to 512 rows with two passes per
-//     chunk: K (16-byte coalesced loads, a row spread over d*sizeof(K)/16
-//     lanes, scores reduced across those lanes with DPP) with raw scores
+//     chunk: K (coalesced 16-byte loads, 8-byte for int8, a row spread over
+//     d*sizeof(K)/load lanes, scores reduced across those lanes with DPP) with raw scores
 //     parked in LDS, then V with the softmax weights broadcast from LDS; the
 //     running max and sum rescale only between chunks;
 //   * scores live in the log2 domain (q pre-multiplied by scale*log2 e) so the
@@ -30,6 +31,9 @@
 //     in the weights pass (it is monotonic, so the max commutes with it);
 //   * vq8: int8 codes are widened in registers and the per-token scale is
 //     folded into the softmax weight, so dequantisation costs no extra pass;
+//   * q8 keys: codes are widened the same way (as code + 128) in the K pass;
+//     the 128 * sum(q) offset and the key's per-token scale are applied to
+//     the raw score once per row, where the chunk max is taken;
 //   * at the end the wave sums its row groups across lanes and writes one
 //     normalised partial and its log-sum-exp per query head.
 // Loads run as a rolling pipeline (the next tiles are requested as soon as
@@ -42,17 +46,21 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "launch.h"
 
 namespace uaii {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;                  // independent waves per work-group
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerChunk = 512;         // rows a wave scores before it reads values
-constexpr int kLoadsInFlight = 8;          // 16-byte loads per lane kept in flight
+constexpr int kLoadsInFlight = 8;          // 16-byte loads per lane kept in flight (or
+                                           // twice as many 8-byte loads)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -114,8 +122,12 @@ __device__ inline float wave_sum(float x) { return group_sum<64>(x); }
 
 // KV rows are read once per step: non-temporal loads stream them past the
 // caches instead of evicting reusable lines (worth about 8% of bandwidth).
-__device__ inline u32x4 load16(const void* p) {
-  return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+template <int NB>
+using vec_t = typename std::conditional<NB == 16, u32x4, u32x2>::type;
+
+template <int NB>
+__device__ inline vec_t<NB> load_nt(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const vec_t<NB>*>(p));
 }
 
 // Score in the log2 domain from a raw score: with a softcap c the raw score is
@@ -125,9 +137,9 @@ __device__ inline float capped_log2(float s, bool capped, float c, float c_inv) 
   return capped ? c * tanhf(s * c_inv) * kLog2e : s;
 }
 
-// Widen the 16 bytes of one lane to E floats.
-template <int DT, int E>
-__device__ inline void widen(const u32x4& w, float (&out)[E]) {
+// Widen the bytes one lane loaded (16 for f32 / bf16, 8 for int8) to E floats.
+template <int DT, int E, typename V>
+__device__ inline void widen(const V& w, float (&out)[E]) {
   if constexpr (DT == kF32) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[e] = __uint_as_float(w[e]);
@@ -138,17 +150,22 @@ __device__ inline void widen(const u32x4& w, float (&out)[E]) {
       out[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
     }
   } else {
-    // vq8 codes are widened as code + 128 (one v_cvt_f32_ubyte per code after
-    // flipping the sign bits); the caller removes 128 * sum(p) at the end.
+    // int8 codes are widened as code + 128 (one v_cvt_f32_ubyte per code after
+    // flipping the sign bits); for values the caller removes 128 * sum(p) at
+    // the end, for keys 128 * sum(q) from each raw score.
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
+    for (int e = 0; e < E; ++e)
       out[e] = static_cast<float>(((w[e >> 2] ^ 0x80808080u) >> (8 * (e & 3))) & 0xFFu);
   }
 }
 
+// Element size and the bytes one lane loads per row segment.  int8 rows
+// use 8-byte loads, so a lane holds 8 codes: the query and accumulator
+// registers then have the bf16 layout instead of twice as many entries.
 template <int DT>
 struct Elem {
   static constexpr int bytes = DT == kF32 ? 4 : (DT == kBF16 ? 2 : 1);
+  static constexpr int load = DT == kI8 ? 8 : 16;
 };
 
 // amdgpu_waves_per_eu(2, 8): at least two waves per SIMD.  Without the hint
@@ -158,21 +175,25 @@ template <int D, int G, int KT, int VT, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 decode_partial_kernel(AttnArgs a) {
   constexpr int KB = Elem<KT>::bytes, VB = Elem<VT>::bytes;
-  constexpr int KLPR = D * KB / 16;  // lanes per K row
-  constexpr int KRPL = 64 / KLPR;    // K rows per wave load
-  constexpr int KE = 16 / KB;        // K elements per lane
-  constexpr int VLPR = D * VB / 16;
+  constexpr int KLB = Elem<KT>::load, VLB = Elem<VT>::load;
+  constexpr int KLPR = D * KB / KLB;  // lanes per K row
+  constexpr int KRPL = 64 / KLPR;     // K rows per wave load
+  constexpr int KE = KLB / KB;        // K elements per lane
+  constexpr int VLPR = D * VB / VLB;
   constexpr int VRPL = 64 / VLPR;
-  constexpr int VE = 16 / VB;
-  // Eight 16-byte loads per lane in flight; four for G = 8, whose query and
-  // accumulator registers would otherwise leave room for one wave per SIMD.
+  constexpr int VE = VLB / VB;
+  // Eight 16-byte loads per lane in flight (the same bytes in 8-byte loads);
+  // half as many for G = 8, whose query and accumulator registers would
+  // otherwise leave room for one wave per SIMD.
   constexpr int LF = G >= 8 ? kLoadsInFlight / 2 : kLoadsInFlight;
-  constexpr int UK = (LF * KRPL <= kRowsPerChunk) ? LF : kRowsPerChunk / KRPL;
-  constexpr int UV = (LF * VRPL <= kRowsPerChunk) ? LF : kRowsPerChunk / VRPL;
+  constexpr int LFK = LF * 16 / KLB, LFV = LF * 16 / VLB;
+  constexpr int UK = (LFK * KRPL <= kRowsPerChunk) ? LFK : kRowsPerChunk / KRPL;
+  constexpr int UV = (LFV * VRPL <= kRowsPerChunk) ? LFV : kRowsPerChunk / VRPL;
   // Paged caches align tiles to blocks, so a chunk's rows sit up to 15 rows
   // after the start of its LDS window.
   constexpr int kLdsRows = kRowsPerChunk + (PAGED ? 16 : 0);
   constexpr int kScaleRegs = (VT == kI8) ? (kLdsRows + 63) / 64 : 1;
+  constexpr int kKScaleRegs = (KT == kI8) ? (kLdsRows + 63) / 64 : 1;
   static_assert(kRowsPerChunk % (UK * KRPL) == 0 && kRowsPerChunk % (UV * VRPL) == 0, "tiling");
   static_assert(KLPR >= 4 && VLPR >= 4, "row must span at least a quad");
 
@@ -199,6 +220,7 @@ decode_partial_kernel(AttnArgs a) {
   const char* kbase = static_cast<const char*>(a.k) + slab * (D * KB);
   const char* vbase = static_cast<const char*>(a.v) + slab * (D * VB);
   const float* sbase = (VT == kI8) ? a.v_scale + slab : nullptr;
+  const float* ksbase = (KT == kI8) ? a.k_scale + slab : nullptr;
 
   // Query group in registers: lane holds q[h][kc*KE .. kc*KE + KE) for its K segment.
   const int kr = lane / KLPR, kc = lane % KLPR;
@@ -216,6 +238,22 @@ decode_partial_kernel(AttnArgs a) {
         q[g][e + 3] = v.w * a.q_mul;
       }
     }
+  }
+  // q8 keys: each raw score carries 128 * sum(q_h) from the code offset.
+  float c128[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float t = 0.0f;
+    if constexpr (KT == kI8) {
+#pragma unroll
+      for (int e = 0; e < KE; ++e) t += q[g][e];
+    }
+    c128[g] = t;
+  }
+  if constexpr (KT == kI8) {
+    group_sum_n<KLPR, G>(c128);
+#pragma unroll
+    for (int g = 0; g < G; ++g) c128[g] *= 128.0f;
   }
   const bool capped = a.softcap > 0.0f;
   const float cap_c = a.softcap, cap_inv = capped ? 1.0f / a.softcap : 0.0f;
@@ -274,36 +312,42 @@ decode_partial_kernel(AttnArgs a) {
       if constexpr (PAGED) {
         const int R = TK0 + t * KRPL;
         const int row = min(max(R + kr, a0), last);
-        return tile_base(a.k, R, D * KB) + static_cast<uint32_t>((row - R) * (D * KB) + kc * 16);
+        return tile_base(a.k, R, D * KB) + static_cast<uint32_t>((row - R) * (D * KB) + kc * KLB);
       } else {
-        return kblk + static_cast<uint32_t>(min(t * KRPL + kr, nrows - 1) * (D * KB) + kc * 16);
+        return kblk + static_cast<uint32_t>(min(t * KRPL + kr, nrows - 1) * (D * KB) + kc * KLB);
       }
     };
     auto vaddr = [&](int t) -> const char* {
       if constexpr (PAGED) {
         const int R = TV0 + t * VRPL;
         const int row = min(max(R + vr, a0), last);
-        return tile_base(a.v, R, D * VB) + static_cast<uint32_t>((row - R) * (D * VB) + vc * 16);
+        return tile_base(a.v, R, D * VB) + static_cast<uint32_t>((row - R) * (D * VB) + vc * VLB);
       } else {
-        return vblk + static_cast<uint32_t>(min(t * VRPL + vr, nrows - 1) * (D * VB) + vc * 16);
+        return vblk + static_cast<uint32_t>(min(t * VRPL + vr, nrows - 1) * (D * VB) + vc * VLB);
       }
     };
 
-    // vq8: the chunk's per-token scales are requested now and used by the
-    // weights pass; LDS row x = lane + 64 i sits in register i.
-    float sreg[kScaleRegs];
+    // Per-token scale of LDS row x = lane + 64 i (clamped into the chunk).
+    auto load_scale = [&](const float* pool, const float* contiguous, int i) -> float {
+      if constexpr (PAGED) {
+        const int row = min(max(A + lane + 64 * i, a0), last);
+        const int pid = __shfl(idreg, (row >> a.log2_bs) - j0);
+        return pool[(static_cast<int64_t>(pid) * a.Hkv + kvh) * a.block_size + (row & (a.block_size - 1))];
+      } else {
+        return contiguous[a0 + min(lane + 64 * i, nrows - 1)];
+      }
+    };
+    // int8 caches: the chunk's per-token scales are requested now; key scales
+    // are used where the chunk max is taken, value scales by the weights
+    // pass.  LDS row x = lane + 64 i sits in register i.
+    float sreg[kScaleRegs], ksreg[kKScaleRegs];
     if constexpr (VT == kI8) {
 #pragma unroll
-      for (int i = 0; i < kScaleRegs; ++i) {
-        if constexpr (PAGED) {
-          const int row = min(max(A + lane + 64 * i, a0), last);
-          const int pid = __shfl(idreg, (row >> a.log2_bs) - j0);
-          sreg[i] = a.v_scale[(static_cast<int64_t>(pid) * a.Hkv + kvh) * a.block_size +
-                              (row & (a.block_size - 1))];
-        } else {
-          sreg[i] = sbase[a0 + min(lane + 64 * i, nrows - 1)];
-        }
-      }
+      for (int i = 0; i < kScaleRegs; ++i) sreg[i] = load_scale(a.v_scale, sbase, i);
+    }
+    if constexpr (KT == kI8) {
+#pragma unroll
+      for (int i = 0; i < kKScaleRegs; ++i) ksreg[i] = load_scale(a.k_scale, ksbase, i);
     }
 
     // ---- pass 1: raw scores of the chunk's rows (rolling prefetch) ----------
@@ -312,7 +356,7 @@ decode_partial_kernel(AttnArgs a) {
     // tile has been widened.  The steady-state loop has no branches (every
     // tile and every reload is in range) so the compiler can count loads in
     // flight exactly; the last one or two batches run in a guarded tail.
-    u32x4 kd[UK];
+    vec_t<KLB> kd[UK];
     auto k_scores = [&](const float (&kf)[KE], int r) {
       float s[G];
 #pragma unroll
@@ -329,7 +373,7 @@ decode_partial_kernel(AttnArgs a) {
       }
     };
 #pragma unroll
-    for (int u = 0; u < UK; ++u) kd[u] = load16(kaddr(min(u, nk - 1)));
+    for (int u = 0; u < UK; ++u) kd[u] = load_nt<KLB>(kaddr(min(u, nk - 1)));
     const int kx0 = TK0 - A + kr;  // LDS row of tile 0 for this lane
     int t0 = 0;
     for (; t0 + 2 * UK <= nk; t0 += UK) {
@@ -337,7 +381,7 @@ decode_partial_kernel(AttnArgs a) {
       for (int u = 0; u < UK; ++u) {
         float kf[KE];
         widen<KT, KE>(kd[u], kf);
-        kd[u] = load16(kaddr(t0 + UK + u));
+        kd[u] = load_nt<KLB>(kaddr(t0 + UK + u));
         k_scores(kf, kx0 + (t0 + u) * KRPL);
       }
     }
@@ -347,15 +391,15 @@ decode_partial_kernel(AttnArgs a) {
         if (t0 + u < nk) {
           float kf[KE];
           widen<KT, KE>(kd[u], kf);
-          if (t0 + UK + u < nk) kd[u] = load16(kaddr(t0 + UK + u));
+          if (t0 + UK + u < nk) kd[u] = load_nt<KLB>(kaddr(t0 + UK + u));
           k_scores(kf, kx0 + (t0 + u) * KRPL);
         }
       }
     }
     // First value tiles are in flight while the weights are computed.
-    u32x4 vd[UV];
+    vec_t<VLB> vd[UV];
 #pragma unroll
-    for (int u = 0; u < UV; ++u) vd[u] = load16(vaddr(min(u, nv - 1)));
+    for (int u = 0; u < UV; ++u) vd[u] = load_nt<VLB>(vaddr(min(u, nv - 1)));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -365,9 +409,27 @@ decode_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) mloc[g] = -INFINITY;
     const int xlo = a0 - A, xhi = a0 - A + nrows;  // LDS rows of the chunk's keys
-    for (int r = xlo + lane; r < xhi; r += 64) {
+    if constexpr (KT == kI8) {
+      // Finish the raw scores in place, (dot - 128 sum q) * key scale; each
+      // lane rewrites exactly the rows it reads again in the weights pass.
 #pragma unroll
-      for (int g = 0; g < G; ++g) mloc[g] = fmaxf(mloc[g], sc[r * G + g]);
+      for (int i = 0; i < kKScaleRegs; ++i) {
+        const int r = lane + 64 * i;
+        if (64 * i >= xhi) break;  // wave-uniform
+        if (r >= xlo && r < xhi) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float sv = (sc[r * G + g] - c128[g]) * ksreg[i];
+            sc[r * G + g] = sv;
+            mloc[g] = fmaxf(mloc[g], sv);
+          }
+        }
+      }
+    } else {
+      for (int r = xlo + lane; r < xhi; r += 64) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) mloc[g] = fmaxf(mloc[g], sc[r * G + g]);
+      }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -423,7 +485,7 @@ decode_partial_kernel(AttnArgs a) {
       for (int u = 0; u < UV; ++u) {
         float vf[VE];
         widen<VT, VE>(vd[u], vf);
-        vd[u] = load16(vaddr(t0 + UV + u));
+        vd[u] = load_nt<VLB>(vaddr(t0 + UV + u));
         v_accum(vf, vx0 + (t0 + u) * VRPL);
       }
     }
@@ -433,7 +495,7 @@ decode_partial_kernel(AttnArgs a) {
         if (t0 + u < nv) {
           float vf[VE];
           widen<VT, VE>(vd[u], vf);
-          if (t0 + UV + u < nv) vd[u] = load16(vaddr(t0 + UV + u));
+          if (t0 + UV + u < nv) vd[u] = load_nt<VLB>(vaddr(t0 + UV + u));
           v_accum(vf, vx0 + (t0 + u) * VRPL);
         }
       }
@@ -496,6 +558,7 @@ hipError_t by_dtype(int kt, int vt, const AttnArgs& a, hipStream_t s) {
   if (kt == kBF16 && vt == kF32) return launch_one<D, G, kBF16, kF32, PAGED>(a, s);
   if (kt == kBF16 && vt == kBF16) return launch_one<D, G, kBF16, kBF16, PAGED>(a, s);
   if (kt == kBF16 && vt == kI8) return launch_one<D, G, kBF16, kI8, PAGED>(a, s);
+  if (kt == kI8 && vt == kI8) return launch_one<D, G, kI8, kI8, PAGED>(a, s);
   return hipErrorInvalidValue;
 }
 

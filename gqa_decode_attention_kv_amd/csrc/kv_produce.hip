@@ -4,14 +4,17 @@
 // Sources: "Universal AI Inference - Hugging Face decoder completeness"
 // (P0.2 RoPE scaling, P1.1 RMSNorm gain (1+w), P1.2 QK-norm before RoPE,
 // P1.3 absolute positions); "llamay - Models and formats" (Architectures:
-// interleaved vs NeoX rotary; The KV cache, in three precisions: vq8);
+// interleaved vs NeoX rotary, gpt-oss YaRN; The KV cache, in three
+// precisions: vq8 and q8); "Algenta - Model support matrix" (Decoder
+// families: linear scaling);
 // "FreeToken PR #722" (Changes: Llama-3 scaling constants).
 //
 // The work is O(B * (H + Hkv) * d): one 64-lane wave per head vector.  The
 // norm and the rotation run in double precision and round once to the
 // stored format, so the stored key matches a double-precision definition
-// to the last bit in all but astronomically rare ties.  The vq8 quantiser is
-// defined in f32 (IEEE division, rounding half away from zero).
+// to the last bit in all but astronomically rare ties.  The int8 quantiser
+// (vq8 values, q8 keys and values) is defined in f32 (IEEE division,
+// rounding half away from zero).
 #include "launch.h"
 
 #include <math.h>
@@ -53,15 +56,47 @@ __device__ inline uint16_t bf16_from_double(double x) {
   return static_cast<uint16_t>(sign | static_cast<uint32_t>(r));
 }
 
-// Rotary frequency of pair i (full head), plain or Llama-3 scaled.
+// Rotary frequency of pair i (full head): plain, Llama-3, linear or YaRN.
+// YaRN's blend band [c_lo, c_hi] in pair indices comes from the host.
 __device__ inline double rope_freq(const ProduceArgs& a, int i) {
   const double f = pow(a.theta, -2.0 * static_cast<double>(i) / static_cast<double>(a.D));
+  if (a.scaling == kLinear) return f / a.factor;
+  if (a.scaling == kYarn) {
+    const double t = fmin(fmax((static_cast<double>(i) - a.c_lo) / (a.c_hi - a.c_lo), 0.0), 1.0);
+    return t * f / a.factor + (1.0 - t) * f;
+  }
   if (a.scaling != kLlama3) return f;
   const double wavelen = kTwoPi / f;
   if (wavelen < a.orig / a.high) return f;
   if (wavelen > a.orig / a.low) return f / a.factor;
   const double mu = (a.orig / wavelen - a.low) / (a.high - a.low);
   return (1.0 - mu) * f / a.factor + mu * f;
+}
+
+// Symmetric int8 quantiser of one row held across the wave, E values per
+// lane at element indices idx[e] (valid[e] false for padding): scale =
+// max|x| / 127 in f32, code = clamp(round_half_away(x / scale), -127, 127);
+// an all-zero row gives scale 0 and codes 0.  Used for vq8 values and q8 keys.
+template <int E>
+__device__ inline void quantize_row(const float (&x)[E], const int (&idx)[E], const bool (&valid)[E],
+                                    int8_t* dst, float* scale_out, int lane) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (valid[e]) amax = fmaxf(amax, fabsf(x[e]));
+  amax = wave_max(amax);
+  const float scale = amax == 0.0f ? 0.0f : __fdiv_rn(amax, 127.0f);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (!valid[e]) continue;
+    float r = 0.0f;
+    if (amax != 0.0f) {
+      r = roundf(__fdiv_rn(x[e], scale));
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+    }
+    dst[idx[e]] = static_cast<int8_t>(static_cast<int>(r));
+  }
+  if (lane == 0) *scale_out = scale;
 }
 
 template <int D>
@@ -129,16 +164,30 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
       slot = ((static_cast<int64_t>(b) * a.Hkv + u) * a.cap + pos) * D;
     }
   }
+  // q8 keys: the rotated key rounded to f32, quantised after the loop.
+  float kq[2 * NP];
+  int kidx[2 * NP];
+  bool kok[2 * NP];
+#pragma unroll
+  for (int e = 0; e < 2 * NP; ++e) {
+    kq[e] = 0.0f;
+    kidx[e] = 0;
+    kok[e] = false;
+  }
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const int i = lane + 64 * j;
-    if (i >= D / 2) break;
+    if (i >= D / 2) continue;
     const int ia = (a.pairing == kNeox) ? i : 2 * i;
     const int ib = (a.pairing == kNeox) ? i + D / 2 : 2 * i + 1;
     const double c = cs[j], sv = sn[j];
     const double xa = sx[ia], xb = sx[ib];
-    const double ya = xa * c - xb * sv;
-    const double yb = xa * sv + xb * c;
+    double ya = xa * c - xb * sv;
+    double yb = xa * sv + xb * c;
+    if (a.attn_factor != 1.0) {  // YaRN scales the rotated q and k
+      ya *= a.attn_factor;
+      yb *= a.attn_factor;
+    }
     if (is_q) {
       float* q = a.q_out + (static_cast<int64_t>(b) * a.H + x) * D;
       q[ia] = static_cast<float>(ya);
@@ -147,13 +196,21 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
       float* k = static_cast<float*>(a.k) + slot;
       k[ia] = static_cast<float>(ya);
       k[ib] = static_cast<float>(yb);
-    } else {
+    } else if (a.k_dtype == kBF16) {
       uint16_t* k = static_cast<uint16_t*>(a.k) + slot;
       k[ia] = bf16_from_double(ya);
       k[ib] = bf16_from_double(yb);
+    } else {
+      kq[2 * j] = static_cast<float>(ya);
+      kq[2 * j + 1] = static_cast<float>(yb);
+      kidx[2 * j] = ia;
+      kidx[2 * j + 1] = ib;
+      kok[2 * j] = kok[2 * j + 1] = true;
     }
   }
   if (is_q) return;
+  if (a.k_dtype == kI8)
+    quantize_row<2 * NP>(kq, kidx, kok, static_cast<int8_t*>(a.k) + slot, a.k_scale + slot / D, lane);
 
   // Value of (b, u): stored as given (f32), rounded to bf16, or quantised.
   if (a.v_dtype == kF32) {
@@ -165,25 +222,14 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) dst[lane + 64 * e] = bf16_from_double(static_cast<double>(v[e]));
   } else {
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    amax = wave_max(amax);
-    int8_t* dst = static_cast<int8_t*>(a.v) + slot;
-    if (amax == 0.0f) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) dst[lane + 64 * e] = 0;
-      if (lane == 0) a.v_scale[slot / D] = 0.0f;
-      return;
-    }
-    const float scale = __fdiv_rn(amax, 127.0f);
+    int idx[EPL];
+    bool ok[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      float r = roundf(__fdiv_rn(v[e], scale));
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      dst[lane + 64 * e] = static_cast<int8_t>(static_cast<int>(r));
+      idx[e] = lane + 64 * e;
+      ok[e] = true;
     }
-    if (lane == 0) a.v_scale[slot / D] = scale;
+    quantize_row<EPL>(v, idx, ok, static_cast<int8_t*>(a.v) + slot, a.v_scale + slot / D, lane);
   }
 }
 

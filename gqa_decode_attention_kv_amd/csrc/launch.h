@@ -12,7 +12,7 @@ constexpr int kMaxBatch = 32;
 
 enum : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
 enum : int { kNeox = 0, kInterleaved = 1 };
-enum : int { kPlain = 0, kLlama3 = 1 };
+enum : int { kPlain = 0, kLlama3 = 1, kLinear = 2, kYarn = 3 };
 
 // Per-sequence schedule of one decode step.  Work item w of the partial
 // kernel belongs to sequence b with work_prefix[b] <= w < work_prefix[b + 1];
@@ -30,6 +30,9 @@ struct ProduceArgs {
   int32_t B, H, Hkv, D;
   int32_t pairing, scaling;
   double theta, factor, low, high, orig;
+  // YaRN: blend band over pair indices [c_lo, c_hi] and the factor that
+  // multiplies the rotated q and k (1 for the other schemes).
+  double c_lo, c_hi, attn_factor;
   int32_t norm_enabled, norm_offset;
   float norm_eps;
   const float* w_q;
@@ -40,7 +43,8 @@ struct ProduceArgs {
   int32_t k_dtype, v_dtype, cap;
   void* k;
   void* v;
-  float* v_scale;
+  float* k_scale;  // q8 keys
+  float* v_scale;  // vq8 / q8 values
   float* q_out;
   // Paged cache (block_table != nullptr): slot p of (b, u) is row p % bs of
   // physical block block_table[b][p / bs], pools [num_blocks][Hkv][bs][D].
@@ -53,6 +57,7 @@ struct AttnArgs {
   int32_t H, Hkv, cap, split_size, max_splits;
   const void* k;
   const void* v;
+  const float* k_scale;
   const float* v_scale;
   const float* q;
   float* part_o;
@@ -69,6 +74,7 @@ struct CombineArgs {
   int32_t H, max_splits;
   const float* part_o;
   const float* part_lse;
+  const float* sinks;  // [H] attention-sink logits, or nullptr
   float* out;
   SeqTable t;
 };

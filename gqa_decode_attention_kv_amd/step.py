@@ -45,9 +45,12 @@ class DeviceStep:
         src_k = paged.pool_k if paged else inputs.cache_k
         src_v = paged.pool_v if paged else inputs.cache_v
         src_s = paged.pool_scale if paged else inputs.v_scale
+        src_ks = paged.pool_k_scale if paged else inputs.k_scale
         self.cache_k = _dev(src_k, device)
         self.cache_v = _dev(src_v, device)
         self.v_scale = _dev(src_s, device) if src_s is not None else None
+        self.k_scale = _dev(src_ks, device) if src_ks is not None else None
+        self.sinks = _dev(inputs.sinks, device) if inputs.sinks is not None else None
         self.block_table = _dev(paged.block_table, device) if paged else None
         self.w_q = _dev(inputs.w_q, device) if inputs.w_q is not None else None
         self.w_k = _dev(inputs.w_k, device) if inputs.w_k is not None else None
@@ -58,18 +61,20 @@ class DeviceStep:
 
         self.shape = B.Shape(Bn, H, Hkv, d)
         r = w.rope
-        self.rope = B.Rope(r.pairing, r.scaling, r.theta, r.factor, r.low, r.high, r.orig)
+        self.rope = B.Rope(r.pairing, r.scaling, r.theta, r.factor, r.low, r.high, r.orig,
+                           int(r.truncate), r.attn_factor)
         n = w.qk_norm
         self.qk_norm = (B.QKNorm(1, n.eps, n.offset, self.w_q.data_ptr(), self.w_k.data_ptr())
                         if n.enabled else None)
         vs_ptr = self.v_scale.data_ptr() if self.v_scale is not None else None
+        ks_ptr = self.k_scale.data_ptr() if self.k_scale is not None else None
         if paged:
             self.cache = B.KVCache(w.k_dtype, w.v_dtype, paged.capacity, self.cache_k.data_ptr(),
                                    self.cache_v.data_ptr(), vs_ptr, self.block_table.data_ptr(),
-                                   paged.block_size, paged.max_blocks, paged.num_blocks)
+                                   paged.block_size, paged.max_blocks, paged.num_blocks, ks_ptr)
         else:
             self.cache = B.KVCache(w.k_dtype, w.v_dtype, w.capacity, self.cache_k.data_ptr(),
-                                   self.cache_v.data_ptr(), vs_ptr, None, 0, 0, 0)
+                                   self.cache_v.data_ptr(), vs_ptr, None, 0, 0, 0, ks_ptr)
         self.scale = 1.0 / math.sqrt(d)
 
     @staticmethod
@@ -87,9 +92,15 @@ class DeviceStep:
                       self.part_o.data_ptr(), self.part_lse.data_ptr(), self.stream())
 
     def combine(self):
-        B.decode_combine(self.shape, self.seq_lens, self.w.window, self.split_size,
-                         self.max_splits, self.part_o.data_ptr(), self.part_lse.data_ptr(),
-                         self.out.data_ptr(), self.stream())
+        if self.sinks is not None:
+            B.decode_combine_sink(self.shape, self.seq_lens, self.w.window, self.split_size,
+                                  self.max_splits, self.part_o.data_ptr(),
+                                  self.part_lse.data_ptr(), self.sinks.data_ptr(),
+                                  self.out.data_ptr(), self.stream())
+        else:
+            B.decode_combine(self.shape, self.seq_lens, self.w.window, self.split_size,
+                             self.max_splits, self.part_o.data_ptr(), self.part_lse.data_ptr(),
+                             self.out.data_ptr(), self.stream())
 
     def step(self):
         self.produce()
@@ -125,4 +136,5 @@ class DeviceStep:
         if self.w.v_dtype == BF16:
             v = v.view(np.uint16)
         s = self.v_scale[bi, :, idx].cpu().numpy() if self.v_scale is not None else None
-        return dict(k=k, v=v, scale=s)
+        ks = self.k_scale[bi, :, idx].cpu().numpy() if self.k_scale is not None else None
+        return dict(k=k, v=v, scale=s, k_scale=ks)

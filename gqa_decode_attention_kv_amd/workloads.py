@@ -13,9 +13,10 @@ standard normal float32 unless stated):
   * cached keys and values: one block per (b, kv head), streams 5 (K) and
     6 (V), filling only the visible cached rows [lo_b, L_b - 1).  bf16
     entries keep the top 16 bits of the float32 draw (a random bf16 number);
-    f32 entries are the draw itself.  vq8 value rows are drawn directly as
-    int8 codes (rounded N(0,1) * 127 / 2.8, clipped to +-127) and an f32
-    scale near 2.8 / 127 (stream 7);
+    f32 entries are the draw itself.  int8 rows are drawn directly as codes
+    (rounded N(0,1) * 127 / 2.8, clipped to +-127) with an f32 scale near
+    2.8 / 127: values from stream 7, q8 keys from stream 9;
+  * attention sinks (one logit per query head): 2 + 3 * N(0, 1), stream 10;
   * every other cache row (before the window, the new token's slot and
     beyond) holds a NaN poison (int8 codes 0 with a NaN scale), so a kernel
     that reads outside the visible range cannot pass a test.
@@ -39,7 +40,7 @@ import numpy as np
 
 F32, BF16, I8 = 0, 1, 2
 NEOX, INTERLEAVED = 0, 1
-PLAIN, LLAMA3 = 0, 1
+PLAIN, LLAMA3, LINEAR, YARN = 0, 1, 2, 3
 
 BF16_NAN = np.uint16(0x7FC0)
 STORAGE = {F32: np.float32, BF16: np.uint16, I8: np.int8}
@@ -55,10 +56,13 @@ class Rope:
     low: float = 1.0
     high: float = 4.0
     orig: int = 8192
+    truncate: bool = True      # YaRN: round the blend edges to whole pair indices
+    attn_factor: float = 0.0   # YaRN: 0 = 1 + 0.1 ln(factor)
 
     def as_dict(self) -> dict:
         return dict(pairing=self.pairing, scaling=self.scaling, theta=self.theta,
-                    factor=self.factor, low=self.low, high=self.high, orig=self.orig)
+                    factor=self.factor, low=self.low, high=self.high, orig=self.orig,
+                    truncate=self.truncate, attn_factor=self.attn_factor)
 
 
 @dataclass(frozen=True)
@@ -87,6 +91,7 @@ class Workload:
     softcap: float = 0.0
     split_size: int = 512
     seed: tuple = (0,)
+    sink: bool = False         # a per-head attention sink in the combine
 
     @property
     def group(self) -> int:
@@ -108,10 +113,10 @@ class Workload:
         return int(-(-int(self.seq_lens().max()) // self.split_size))
 
     def kv_row_bytes(self) -> int:
-        """Algorithmic bytes per visible (token, kv head): K row + V row (+ vq8 scale)."""
+        """Algorithmic bytes per visible (token, kv head): K row + V row (+ int8 scales)."""
         d = self.head_dim
         b = d * ELEM_BYTES[self.k_dtype] + d * ELEM_BYTES[self.v_dtype]
-        return b + (4 if self.v_dtype == I8 else 0)
+        return b + (4 if self.v_dtype == I8 else 0) + (4 if self.k_dtype == I8 else 0)
 
     def kv_bytes(self) -> int:
         """Algorithmic KV bytes one decode step reads (visible rows only)."""
@@ -150,6 +155,32 @@ WORKLOADS = {
                                       8192, BF16, BF16,
                                       Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
                                       split_size=1024, seed=(6,)),
+    # The headline shape with the q8 cache (int8 keys and values, one f32
+    # scale each per token per kv head).
+    "llama3.1-8b-q8": Workload("llama3.1-8b-q8", 32, 32, 8, 128, ("fixed", 8192), 8192, I8, I8,
+                               Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
+                               split_size=1024, seed=(7,)),
+    # gpt-oss-20b attention: 64/8 heads of 64, YaRN (theta 150000, factor 32,
+    # beta 1..32 over 4096, edges not rounded), a per-head sink, and the exact
+    # f32 cache (its sampler moves too far under vq8); full-attention layers
+    # and 128-key sliding-window layers alternate.
+    "gpt-oss-20b-full": Workload("gpt-oss-20b-full", 32, 64, 8, 64, ("fixed", 8192), 8192, F32, F32,
+                                 Rope(NEOX, YARN, 150000.0, 32.0, 1.0, 32.0, 4096, False),
+                                 split_size=1024, seed=(8, 0), sink=True),
+    "gpt-oss-20b-sliding": Workload("gpt-oss-20b-sliding", 32, 64, 8, 64, ("fixed", 8192), 8192,
+                                    F32, F32,
+                                    Rope(NEOX, YARN, 150000.0, 32.0, 1.0, 32.0, 4096, False),
+                                    window=128, split_size=64, seed=(8, 1), sink=True),
+    # Gemma-3-27B attention: 32/16 heads of 128, QK-norm with gain (1 + w),
+    # global layers with theta 1e6 and linear scaling 8, local layers with
+    # theta 1e4 and a 1024-key window.
+    "gemma3-27b-global": Workload("gemma3-27b-global", 8, 32, 16, 128, ("fixed", 32768), 32768,
+                                  BF16, BF16, Rope(NEOX, LINEAR, 1000000.0, 8.0),
+                                  QKNorm(True, 1e-6, 1, 0.0, 0.1), split_size=1024, seed=(9, 0)),
+    "gemma3-27b-local": Workload("gemma3-27b-local", 8, 32, 16, 128, ("fixed", 32768), 32768,
+                                 BF16, BF16, Rope(NEOX, PLAIN, 10000.0),
+                                 QKNorm(True, 1e-6, 1, 0.0, 0.1), window=1024, split_size=128,
+                                 seed=(9, 1)),
 }
 
 HEADLINE = "llama3.1-8b-b32-ctx8k"
@@ -172,7 +203,9 @@ class Inputs:
     w_k: np.ndarray | None
     cache_k: np.ndarray       # [B][Hkv][cap][d] f32 or uint16 (bf16 bits)
     cache_v: np.ndarray       # [B][Hkv][cap][d] f32, uint16 or int8
-    v_scale: np.ndarray | None  # [B][Hkv][cap] f32 (vq8 only)
+    v_scale: np.ndarray | None  # [B][Hkv][cap] f32 (int8 values only)
+    k_scale: np.ndarray | None = None  # [B][Hkv][cap] f32 (int8 keys only)
+    sinks: np.ndarray | None = None    # [H] f32 attention-sink logits
 
 
 def _workers() -> int:
@@ -207,6 +240,8 @@ def make_inputs(w: Workload, seq_lens=None) -> Inputs:
     cache_k = np.empty((B, Hkv, cap, d), dtype=STORAGE[w.k_dtype])
     cache_v = np.empty((B, Hkv, cap, d), dtype=STORAGE[w.v_dtype])
     v_scale = np.empty((B, Hkv, cap), dtype=np.float32) if w.v_dtype == I8 else None
+    k_scale = np.empty((B, Hkv, cap), dtype=np.float32) if w.k_dtype == I8 else None
+    sinks = (2.0 + 3.0 * _normal([*s, 10], (H,))).astype(np.float32) if w.sink else None
 
     def fill(bu):
         b, u = bu
@@ -224,33 +259,40 @@ def make_inputs(w: Workload, seq_lens=None) -> Inputs:
             else:
                 slab[:lo] = 0
                 slab[lo + n:] = 0
+        def int8_rows(stream, codes, scale):
+            rng = np.random.default_rng([*s, stream, b, u])
+            z = rng.standard_normal((n, d), dtype=np.float32)
+            codes[b, u, lo:lo + n] = np.clip(np.rint(z * (127.0 / 2.8)), -127, 127)
+            scale[b, u, lo:lo + n] = (2.8 / 127.0) * (
+                1.0 + 0.05 * rng.standard_normal(n, dtype=np.float32))
+
         if n > 0:
-            zk = _normal([*s, 5, b, u], (n, d))
-            if w.k_dtype == F32:
-                cache_k[b, u, lo:lo + n] = zk
+            if w.k_dtype == I8:
+                int8_rows(9, cache_k, k_scale)
             else:
-                cache_k[b, u, lo:lo + n] = zk.view(np.uint16)[:, 1::2]
+                zk = _normal([*s, 5, b, u], (n, d))
+                if w.k_dtype == F32:
+                    cache_k[b, u, lo:lo + n] = zk
+                else:
+                    cache_k[b, u, lo:lo + n] = zk.view(np.uint16)[:, 1::2]
             if w.v_dtype == I8:
-                rng = np.random.default_rng([*s, 7, b, u])
-                z = rng.standard_normal((n, d), dtype=np.float32)
-                cache_v[b, u, lo:lo + n] = np.clip(np.rint(z * (127.0 / 2.8)), -127, 127)
-                v_scale[b, u, lo:lo + n] = (2.8 / 127.0) * (
-                    1.0 + 0.05 * rng.standard_normal(n, dtype=np.float32))
+                int8_rows(7, cache_v, v_scale)
             else:
                 zv = _normal([*s, 6, b, u], (n, d))
                 if w.v_dtype == F32:
                     cache_v[b, u, lo:lo + n] = zv
                 else:
                     cache_v[b, u, lo:lo + n] = zv.view(np.uint16)[:, 1::2]
-        if v_scale is not None:
-            v_scale[b, u, :lo] = np.nan
-            v_scale[b, u, lo + n:] = np.nan
+        for sc in (v_scale, k_scale):
+            if sc is not None:
+                sc[b, u, :lo] = np.nan
+                sc[b, u, lo + n:] = np.nan
 
     jobs = [(b, u) for b in range(B) for u in range(Hkv)]
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(fill, jobs))
     return Inputs(w, lens, (lens - 1).astype(np.int32), q_in, k_in, v_in, w_q, w_k,
-                  cache_k, cache_v, v_scale)
+                  cache_k, cache_v, v_scale, k_scale, sinks)
 
 
 @dataclass
@@ -261,7 +303,8 @@ class PagedInputs:
     block_table: np.ndarray     # [B][max_blocks] int32
     pool_k: np.ndarray          # [num_blocks][Hkv][block_size][d]
     pool_v: np.ndarray
-    pool_scale: np.ndarray | None  # [num_blocks][Hkv][block_size] (vq8)
+    pool_scale: np.ndarray | None  # [num_blocks][Hkv][block_size] (int8 values)
+    pool_k_scale: np.ndarray | None = None  # same, int8 keys
 
     @property
     def capacity(self) -> int:
@@ -297,13 +340,6 @@ def make_paged(inputs: Inputs, block_size: int, spare_blocks: int = 3) -> PagedI
 
     pk = scatter(inputs.cache_k, (d,))
     pv = scatter(inputs.cache_v, (d,))
-    ps = None
-    if inputs.v_scale is not None:
-        vs = inputs.v_scale
-        pad = mb * bs - cap
-        if pad:
-            vs = np.concatenate([vs, np.full((B, Hkv, pad), np.nan, np.float32)], axis=2)
-        blocks = np.moveaxis(vs.reshape(B, Hkv, mb, bs), 2, 1).reshape(B * mb, Hkv, bs)
-        ps = np.full((nblk, Hkv, bs), np.nan, np.float32)
-        ps[table.reshape(-1)] = blocks
-    return PagedInputs(bs, mb, nblk, table, pk, pv, ps)
+    ps = scatter(inputs.v_scale, ()) if inputs.v_scale is not None else None
+    pks = scatter(inputs.k_scale, ()) if inputs.k_scale is not None else None
+    return PagedInputs(bs, mb, nblk, table, pk, pv, ps, pks)

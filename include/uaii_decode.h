@@ -9,6 +9,8 @@
  *                        sequences, with an optional sliding window and
  *                        attention-logit softcap
  *   uaii_decode_combine  log-sum-exp combine of the partials
+ *   uaii_decode_combine_sink  the same combine with a per-head attention
+ *                        sink in the softmax denominator
  *
  * Sources (page title, then section):
  *   [UAII]      "Universal AI Inference - Hugging Face decoder completeness"
@@ -29,8 +31,9 @@
  *   k_in, v_in               [batch][n_kv_heads][head_dim]         f32
  *   cache K, V               [batch][n_kv_heads][capacity][head_dim] (contiguous;
  *                            the paged layout is described at uaii_kv_cache)
- *                            K: f32 or bf16; V: f32, bf16 or int8 (vq8)
- *   v_scale (vq8 only)       [batch][n_kv_heads][capacity]         f32
+ *                            K: f32, bf16 or int8 (q8); V: f32, bf16 or
+ *                            int8 (vq8, q8)
+ *   k_scale (q8), v_scale (vq8, q8)  [batch][n_kv_heads][capacity]  f32
  *   part_o                   [batch][n_heads][max_splits][head_dim] f32
  *   part_lse                 [batch][n_heads][max_splits]          f32
  *   out                      [batch][n_heads][head_dim]            f32
@@ -58,7 +61,9 @@
  *   Kernel path capabilities: batched decode partial, B <= 32);
  *   n_heads / n_kv_heads in {1, 2, 4, 8}; K dtype f32 or bf16; V dtype f32,
  *   bf16 or int8 with an f32 scale per token per kv head (vq8: values
- *   quantised, keys exact; [LLAMAY] The KV cache, in three precisions).
+ *   quantised, keys exact; [LLAMAY] The KV cache, in three precisions);
+ *   int8 keys only together with int8 values (q8: both quantised, each
+ *   with its own scale per token per kv head; same section).
  * Threads.  Re-entrant; calls on different streams may overlap.  Calls that
  *   write the same cache slot or partial rows concurrently race.
  */
@@ -85,10 +90,12 @@ enum { UAII_F32 = 0, UAII_BF16 = 1, UAII_I8 = 2 };
  * ([UAII] P0.2; [LLAMAY] Architectures; [FREETOKEN] Changes). */
 enum { UAII_ROPE_NEOX = 0, UAII_ROPE_INTERLEAVED = 1 };
 
-/* RoPE frequency scheme: plain theta^(-2i/d), or Llama-3 frequency scaling
+/* RoPE frequency scheme: plain theta^(-2i/d), Llama-3 frequency scaling
  * ([UAII] P0.2: match Hugging Face's Llama-3 rotary embedding;
- * [ALGENTA] Structural fact requirements: plain or llama3). */
-enum { UAII_ROPE_PLAIN = 0, UAII_ROPE_LLAMA3 = 1 };
+ * [ALGENTA] Structural fact requirements: plain or llama3), linear scaling
+ * ([ALGENTA] Decoder families: gemma3 linear global scaling) or YaRN
+ * ([UAII] P0.2 names it; [LLAMAY] Architectures: gpt-oss). */
+enum { UAII_ROPE_PLAIN = 0, UAII_ROPE_LLAMA3 = 1, UAII_ROPE_LINEAR = 2, UAII_ROPE_YARN = 3 };
 
 typedef struct uaii_attn_shape {
     int32_t batch;      /* B, 1..32 */
@@ -106,15 +113,27 @@ typedef struct uaii_attn_shape {
  *   lambda < original/high  -> f;    lambda > original/low -> f / factor;
  *   otherwise mu = (original/lambda - low)/(high - low) and
  *   (1 - mu) f / factor + mu f   ([FREETOKEN] Changes: low 1, high 4,
- *   original 8192 for every Llama 3.1-3.3 release). */
+ *   original 8192 for every Llama 3.1-3.3 release).
+ * Linear scaling: f / factor for every pair (positions divided by factor).
+ * YaRN, as Hugging Face computes it: low_freq_factor is beta_slow and
+ *   high_freq_factor is beta_fast, the numbers of turns over the original
+ *   context that bound the blend.  With c(n) = d ln(original / (2 pi n)) /
+ *   (2 ln theta), the pair index that turns n times, the blend runs from
+ *   c_lo = c(beta_fast) to c_hi = c(beta_slow) (rounded outwards to whole
+ *   indices if truncate != 0, clamped to [0, d - 1]):
+ *   t_i = clamp((i - c_lo)/(c_hi - c_lo), 0, 1), g_i = t_i f / factor +
+ *   (1 - t_i) f.  The rotated q and k are multiplied by attention_factor
+ *   (0 selects 1 + 0.1 ln(factor) for factor > 1, else 1). */
 typedef struct uaii_rope {
     int32_t pairing;               /* UAII_ROPE_NEOX | UAII_ROPE_INTERLEAVED */
-    int32_t scaling;               /* UAII_ROPE_PLAIN | UAII_ROPE_LLAMA3 */
+    int32_t scaling;               /* UAII_ROPE_PLAIN | _LLAMA3 | _LINEAR | _YARN */
     double theta;                  /* > 0 */
-    double factor;                 /* llama3: >= 1 */
-    double low_freq_factor;        /* llama3: > 0 */
-    double high_freq_factor;       /* llama3: > low_freq_factor */
-    int32_t original_max_position; /* llama3: > 0 */
+    double factor;                 /* llama3, yarn: >= 1; linear: > 0 */
+    double low_freq_factor;        /* llama3: > 0; yarn: beta_slow > 0 */
+    double high_freq_factor;       /* llama3: > low_freq_factor; yarn: beta_fast > beta_slow */
+    int32_t original_max_position; /* llama3, yarn: > 0 */
+    int32_t truncate;              /* yarn: round the blend edges to whole pair indices */
+    double attention_factor;       /* yarn: > 0, or 0 for the default */
 } uaii_rope;
 
 /* Per-head QK-RMSNorm, applied to every q and k head before RoPE
@@ -134,14 +153,15 @@ typedef struct uaii_qk_norm {
  *
  * Contiguous (block_table == NULL): one slab per (sequence, kv head),
  *   k, v     device [B][Hkv][capacity][d]
- *   v_scale  device [B][Hkv][capacity]          (vq8 only)
+ *   v_scale  device [B][Hkv][capacity]          (int8 values only)
+ *   k_scale  device [B][Hkv][capacity]          (int8 keys only)
  *
  * Paged (block_table != NULL): pools of fixed-size blocks shared by all
  * sequences, and a table that maps each sequence's logical blocks to
  * physical ones.  Slot p of (sequence b, kv head u) is row p % block_size of
  * physical block block_table[b][p / block_size]:
  *   k, v         device [num_blocks][Hkv][block_size][d]
- *   v_scale      device [num_blocks][Hkv][block_size]   (vq8 only)
+ *   v_scale, k_scale  device [num_blocks][Hkv][block_size]  (int8 only)
  *   block_table  device [B][max_blocks] int32
  *   capacity     must equal max_blocks * block_size (logical slots per
  *                sequence)
@@ -154,8 +174,8 @@ typedef struct uaii_qk_norm {
  * (Paged KV pages: "llamay - Models and formats", What is refused: a KV
  * page, the paged allocator, copy-on-write fork.) */
 typedef struct uaii_kv_cache {
-    int32_t k_dtype;   /* UAII_F32 | UAII_BF16 */
-    int32_t v_dtype;   /* UAII_F32 | UAII_BF16 | UAII_I8 (vq8) */
+    int32_t k_dtype;   /* UAII_F32 | UAII_BF16 | UAII_I8 (q8, with v_dtype int8) */
+    int32_t v_dtype;   /* UAII_F32 | UAII_BF16 | UAII_I8 (vq8, q8) */
     int32_t capacity;  /* slots per (sequence, kv head), >= 1 */
     void *k;           /* device, see the layouts above */
     void *v;           /* device */
@@ -164,6 +184,7 @@ typedef struct uaii_kv_cache {
     int32_t block_size; /* paged: rows per block, a power of two in [16, 1024] */
     int32_t max_blocks; /* paged: table entries per sequence, >= 1 */
     int32_t num_blocks; /* paged: blocks in each pool, >= 1 */
+    float *k_scale;    /* device, q8 only (else ignored); same layout as v_scale */
 } uaii_kv_cache;
 
 /* Text of the last error on the calling thread ("" if none); valid until the
@@ -173,13 +194,16 @@ const char *uaii_last_error(void);
 /* KV producer.  For every sequence b at position p = positions[b]:
  *   q' = RoPE(norm_q(q_in[b][h]), p)   -> q_out[b][h]           (f32)
  *   k' = RoPE(norm_k(k_in[b][u]), p)   -> K[b][u][p]  (f32, or bf16 rounded
- *                                                       to nearest even)
+ *        to nearest even; q8: k' rounded to f32, then quantised like v
+ *        below, scale -> k_scale[b][u][p])
  *   v  = v_in[b][u]                    -> V[b][u][p]  (f32; bf16 rounded to
  *        nearest even; vq8: scale = max|v| / 127 in f32, code =
  *        clamp(round_half_away(v / scale), -127, 127), all-zero v gives
  *        scale 0 and codes 0; scale -> v_scale[b][u][p])
- * The norm and the rotation are evaluated in double precision and rounded
- * once to the stored format.  Only slot p of each (b, u) is written.
+ * RoPE is the pairing and frequency scheme of rope; for YaRN, q' and k' are
+ * also multiplied by its attention factor.  The norm and the rotation are
+ * evaluated in double precision and rounded once to the stored format.
+ * Only slot p of each (b, u) is written.
  *   shape      host, required
  *   rope       host, required
  *   qk_norm    host, may be NULL (no norm)
@@ -203,8 +227,9 @@ uaii_status uaii_kv_produce(const uaii_attn_shape *shape, const uaii_rope *rope,
  *           scale 1/sqrt(head_dim))
  *   part_o[b][h][sigma]   = sum_j e^(s_j - m) v_j / sum_j e^(s_j - m)
  *   part_lse[b][h][sigma] = m + ln sum_j e^(s_j - m)
- * over the split's visible keys, with m their largest score; v_j is the
- * cached value widened to f32 (vq8: code * scale).  Accumulation is f32.
+ * over the split's visible keys, with m their largest score; K and v_j are
+ * the cached entries widened to f32 (int8: code * scale).  Accumulation is
+ * f32.
  * Entries of splits outside the visible range are not written.
  *   scale       must equal 1/sqrt(head_dim) (any other value is refused)
  *   seq_lens    host [batch], each in [1, capacity]
@@ -227,6 +252,21 @@ uaii_status uaii_decode_combine(const uaii_attn_shape *shape, const int32_t *seq
                                 int32_t window, int32_t split_size, int32_t max_splits,
                                 const float *part_o, const float *part_lse, float *out,
                                 void *stream);
+
+/* The combine with an attention sink: one learned logit per query head that
+ * joins the softmax denominator but carries no value ([LLAMAY]
+ * Architectures: gpt-oss puts a per-head sink in the denominator).  The sink
+ * belongs to no split, so the partials are those of uaii_decode_attn
+ * unchanged and
+ *   out[b][h] = sum_sigma e^(lse_sigma - M) part_o_sigma /
+ *               (sum_sigma e^(lse_sigma - M) + e^(sinks[h] - M)),
+ * with M the largest of the split lse values and sinks[h] (the sink is in
+ * the units of the scaled, softcapped scores).
+ *   sinks  device [n_heads] f32, finite (not checked: device memory) */
+uaii_status uaii_decode_combine_sink(const uaii_attn_shape *shape, const int32_t *seq_lens,
+                                     int32_t window, int32_t split_size, int32_t max_splits,
+                                     const float *part_o, const float *part_lse,
+                                     const float *sinks, float *out, void *stream);
 
 #ifdef __cplusplus
 }

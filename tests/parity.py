@@ -18,10 +18,10 @@ TOL_VQ8_REL = 1e-2
 
 
 def out_tolerance(w: W.Workload, ref: np.ndarray) -> tuple[float, str]:
-    """Absolute tolerance for workload w (the vq8 bound is relative to the
-    oracle output's max-abs)."""
+    """Absolute tolerance for workload w (the int8 bound, vq8 and q8, is
+    relative to the oracle output's max-abs)."""
     if w.v_dtype == W.I8:
-        return TOL_VQ8_REL * float(np.max(np.abs(ref))), "vq8 1e-2 x max|out|"
+        return TOL_VQ8_REL * float(np.max(np.abs(ref))), "int8 1e-2 x max|out|"
     if w.k_dtype == W.BF16 or w.v_dtype == W.BF16:
         return TOL_BF16, "bf16 2e-3"
     return TOL_F32, "f32 1e-5"
@@ -48,8 +48,10 @@ class OracleStep:
         self.o, self.w, self.inputs = o, w, inputs
         self.ck = inputs.cache_k.copy() if copy_cache else inputs.cache_k
         self.cv = inputs.cache_v.copy() if copy_cache else inputs.cache_v
-        vs = inputs.v_scale
+        vs, ks = inputs.v_scale, inputs.k_scale
         self.vs = (vs.copy() if copy_cache else vs) if vs is not None else None
+        self.ks = (ks.copy() if copy_cache else ks) if ks is not None else None
+        self.sinks = inputs.sinks
         norm = None
         if w.qk_norm.enabled:
             norm = dict(enabled=True, eps=w.qk_norm.eps, offset=w.qk_norm.offset,
@@ -57,7 +59,7 @@ class OracleStep:
         self.q = o.kv_produce(rope=w.rope.as_dict(), norm=norm, q_in=inputs.q_in,
                               k_in=inputs.k_in, v_in=inputs.v_in, positions=inputs.positions,
                               k_dtype=w.k_dtype, v_dtype=w.v_dtype, cache_k=self.ck,
-                              cache_v=self.cv, v_scale=self.vs)
+                              cache_v=self.cv, v_scale=self.vs, k_scale=self.ks)
 
     def slot_rows(self):
         b = np.arange(self.w.batch)
@@ -65,13 +67,14 @@ class OracleStep:
         k = self.ck[b, :, p]
         v = self.cv[b, :, p]
         s = self.vs[b, :, p] if self.vs is not None else None
-        return dict(k=k, v=v, scale=s)
+        ks = self.ks[b, :, p] if self.ks is not None else None
+        return dict(k=k, v=v, scale=s, k_scale=ks)
 
     def decode(self, pairs=None) -> np.ndarray:
         w = self.w
-        kw = dict(q=self.q, cache_k=self.ck, cache_v=self.cv, v_scale=self.vs, k_dtype=w.k_dtype,
-                  v_dtype=w.v_dtype, seq_lens=self.inputs.seq_lens, window=w.window,
-                  softcap=w.softcap)
+        kw = dict(q=self.q, cache_k=self.ck, cache_v=self.cv, v_scale=self.vs, k_scale=self.ks,
+                  k_dtype=w.k_dtype, v_dtype=w.v_dtype, seq_lens=self.inputs.seq_lens,
+                  window=w.window, softcap=w.softcap, sinks=self.sinks)
         if pairs is None:
             pairs = [(b, h) for b in range(w.batch) for h in range(w.n_heads)]
         pairs = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
@@ -84,7 +87,8 @@ class OracleStep:
     def partial(self, b, h, sigma, split_size):
         w = self.w
         return self.o.split_partial(q_bh=self.q[b, h], cache_k=self.ck, cache_v=self.cv,
-                                    v_scale=self.vs, k_dtype=w.k_dtype, v_dtype=w.v_dtype,
+                                    v_scale=self.vs, k_scale=self.ks, k_dtype=w.k_dtype,
+                                    v_dtype=w.v_dtype,
                                     n_heads=w.n_heads, b=b, h=h, L=int(self.inputs.seq_lens[b]),
                                     window=w.window, softcap=w.softcap, split_size=split_size,
                                     sigma=sigma)
@@ -104,8 +108,9 @@ def bf16_ulps(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 
 
 def check_slot(w: W.Workload, gpu: dict, ref: dict, q_gpu: np.ndarray, q_ref: np.ndarray) -> dict:
-    """Produced rows: V bit-exact (f32 copy, bf16 RNE, vq8 codes and scales),
-    K within 1 bf16 ulp or 1e-6 relative (f32), q' within 1e-6 relative."""
+    """Produced rows: V bit-exact (f32 copy, bf16 RNE, int8 codes and scales),
+    K within 1 bf16 ulp or 1e-6 relative (f32), q8 key codes within 1 and
+    their scales within 1 f32 ulp, q' within 1e-6 relative."""
     res = {}
     qerr = np.max(np.abs(q_gpu.astype(np.float64) - q_ref)) / max(1e-30, np.max(np.abs(q_ref)))
     res["q_rel"] = float(qerr)
@@ -114,6 +119,15 @@ def check_slot(w: W.Workload, gpu: dict, ref: dict, q_gpu: np.ndarray, q_ref: np
         u = bf16_ulps(gpu["k"], ref["k"])
         res["k_ulps"] = int(u.max())
         assert u.max() <= 1, f"K slot differs by {u.max()} bf16 ulps"
+    elif w.k_dtype == W.I8:
+        # The rotated key is rounded to f32 before quantising; a key whose
+        # f32 rounding differs (a double-precision tie) could move a code by
+        # one, so codes may differ by at most 1 and scales by 1 f32 ulp.
+        dk = np.abs(gpu["k"].astype(np.int32) - ref["k"].astype(np.int32))
+        du = np.abs(gpu["k_scale"].view(np.int32).astype(np.int64)
+                    - ref["k_scale"].view(np.int32).astype(np.int64))
+        res["k_code_diff"], res["k_scale_ulps"] = int(dk.max()), int(du.max())
+        assert dk.max() <= 1 and du.max() <= 1, (dk.max(), du.max())
     else:
         kr = ref["k"].astype(np.float64)
         kerr = np.max(np.abs(gpu["k"].astype(np.float64) - kr)) / max(1e-30, np.max(np.abs(kr)))
@@ -177,15 +191,20 @@ def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0, bloc
     lens = np.asarray(lens, dtype=np.int32)
     say(f"case {w.name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
         f"K/V={w.k_dtype}/{w.v_dtype} lens={lens.tolist()[:8]} S={w.split_size} W={w.window} "
-        f"cap={w.softcap} rope={w.rope.pairing}/{w.rope.scaling} norm={w.qk_norm.enabled}")
+        f"cap={w.softcap} rope={w.rope.pairing}/{w.rope.scaling} norm={w.qk_norm.enabled} "
+        f"sink={w.sink}")
     inputs = W.make_inputs(w, seq_lens=lens)
     paged = W.make_paged(inputs, block_size) if block_size else None
     if paged:
         say(f"  paged: block_size={paged.block_size} max_blocks={paged.max_blocks} "
             f"num_blocks={paged.num_blocks}")
         ck0, cv0 = paged.pool_k.copy(), paged.pool_v.copy()
+        vs0, ks0 = paged.pool_scale, paged.pool_k_scale
     else:
         ck0, cv0 = inputs.cache_k.copy(), inputs.cache_v.copy()
+        vs0, ks0 = inputs.v_scale, inputs.k_scale
+    vs0 = vs0.copy() if vs0 is not None else None
+    ks0 = ks0.copy() if ks0 is not None else None
     st = run_gpu(inputs, paged=paged)
     ref = OracleStep(inputs)
     out = st.out.cpu().numpy()
@@ -198,10 +217,47 @@ def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0, bloc
     mask = np.ones(ck0.shape[:3], bool)
     first, row = st.slot_index()
     mask[first, :, row] = False
-    for dev, host in ((st.cache_k, ck0), (st.cache_v, cv0)):
+    pairs = [(st.cache_k, ck0), (st.cache_v, cv0)]
+    if st.v_scale is not None:
+        pairs.append((st.v_scale, vs0))
+    if st.k_scale is not None:
+        pairs.append((st.k_scale, ks0))
+    for dev, host in pairs:
         g = dev.cpu().numpy().view(host.dtype)
         assert np.array_equal(g[mask].view(np.uint8), host[mask].view(np.uint8)), \
             "cache rows other than the new token's slot changed"
     say(f"  max abs err {err:.3g} (tol {tol:.3g}, {cls})")
     assert err <= tol, (err, tol)
     return err, tol, cls
+
+
+def check_full_size(w: W.Workload, block_size=None):
+    """A named workload at its full size, in the launch configuration the
+    benchmark times: every produced cache row, and a sample of outputs
+    (4 heads per sequence; every head for B = 1) and of split partials (the
+    first and last valid split of 2 heads per sequence) against the oracle."""
+    say(f"full-size {w.name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
+        f"cap={w.capacity} S={w.split_size} window={w.window} softcap={w.softcap} "
+        f"K/V={w.k_dtype}/{w.v_dtype} rope={w.rope.scaling} sink={w.sink} paged={block_size}")
+    inputs = W.make_inputs(w)
+    paged = W.make_paged(inputs, block_size) if block_size else None
+    st = run_gpu(inputs, paged=paged)
+    ref = OracleStep(inputs, copy_cache=False)  # inputs are on the device already
+    rng = np.random.default_rng(99)
+    H = w.n_heads
+    pairs = []
+    for b in range(w.batch):
+        hs = rng.choice(H, size=min(H, 4 if w.batch > 1 else H), replace=False)
+        pairs += [(b, int(h)) for h in hs]
+    out = st.out.cpu().numpy()
+    want = ref.decode(pairs)
+    got = np.stack([out[b, h] for b, h in pairs])
+    tol, cls = out_tolerance(w, want)
+    err = float(np.max(np.abs(got - want)))
+    check_slot(w, st.cache_rows(), ref.slot_rows(), st.q_out.cpu().numpy(), ref.q)
+    sel = {b: [h for bb, h in pairs if bb == b][:2] for b in range(w.batch)}
+    compare_partials(st, ref, w, inputs.seq_lens, pick=lambda b: sel[b])
+    assert np.all(np.isfinite(out))
+    say(f"  sampled {len(pairs)} outputs: max abs err {err:.3g} (tol {tol:.3g}, {cls})")
+    assert err <= tol
+    return err

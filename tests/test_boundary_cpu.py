@@ -48,18 +48,20 @@ def test_library_exports_every_declared_function():
 def test_struct_layouts_match_header():
     import ctypes as C
     assert C.sizeof(B.Shape) == 16
-    assert C.sizeof(B.Rope) == 48 and B.Rope.theta.offset == 8
+    assert C.sizeof(B.Rope) == 56 and B.Rope.theta.offset == 8
+    assert B.Rope.truncate.offset == 44 and B.Rope.attention_factor.offset == 48
     assert C.sizeof(B.QKNorm) == 32 and B.QKNorm.q_weight.offset == 16
-    assert C.sizeof(B.KVCache) == 64 and B.KVCache.k.offset == 16
+    assert C.sizeof(B.KVCache) == 72 and B.KVCache.k.offset == 16
     assert B.KVCache.block_table.offset == 40 and B.KVCache.num_blocks.offset == 56
+    assert B.KVCache.k_scale.offset == 64
 
 
 def shape(b=2, h=8, hkv=2, d=128):
     return B.Shape(b, h, hkv, d)
 
 
-def cache(kd=B.BF16, vd=B.BF16, cap=64, k=FAKE, v=FAKE, s=None):
-    return B.KVCache(kd, vd, cap, k, v, s)
+def cache(kd=B.BF16, vd=B.BF16, cap=64, k=FAKE, v=FAKE, s=None, ks=None):
+    return B.KVCache(kd, vd, cap, k, v, s, None, 0, 0, 0, ks)
 
 
 def attn(sh=None, ca=None, q=FAKE, lens=(10, 20), scale=None, window=0, softcap=0.0, split=16,
@@ -78,6 +80,10 @@ def produce(sh=None, rope=None, norm=None, ca=None, pos=(3, 4), q_in=FAKE, q_out
 
 def combine(sh=None, lens=(10, 20), window=0, split=16, max_splits=4, out=FAKE):
     B.decode_combine(sh or shape(), lens, window, split, max_splits, FAKE, FAKE, out, 0)
+
+
+def combine_sink(sh=None, lens=(10, 20), window=0, split=16, max_splits=4, sinks=FAKE, out=FAKE):
+    B.decode_combine_sink(sh or shape(), lens, window, split, max_splits, FAKE, FAKE, sinks, out, 0)
 
 
 def refused(fn, status, *needles):
@@ -110,7 +116,11 @@ INV, NI = B.ERR_INVALID_ARGUMENT, B.ERR_NOT_IMPLEMENTED
      ["max_splits=2", "need 3"]),
     ("len 0", lambda: attn(lens=(0, 5)), INV, ["seq_lens[0]=0", "[1, 64]"]),
     ("len > cap", lambda: attn(lens=(65, 5)), INV, ["seq_lens[0]=65"]),
-    ("q8 keys", lambda: attn(ca=cache(kd=B.I8, vd=B.I8, s=FAKE)), NI, ["q8", "vq8"]),
+    ("int8 keys, bf16 values", lambda: attn(ca=cache(kd=B.I8, vd=B.BF16)), NI,
+     ["k_dtype=int8 with v_dtype=1", "q8"]),
+    ("q8 no key scale", lambda: attn(ca=cache(kd=B.I8, vd=B.I8, s=FAKE)), INV, ["k_scale is NULL"]),
+    ("q8 key scale misaligned", lambda: attn(ca=cache(kd=B.I8, vd=B.I8, s=FAKE, ks=FAKE + 2)), INV,
+     ["cache.k_scale", "4-byte aligned"]),
     ("bad k dtype", lambda: attn(ca=cache(kd=7)), INV, ["k_dtype=7"]),
     ("bad v dtype", lambda: attn(ca=cache(vd=5)), INV, ["v_dtype=5"]),
     ("vq8 no scale", lambda: attn(ca=cache(vd=B.I8)), INV, ["v_scale is NULL"]),
@@ -133,8 +143,20 @@ def test_decode_attn_refusals(case):
                                                     FAKE, 0), None, []),
     ("theta 0", lambda: produce(rope=B.Rope(0, 0, 0.0, 1, 1, 4, 8192)), INV, ["rope.theta=0"]),
     ("pairing 2", lambda: produce(rope=B.Rope(2, 0, 1e4, 1, 1, 4, 8192)), INV, ["rope.pairing=2"]),
-    ("yarn", lambda: produce(rope=B.Rope(0, 2, 1e4, 1, 1, 4, 8192)), NI,
-     ["unsupported rope_scaling.type=2"]),
+    ("scaling 4", lambda: produce(rope=B.Rope(0, 4, 1e4, 1, 1, 4, 8192)), NI,
+     ["unsupported rope_scaling.type=4", "yarn=3"]),
+    ("linear factor 0", lambda: produce(rope=B.Rope(0, 2, 1e4, 0.0, 1, 4, 8192)), INV,
+     ["rope.factor=0 is invalid for linear"]),
+    ("yarn factor", lambda: produce(rope=B.Rope(0, 3, 1.5e5, 0.5, 1, 32, 4096)), INV,
+     ["rope.factor=0.5 is invalid for yarn"]),
+    ("yarn betas", lambda: produce(rope=B.Rope(0, 3, 1.5e5, 32, 32, 32, 4096)), INV,
+     ["beta_fast)=32 must be finite and > beta_slow=32"]),
+    ("yarn beta_slow", lambda: produce(rope=B.Rope(0, 3, 1.5e5, 32, 0, 32, 4096)), INV,
+     ["beta_slow)=0"]),
+    ("yarn orig", lambda: produce(rope=B.Rope(0, 3, 1.5e5, 32, 1, 32, 0)), INV,
+     ["original_max_position=0"]),
+    ("yarn attention factor", lambda: produce(rope=B.Rope(0, 3, 1.5e5, 32, 1, 32, 4096, 0, -1.0)),
+     INV, ["rope.attention_factor=-1"]),
     ("llama3 factor", lambda: produce(rope=B.Rope(1, 1, 5e5, 0.5, 1, 4, 8192)), INV, ["rope.factor=0.5"]),
     ("llama3 high<=low", lambda: produce(rope=B.Rope(1, 1, 5e5, 8, 4, 4, 8192)), INV,
      ["high_freq_factor=4"]),
@@ -173,6 +195,20 @@ def test_decode_combine_refusals(case):
     _, fn, status, needles = case
     msg = refused(fn, status, *needles)
     assert msg.startswith("uaii_decode_combine: ")
+
+
+@host_only
+@pytest.mark.parametrize("case", [
+    ("sinks null", lambda: combine_sink(sinks=None), INV, ["sinks is NULL"]),
+    ("sinks misaligned", lambda: combine_sink(sinks=FAKE + 2), INV, ["sinks", "4-byte aligned"]),
+    ("window", lambda: combine_sink(window=-3), INV, ["window=-3"]),
+    ("out null", lambda: combine_sink(out=None), INV, ["out is NULL"]),
+    ("head_dim", lambda: combine_sink(sh=shape(d=48)), NI, ["head_dim=48"]),
+], ids=lambda c: c[0])
+def test_decode_combine_sink_refusals(case):
+    _, fn, status, needles = case
+    msg = refused(fn, status, *needles)
+    assert msg.startswith("uaii_decode_combine_sink: ")
 
 
 @host_only

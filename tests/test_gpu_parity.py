@@ -86,29 +86,7 @@ FULL = ["tiny", "llama3.2-1b", "llama3.1-8b-ragged", "qwen3-vq8", "gemma2-local"
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload(name):
-    w = W.WORKLOADS[name]
-    P.say(f"full-size {name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
-          f"cap={w.capacity} S={w.split_size} window={w.window} softcap={w.softcap}")
-    inputs = W.make_inputs(w)
-    st = run_gpu(inputs)
-    ref = P.OracleStep(inputs, copy_cache=False)  # inputs are on the device already
-    rng = np.random.default_rng(99)
-    H = w.n_heads
-    pairs = []
-    for b in range(w.batch):
-        hs = rng.choice(H, size=min(H, 4 if w.batch > 1 else H), replace=False)
-        pairs += [(b, int(h)) for h in hs]
-    out = st.out.cpu().numpy()
-    want = ref.decode(pairs)
-    got = np.stack([out[b, h] for b, h in pairs])
-    tol, cls = P.out_tolerance(w, want)
-    err = float(np.max(np.abs(got - want)))
-    P.check_slot(w, st.cache_rows(), ref.slot_rows(), st.q_out.cpu().numpy(), ref.q)
-    sel = {b: [h for bb, h in pairs if bb == b][:2] for b in range(w.batch)}
-    compare_partials(st, ref, w, inputs.seq_lens, pick=lambda b: sel[b])
-    assert np.all(np.isfinite(out))
-    P.say(f"  sampled {len(pairs)} outputs: max abs err {err:.3g} (tol {tol:.3g}, {cls})")
-    assert err <= tol
+    P.check_full_size(W.WORKLOADS[name])
 
 
 def test_deterministic():
