@@ -21,9 +21,10 @@
 //     work-group but never synchronise (no barriers, no cross-wave merge);
 //   * the G query heads that share the kv head are held in registers, so
 //     every K and V byte is read from HBM exactly once per group;
+//   * int8 values use 8-byte loads (see Elem);
 //   * a wave walks its split in chunks of up to 512 rows with two passes per
-//     chunk: K (coalesced 16-byte loads, 8-byte for int8, a row spread over
-//     d*sizeof(K)/load lanes, scores reduced across those lanes with DPP) with raw scores
+//     chunk: K (coalesced 16-byte loads, a row spread over d*sizeof(K)/16
+//     lanes, scores reduced across those lanes with DPP) with raw scores
 //     parked in LDS, then V with the softmax weights broadcast from LDS; the
 //     running max and sum rescale only between chunks;
 //   * scores live in the log2 domain (q pre-multiplied by scale*log2 e) so the
@@ -159,13 +160,18 @@ __device__ inline void widen(const V& w, float (&out)[E]) {
   }
 }
 
-// Element size and the bytes one lane loads per row segment.  int8 rows
-// use 8-byte loads, so a lane holds 8 codes: the query and accumulator
-// registers then have the bf16 layout instead of twice as many entries.
+// Element size and the bytes one lane loads per row segment.  Keys use
+// 16-byte loads (a wider segment means fewer cross-lane reduction steps per
+// byte), except int8 keys with G = 8, whose 16 query entries per head would
+// not fit in registers.  int8 values use 8-byte loads, so a lane
+// accumulates 8 values per head: the accumulator keeps the bf16 layout
+// instead of twice as many registers.
 template <int DT>
 struct Elem {
   static constexpr int bytes = DT == kF32 ? 4 : (DT == kBF16 ? 2 : 1);
-  static constexpr int load = DT == kI8 ? 8 : 16;
+  static constexpr int value_load = DT == kI8 ? 8 : 16;
+  template <int G>
+  static constexpr int key_load() { return (DT == kI8 && G >= 8) ? 8 : 16; }
 };
 
 // amdgpu_waves_per_eu(2, 8): at least two waves per SIMD.  Without the hint
@@ -175,7 +181,7 @@ template <int D, int G, int KT, int VT, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 decode_partial_kernel(AttnArgs a) {
   constexpr int KB = Elem<KT>::bytes, VB = Elem<VT>::bytes;
-  constexpr int KLB = Elem<KT>::load, VLB = Elem<VT>::load;
+  constexpr int KLB = Elem<KT>::template key_load<G>(), VLB = Elem<VT>::value_load;
   constexpr int KLPR = D * KB / KLB;  // lanes per K row
   constexpr int KRPL = 64 / KLPR;     // K rows per wave load
   constexpr int KE = KLB / KB;        // K elements per lane
@@ -265,7 +271,7 @@ decode_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
   float m_run[G], l_run[G];
-  float psum[G];  // vq8: sum of this lane's scaled weights (removes the +128 of the codes)
+  float psum[G];  // int8 values: sum of the scaled weights this lane wrote (removes the +128)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m_run[g] = -INFINITY;
@@ -458,7 +464,9 @@ decode_partial_kernel(AttnArgs a) {
           const float p =
               ok ? __builtin_amdgcn_exp2f(capped_log2(sc[r * G + g], capped, cap_c, cap_inv) - m_run[g]) : 0.0f;
           l_run[g] += p;
-          sc[r * G + g] = p * vs;
+          const float pv = p * vs;
+          sc[r * G + g] = pv;
+          if constexpr (VT == kI8) psum[g] += pv;
         }
       }
     }
@@ -475,7 +483,6 @@ decode_partial_kernel(AttnArgs a) {
       for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(p[g], vf[e], acc[g][e]);
-        if constexpr (VT == kI8) psum[g] += p[g];
       }
     };
     const int vx0 = TV0 - A + vr;  // LDS row of tile 0 for this lane
@@ -509,12 +516,7 @@ decode_partial_kernel(AttnArgs a) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     l_run[g] = wave_sum(l_run[g]);
-    if constexpr (VT == kI8) {
-      // Each row's weight sits in every lane of the row; summing one lane
-      // per row group counts it once.
-#pragma unroll
-      for (int m = VLPR; m < 64; m <<= 1) psum[g] += __shfl_xor(psum[g], m);
-    }
+    if constexpr (VT == kI8) psum[g] = wave_sum(psum[g]);  // one lane wrote each row's weight
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       float x = acc[g][e];
