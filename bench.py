@@ -127,6 +127,8 @@ def main() -> int:
     ap.add_argument("--split-size", type=int, default=None)
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK_SIZE",
                     help="use the paged cache layout with this block size (0: contiguous)")
+    ap.add_argument("--fused", action="store_true",
+                    help="run the step as one launch (uaii_decode_step) instead of three calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -170,8 +172,9 @@ def main() -> int:
     # slower than steady state; they are kept out of the timed region.
     t_w = time.perf_counter()
     n_w = 0
+    one_step = st.fused_step if args.fused else st.step
     while n_w < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
-        st.step()
+        one_step()
         n_w += 1
         if n_w % 10 == 0:
             torch.cuda.synchronize()
@@ -189,6 +192,15 @@ def main() -> int:
     t0 = time.perf_counter()
     start.record()
     for i in range(K):
+        if args.fused:
+            # The single launch is the whole step and its dominant kernel.
+            if i % EVERY == 0:
+                ev[i // EVERY][0].record()
+                st.fused_step()
+                ev[i // EVERY][1].record()
+            else:
+                st.fused_step()
+            continue
         st.produce()
         if i % EVERY == 0:
             ev[i // EVERY][0].record()
@@ -207,7 +219,7 @@ def main() -> int:
 
     step_gbs = kv_bytes / (ms_step * 1e-3) / 1e9
     attn_gbs = kv_bytes / (attn_mean * 1e-3) / 1e9
-    traffic = measured_traffic(name) if not args.paged else None
+    traffic = measured_traffic(name) if not (args.paged or args.fused) else None
     result = {
         "metric": METRIC,
         "value": round(step_gbs, 2),
@@ -230,6 +242,7 @@ def main() -> int:
                    "rope_scaling": {0: "plain", 1: "llama3", 2: "linear", 3: "yarn"}[w.rope.scaling],
                    "attention_sink": w.sink,
                    "layout": f"paged(block_size={args.paged})" if args.paged else "contiguous",
+                   "launches_per_step": 1 if args.fused else 3,
                    "parallelism": "single-gpu"},
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(w.batch / (ms_step * 1e-3), 1),
@@ -237,7 +250,8 @@ def main() -> int:
         "attn_partial_ms": round(attn_mean, 5),
         "wall_s_timed": round(wall, 3),
         "roofline": {
-            "kernel": "decode_partial_kernel",
+            "kernel": ("decode_partial_kernel (single-launch step)" if args.fused
+                       else "decode_partial_kernel"),
             "bound": "hbm",
             "achieved": round(attn_gbs, 2),
             "peak": HBM_PEAK_GBS,

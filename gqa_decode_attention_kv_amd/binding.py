@@ -22,7 +22,7 @@ ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 ROPE_PLAIN, ROPE_LLAMA3, ROPE_LINEAR, ROPE_YARN = 0, 1, 2, 3
 
 EXPORTS = ("uaii_last_error", "uaii_kv_produce", "uaii_decode_attn", "uaii_decode_combine",
-           "uaii_decode_combine_sink")
+           "uaii_decode_combine_sink", "uaii_decode_step")
 
 
 class UaiiError(RuntimeError):
@@ -82,6 +82,11 @@ def load() -> C.CDLL:
         lib.uaii_decode_combine_sink.restype = C.c_int
         lib.uaii_decode_combine_sink.argtypes = [C.POINTER(Shape), ip, C.c_int32, C.c_int32,
                                                  C.c_int32, vp, vp, vp, vp, vp]
+        lib.uaii_decode_step.restype = C.c_int
+        lib.uaii_decode_step.argtypes = [C.POINTER(Shape), C.POINTER(Rope), C.POINTER(QKNorm),
+                                         vp, vp, vp, ip, C.POINTER(KVCache), C.c_float, C.c_int32,
+                                         C.c_float, C.c_int32, C.c_int32, vp, vp, vp, vp, vp, vp,
+                                         vp]
         _lib = lib
     return _lib
 
@@ -132,3 +137,15 @@ def decode_combine_sink(shape: Shape, seq_lens, window: int, split_size: int, ma
     arr, p = _host_i32(seq_lens, shape.batch)
     _check(load().uaii_decode_combine_sink(C.byref(shape), p, window, split_size, max_splits,
                                            part_o, part_lse, sinks, out, stream))
+
+
+def decode_step(shape: Shape, rope: Rope, qk_norm: QKNorm | None, q_in: int, k_in: int, v_in: int,
+                seq_lens, cache: KVCache, scale: float, window: int, softcap: float,
+                split_size: int, max_splits: int, sinks: int | None, q_out: int, part_o: int,
+                part_lse: int, counters: int, out: int, stream: int = 0) -> None:
+    arr, p = _host_i32(seq_lens, shape.batch)
+    _check(load().uaii_decode_step(C.byref(shape), C.byref(rope),
+                                   C.byref(qk_norm) if qk_norm is not None else None,
+                                   q_in, k_in, v_in, p, C.byref(cache), scale, window, softcap,
+                                   split_size, max_splits, sinks, q_out, part_o, part_lse,
+                                   counters, out, stream))

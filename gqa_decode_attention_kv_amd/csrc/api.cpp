@@ -176,22 +176,13 @@ uaii_status check_lens(const char* fn, const uaii_attn_shape* s, const int32_t* 
   return UAII_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* uaii_last_error(void) { return g_error.c_str(); }
-
-uaii_status uaii_kv_produce(const uaii_attn_shape* shape, const uaii_rope* rope,
-                            const uaii_qk_norm* qk_norm, const float* q_in, const float* k_in,
-                            const float* v_in, const int32_t* positions, const uaii_kv_cache* cache,
-                            float* q_out, void* stream) {
-  const char* fn = "uaii_kv_produce";
-  g_error.clear();
-  uaii_status st = check_shape(fn, shape);
-  if (st != UAII_OK) return st;
-  st = check_cache(fn, cache);
-  if (st != UAII_OK) return st;
+// Checks the producer's arguments (rope, norm, inputs, q_out) and fills
+// everything in ProduceArgs except the positions.  Shape and cache are
+// checked by the caller.
+uaii_status produce_args(const char* fn, const uaii_attn_shape* shape, const uaii_rope* rope,
+                         const uaii_qk_norm* qk_norm, const float* q_in, const float* k_in,
+                         const float* v_in, const uaii_kv_cache* cache, float* q_out,
+                         uaii::ProduceArgs* out) {
   REQUIRE(rope != nullptr, kInvalid, "rope is NULL; pass a uaii_rope");
   REQUIRE(rope->pairing == UAII_ROPE_NEOX || rope->pairing == UAII_ROPE_INTERLEAVED, kInvalid,
           "rope.pairing=%d is not a pairing code (neox=0, interleaved=1)", rope->pairing);
@@ -242,11 +233,6 @@ uaii_status uaii_kv_produce(const uaii_attn_shape* shape, const uaii_rope* rope,
   CHECK_PTR("k_in", k_in, 16);
   CHECK_PTR("v_in", v_in, 16);
   CHECK_PTR("q_out", q_out, 16);
-  REQUIRE(positions != nullptr, kInvalid, "positions is NULL; pass a host array of batch=%d positions",
-          shape->batch);
-  for (int b = 0; b < shape->batch; ++b)
-    REQUIRE(positions[b] >= 0 && positions[b] < cache->capacity, kInvalid,
-            "positions[%d]=%d is outside [0, capacity=%d)", b, positions[b], cache->capacity);
 
   uaii::ProduceArgs a{};
   a.B = shape->batch;
@@ -301,21 +287,19 @@ uaii_status uaii_kv_produce(const uaii_attn_shape* shape, const uaii_rope* rope,
   a.block_size = cache->block_table ? cache->block_size : 0;
   a.max_blocks = cache->block_table ? cache->max_blocks : 0;
   a.num_blocks = cache->block_table ? cache->num_blocks : 0;
-  for (int b = 0; b < shape->batch; ++b) a.pos[b] = positions[b];
-  return device_status(fn, uaii::launch_kv_produce(a, static_cast<hipStream_t>(stream)));
+  *out = a;
+  return UAII_OK;
 }
 
-uaii_status uaii_decode_attn(const uaii_attn_shape* shape, const uaii_kv_cache* cache, const float* q,
-                             const int32_t* seq_lens, float scale, int32_t window, float softcap,
-                             int32_t split_size, int32_t max_splits, float* part_o, float* part_lse,
-                             void* stream) {
-  const char* fn = "uaii_decode_attn";
-  g_error.clear();
-  uaii_status st = check_shape(fn, shape);
-  if (st != UAII_OK) return st;
-  st = check_cache(fn, cache);
-  if (st != UAII_OK) return st;
-  st = check_lens(fn, shape, seq_lens, cache->capacity, split_size, max_splits, window);
+// Checks the attention arguments (lengths, window, softcap, scale,
+// partials) and fills AttnArgs with the work table.  Shape and cache are
+// checked by the caller; q is checked here only when check_q is set (the
+// fused step computes the queries itself).
+uaii_status attn_args(const char* fn, const uaii_attn_shape* shape, const uaii_kv_cache* cache,
+                      const float* q, bool check_q, const int32_t* seq_lens, float scale, int32_t window,
+                      float softcap, int32_t split_size, int32_t max_splits, float* part_o, float* part_lse,
+                      uaii::AttnArgs* out) {
+  uaii_status st = check_lens(fn, shape, seq_lens, cache->capacity, split_size, max_splits, window);
   if (st != UAII_OK) return st;
   REQUIRE(std::isfinite(softcap) && softcap >= 0.0f, kInvalid,
           "softcap=%g is invalid (0 = none, c > 0 applies c*tanh(s/c))", static_cast<double>(softcap));
@@ -325,7 +309,7 @@ uaii_status uaii_decode_attn(const uaii_attn_shape* shape, const uaii_kv_cache* 
           "scale=%.9g is not supported (supported: 1/sqrt(head_dim)=%.9g; a differing "
           "query_pre_attn_scalar is refused)",
           static_cast<double>(scale), want);
-  CHECK_PTR("q", q, 16);
+  if (check_q) CHECK_PTR("q", q, 16);
   CHECK_PTR("part_o", part_o, 16);
   CHECK_PTR("part_lse", part_lse, 4);
 
@@ -347,7 +331,6 @@ uaii_status uaii_decode_attn(const uaii_attn_shape* shape, const uaii_kv_cache* 
   a.q_mul = softcap > 0.0f ? s : s * log2e;
   a.softcap = softcap;
   build_table(shape->batch, seq_lens, window, split_size, &a.t);
-  const int G = shape->n_heads / shape->n_kv_heads;
   if (cache->block_table != nullptr) {
     a.block_table = cache->block_table;
     a.block_size = cache->block_size;
@@ -355,13 +338,91 @@ uaii_status uaii_decode_attn(const uaii_attn_shape* shape, const uaii_kv_cache* 
     while ((1 << a.log2_bs) < cache->block_size) ++a.log2_bs;
     a.max_blocks = cache->max_blocks;
     a.num_blocks = cache->num_blocks;
-    return device_status(fn, uaii::launch_decode_partial_paged(shape->head_dim, G, cache->k_dtype,
-                                                               cache->v_dtype, a,
-                                                               static_cast<hipStream_t>(stream)));
   }
-  return device_status(fn, uaii::launch_decode_partial(shape->head_dim, G, cache->k_dtype,
-                                                       cache->v_dtype, a,
-                                                       static_cast<hipStream_t>(stream)));
+  *out = a;
+  return UAII_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* uaii_last_error(void) { return g_error.c_str(); }
+
+uaii_status uaii_kv_produce(const uaii_attn_shape* shape, const uaii_rope* rope,
+                            const uaii_qk_norm* qk_norm, const float* q_in, const float* k_in,
+                            const float* v_in, const int32_t* positions, const uaii_kv_cache* cache,
+                            float* q_out, void* stream) {
+  const char* fn = "uaii_kv_produce";
+  g_error.clear();
+  uaii_status st = check_shape(fn, shape);
+  if (st != UAII_OK) return st;
+  st = check_cache(fn, cache);
+  if (st != UAII_OK) return st;
+  uaii::ProduceArgs a{};
+  st = produce_args(fn, shape, rope, qk_norm, q_in, k_in, v_in, cache, q_out, &a);
+  if (st != UAII_OK) return st;
+  REQUIRE(positions != nullptr, kInvalid, "positions is NULL; pass a host array of batch=%d positions",
+          shape->batch);
+  for (int b = 0; b < shape->batch; ++b)
+    REQUIRE(positions[b] >= 0 && positions[b] < cache->capacity, kInvalid,
+            "positions[%d]=%d is outside [0, capacity=%d)", b, positions[b], cache->capacity);
+  for (int b = 0; b < shape->batch; ++b) a.pos[b] = positions[b];
+  return device_status(fn, uaii::launch_kv_produce(a, static_cast<hipStream_t>(stream)));
+}
+
+uaii_status uaii_decode_attn(const uaii_attn_shape* shape, const uaii_kv_cache* cache, const float* q,
+                             const int32_t* seq_lens, float scale, int32_t window, float softcap,
+                             int32_t split_size, int32_t max_splits, float* part_o, float* part_lse,
+                             void* stream) {
+  const char* fn = "uaii_decode_attn";
+  g_error.clear();
+  uaii_status st = check_shape(fn, shape);
+  if (st != UAII_OK) return st;
+  st = check_cache(fn, cache);
+  if (st != UAII_OK) return st;
+  uaii::AttnArgs a{};
+  st = attn_args(fn, shape, cache, q, true, seq_lens, scale, window, softcap, split_size, max_splits, part_o,
+                 part_lse, &a);
+  if (st != UAII_OK) return st;
+  const int G = shape->n_heads / shape->n_kv_heads;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->block_table != nullptr)
+    return device_status(
+        fn, uaii::launch_decode_partial_paged(shape->head_dim, G, cache->k_dtype, cache->v_dtype, a, s));
+  return device_status(fn,
+                       uaii::launch_decode_partial(shape->head_dim, G, cache->k_dtype, cache->v_dtype, a, s));
+}
+
+uaii_status uaii_decode_step(const uaii_attn_shape* shape, const uaii_rope* rope, const uaii_qk_norm* qk_norm,
+                             const float* q_in, const float* k_in, const float* v_in, const int32_t* seq_lens,
+                             const uaii_kv_cache* cache, float scale, int32_t window, float softcap,
+                             int32_t split_size, int32_t max_splits, const float* sinks, float* q_out,
+                             float* part_o, float* part_lse, int32_t* counters, float* out, void* stream) {
+  const char* fn = "uaii_decode_step";
+  g_error.clear();
+  uaii_status st = check_shape(fn, shape);
+  if (st != UAII_OK) return st;
+  st = check_cache(fn, cache);
+  if (st != UAII_OK) return st;
+  uaii::StepArgs x{};
+  st = produce_args(fn, shape, rope, qk_norm, q_in, k_in, v_in, cache, q_out, &x.p);
+  if (st != UAII_OK) return st;
+  st = attn_args(fn, shape, cache, q_out, false, seq_lens, scale, window, softcap, split_size, max_splits, part_o,
+                 part_lse, &x.a);
+  if (st != UAII_OK) return st;
+  if (sinks != nullptr) CHECK_PTR("sinks", sinks, 4);
+  CHECK_PTR("counters", counters, 4);
+  CHECK_PTR("out", out, 16);
+  x.sinks = sinks;
+  x.out = out;
+  x.counters = counters;
+  const int G = shape->n_heads / shape->n_kv_heads;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->block_table != nullptr)
+    return device_status(
+        fn, uaii::launch_decode_step_paged(shape->head_dim, G, cache->k_dtype, cache->v_dtype, x, s));
+  return device_status(fn, uaii::launch_decode_step(shape->head_dim, G, cache->k_dtype, cache->v_dtype, x, s));
 }
 
 }  // extern "C"

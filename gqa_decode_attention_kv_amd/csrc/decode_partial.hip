@@ -6,7 +6,7 @@ namespace uaii {
 
 hipError_t launch_decode_partial(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a,
                                  hipStream_t stream) {
-  return dispatch<false>(D, G, k_dtype, v_dtype, a, stream);
+  return dispatch<false, false>(D, G, k_dtype, v_dtype, a, stream);
 }
 
 }  // namespace uaii

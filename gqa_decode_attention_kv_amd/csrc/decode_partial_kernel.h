@@ -49,7 +49,9 @@
 
 #include <type_traits>
 
+#include "combine_math.h"
 #include "launch.h"
+#include "producer_math.h"
 
 namespace uaii {
 namespace {
@@ -174,12 +176,39 @@ struct Elem {
   static constexpr int key_load() { return (DT == kI8 && G >= 8) ? 8 : 16; }
 };
 
+// Kernel arguments: the partials alone, or the fused step (partials plus
+// the producer's inputs, the sinks, the output and the arrival counters).
+template <bool FUSED>
+using KernelArgs = typename std::conditional<FUSED, StepArgs, AttnArgs>::type;
+
+__host__ __device__ inline const AttnArgs& attn_of(const AttnArgs& a) { return a; }
+__host__ __device__ inline const AttnArgs& attn_of(const StepArgs& s) { return s.a; }
+__device__ inline const StepArgs* step_of(const AttnArgs&) { return nullptr; }
+__device__ inline const StepArgs* step_of(const StepArgs& s) { return &s; }
+
+// FUSED = false: the split-K partials of uaii_decode_attn.
+// FUSED = true: the whole decode step of uaii_decode_step in one launch.
+//   * Each wave computes its G query heads from q_in (norm, RoPE, in double
+//     precision, exactly as the producer does) instead of loading q_out;
+//     the wave of the first split also writes q_out.
+//   * The wave whose split holds the new token's slot (the last one) stores
+//     the new key and value in the cache format and keeps the stored values
+//     in registers: its K and V passes read the cache rows before the slot,
+//     and the new row is merged into the softmax afterwards.  No wave reads
+//     a cache row that another wave of the same launch writes.
+//   * After writing its partial, a wave takes a ticket from the arrival
+//     counter of its (sequence, kv head); the last of that pair's splits to
+//     arrive combines the G heads (with the optional sink) and returns the
+//     counter to zero, so the counters need no clearing between launches.
+//
 // amdgpu_waves_per_eu(2, 8): at least two waves per SIMD.  Without the hint
 // the allocator spends registers freely (the vq8 kernel spilled into AGPRs at
 // one wave per SIMD); with it the bf16 d128 kernel fits three waves per SIMD.
-template <int D, int G, int KT, int VT, bool PAGED>
+template <int D, int G, int KT, int VT, bool PAGED, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void
-decode_partial_kernel(AttnArgs a) {
+decode_partial_kernel(const KernelArgs<FUSED> args) {
+  const AttnArgs& a = attn_of(args);
+  const StepArgs* x = step_of(args);
   constexpr int KB = Elem<KT>::bytes, VB = Elem<VT>::bytes;
   constexpr int KLB = Elem<KT>::template key_load<G>(), VLB = Elem<VT>::value_load;
   constexpr int KLPR = D * KB / KLB;  // lanes per K row
@@ -204,6 +233,9 @@ decode_partial_kernel(AttnArgs a) {
   static_assert(KLPR >= 4 && VLPR >= 4, "row must span at least a quad");
 
   __shared__ __attribute__((aligned(16))) float smem[kWaves * kLdsRows * G];
+  // Fused step: per-wave staging of one head vector in double precision.
+  __shared__ double sxd[FUSED ? kWaves * D : 1];
+  static_assert(!FUSED || kLdsRows * G >= (G + 1) * D, "query and value staging must fit a wave's LDS");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -218,7 +250,12 @@ decode_partial_kernel(AttnArgs a) {
   for (int i = 1; i < a.t.n_seq; ++i) b += (w >= a.t.work_prefix[i]) ? 1 : 0;
   const int sigma = a.t.first_split[b] + (w - a.t.work_prefix[b]);
   const int r0 = max(sigma * a.split_size, a.t.lo[b]);
-  const int r1 = min((sigma + 1) * a.split_size, a.t.len[b]);
+  // Cache rows [r0, r1) are read.  The fused step leaves out the new
+  // token's slot L - 1: the wave that holds it (has_new) merges it from
+  // registers after the last chunk.
+  const int L = a.t.len[b];
+  const bool has_new = FUSED && (sigma + 1) * a.split_size >= L;
+  const int r1 = min((sigma + 1) * a.split_size, FUSED ? L - 1 : L);
 
   // Contiguous: the (b, kvh) slab starts at row slab of the cache.  Paged:
   // row r lives in physical block block_table[b][r / bs] at offset r % bs.
@@ -230,8 +267,79 @@ decode_partial_kernel(AttnArgs a) {
 
   // Query group in registers: lane holds q[h][kc*KE .. kc*KE + KE) for its K segment.
   const int kr = lane / KLPR, kc = lane % KLPR;
+  const int vr = lane / VLPR, vc = lane % VLPR;
+  float* sc = smem + wave * (kLdsRows * G);  // this wave's [row][G] scores / weights
   float q[G][KE];
-  {
+  float s_new[G];  // fused step: raw scores of the new token's row
+  float vnew[VE];  // fused step: its stored value, this lane's V segment
+  if constexpr (FUSED) {
+    const ProduceArgs& p = x->p;
+    constexpr int EPL = pm::Shape<D>::EPL, NP = pm::Shape<D>::NP;
+    const int pos = L - 1;
+    double* sx = sxd + wave * D;
+    float* qs = sc;  // G rows of D floats: the rotated queries
+    pm::Angles<D> an;
+    pm::rope_angles<D>(p, pos, lane, an);
+    const bool write_q = sigma == a.t.first_split[b];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t hrow = static_cast<int64_t>(b) * a.H + kvh * G + g;
+      float xin[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) xin[e] = p.q_in[hrow * D + lane + 64 * e];
+      pm::Rotated<D> r;
+      pm::norm_rope<D>(p, xin, p.w_q, an, sx, lane, r);
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        if (!r.ok[j]) continue;
+        const float fa = static_cast<float>(r.ya[j]), fb = static_cast<float>(r.yb[j]);
+        qs[g * D + r.ia[j]] = fa;
+        qs[g * D + r.ib[j]] = fb;
+        if (write_q) {
+          p.q_out[hrow * D + r.ia[j]] = fa;
+          p.q_out[hrow * D + r.ib[j]] = fb;
+        }
+      }
+    }
+    pm::wave_sync();
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < KE; ++e) q[g][e] = qs[g * D + kc * KE + e] * a.q_mul;
+    if (has_new) {
+      const int64_t krow = static_cast<int64_t>(b) * a.Hkv + kvh;
+      float kin[EPL], vin[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        kin[e] = p.k_in[krow * D + lane + 64 * e];
+        vin[e] = p.v_in[krow * D + lane + 64 * e];
+      }
+      pm::Rotated<D> r;
+      pm::norm_rope<D>(p, kin, p.w_k, an, sx, lane, r);
+      const int64_t slot = pm::cache_slot<D>(p, b, kvh, pos);
+      float kst[2 * NP], vst[EPL];
+      pm::store_key<D>(p, r, slot, lane, kst);
+      pm::store_value<D>(p, vin, slot, lane, vst);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          if (!r.ok[j]) continue;
+          t = fmaf(qs[g * D + r.ia[j]] * a.q_mul, kst[2 * j], t);
+          t = fmaf(qs[g * D + r.ib[j]] * a.q_mul, kst[2 * j + 1], t);
+        }
+        s_new[g] = wave_sum(t);
+      }
+      float* vs = sc + G * D;  // the stored value row, then this lane's segment
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vs[lane + 64 * e] = vst[e];
+      pm::wave_sync();
+#pragma unroll
+      for (int e = 0; e < VE; ++e) vnew[e] = vs[vc * VE + e];
+    }
+    pm::wave_sync();  // the staging area is the K pass's score buffer
+  } else {
     const float* qb = a.q + (static_cast<int64_t>(b) * a.H + kvh * G) * D + kc * KE;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -245,6 +353,8 @@ decode_partial_kernel(AttnArgs a) {
       }
     }
   }
+  (void)s_new;
+  (void)vnew;
   // q8 keys: each raw score carries 128 * sum(q_h) from the code offset.
   float c128[G];
 #pragma unroll
@@ -264,7 +374,6 @@ decode_partial_kernel(AttnArgs a) {
   const bool capped = a.softcap > 0.0f;
   const float cap_c = a.softcap, cap_inv = capped ? 1.0f / a.softcap : 0.0f;
 
-  const int vr = lane / VLPR, vc = lane % VLPR;
   float acc[G][VE];
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -278,8 +387,6 @@ decode_partial_kernel(AttnArgs a) {
     l_run[g] = 0.0f;
     psum[g] = 0.0f;
   }
-
-  float* sc = smem + wave * (kLdsRows * G);  // this wave's [row][G] scores / weights
 
   for (int a0 = r0; a0 < r1; a0 += kRowsPerChunk) {
     const int nrows = min(kRowsPerChunk, r1 - a0);  // rows [a0, a0 + nrows), wave-uniform
@@ -512,6 +619,29 @@ decode_partial_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
+  // ---- fused step: merge the new token's row (scores from the prologue) ----
+  if constexpr (FUSED) {
+    if (has_new) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float sl = capped_log2(s_new[g], capped, cap_c, cap_inv);
+        const float m_new = fmaxf(m_run[g], sl);
+        const float alpha = (m_run[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
+        psum[g] *= alpha;
+        m_run[g] = m_new;
+        const float pn = __builtin_amdgcn_exp2f(sl - m_new);
+        if (lane == 0) l_run[g] += pn;  // l is summed over the whole wave below
+        if (vr == 0) {                  // acc is summed over the row groups below
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(pn, vnew[e], acc[g][e]);
+        }
+      }
+    }
+  }
+
   // ---- merge the wave's row groups and write the split's partial ----------
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -542,45 +672,70 @@ decode_partial_kernel(AttnArgs a) {
     for (int g = 0; g < G; ++g)
       a.part_lse[row0 + static_cast<int64_t>(g) * a.max_splits] = (m_run[g] + log2f(l_run[g])) * kLn2;
   }
+
+  // ---- fused step: the last split of (b, kvh) to arrive combines ----------
+  if constexpr (FUSED) {
+    const int ns = a.t.work_prefix[b + 1] - a.t.work_prefix[b];
+    int32_t* ctr = x->counters + static_cast<int64_t>(b) * a.Hkv + kvh;
+    // Release this wave's partial before taking the ticket; the combining
+    // wave acquires before reading the others' partials.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    int ticket = 0;
+    if (lane == 0) ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ticket = __shfl(ticket, 0);
+    if (ticket != ns - 1) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int s0 = a.t.first_split[b];
+    const bool has_sink = x->sinks != nullptr;
+#pragma unroll 1
+    for (int g = 0; g < G; ++g) {
+      const int h = kvh * G + g;
+      const int64_t crow = (static_cast<int64_t>(b) * a.H + h) * a.max_splits + s0;
+      combine_row<D>(a.part_lse + crow, a.part_o + crow * D + lane, ns, has_sink, has_sink ? x->sinks[h] : 0.0f,
+                     x->out + (static_cast<int64_t>(b) * a.H + h) * D, lane);
+    }
+    if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
-template <int D, int G, int KT, int VT, bool PAGED>
-hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
+template <int D, int G, int KT, int VT, bool PAGED, bool FUSED>
+hipError_t launch_one(const KernelArgs<FUSED>& args, hipStream_t stream) {
+  const AttnArgs& a = attn_of(args);
   const int items = a.t.work_prefix[a.t.n_seq] * a.Hkv;
   const dim3 grid((items + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL((decode_partial_kernel<D, G, KT, VT, PAGED>), grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((decode_partial_kernel<D, G, KT, VT, PAGED, FUSED>), grid, dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
-template <int D, int G, bool PAGED>
-hipError_t by_dtype(int kt, int vt, const AttnArgs& a, hipStream_t s) {
-  if (kt == kF32 && vt == kF32) return launch_one<D, G, kF32, kF32, PAGED>(a, s);
-  if (kt == kF32 && vt == kBF16) return launch_one<D, G, kF32, kBF16, PAGED>(a, s);
-  if (kt == kF32 && vt == kI8) return launch_one<D, G, kF32, kI8, PAGED>(a, s);
-  if (kt == kBF16 && vt == kF32) return launch_one<D, G, kBF16, kF32, PAGED>(a, s);
-  if (kt == kBF16 && vt == kBF16) return launch_one<D, G, kBF16, kBF16, PAGED>(a, s);
-  if (kt == kBF16 && vt == kI8) return launch_one<D, G, kBF16, kI8, PAGED>(a, s);
-  if (kt == kI8 && vt == kI8) return launch_one<D, G, kI8, kI8, PAGED>(a, s);
+template <int D, int G, bool PAGED, bool FUSED>
+hipError_t by_dtype(int kt, int vt, const KernelArgs<FUSED>& a, hipStream_t s) {
+  if (kt == kF32 && vt == kF32) return launch_one<D, G, kF32, kF32, PAGED, FUSED>(a, s);
+  if (kt == kF32 && vt == kBF16) return launch_one<D, G, kF32, kBF16, PAGED, FUSED>(a, s);
+  if (kt == kF32 && vt == kI8) return launch_one<D, G, kF32, kI8, PAGED, FUSED>(a, s);
+  if (kt == kBF16 && vt == kF32) return launch_one<D, G, kBF16, kF32, PAGED, FUSED>(a, s);
+  if (kt == kBF16 && vt == kBF16) return launch_one<D, G, kBF16, kBF16, PAGED, FUSED>(a, s);
+  if (kt == kBF16 && vt == kI8) return launch_one<D, G, kBF16, kI8, PAGED, FUSED>(a, s);
+  if (kt == kI8 && vt == kI8) return launch_one<D, G, kI8, kI8, PAGED, FUSED>(a, s);
   return hipErrorInvalidValue;
 }
 
-template <int D, bool PAGED>
-hipError_t by_group(int G, int kt, int vt, const AttnArgs& a, hipStream_t s) {
+template <int D, bool PAGED, bool FUSED>
+hipError_t by_group(int G, int kt, int vt, const KernelArgs<FUSED>& a, hipStream_t s) {
   switch (G) {
-    case 1: return by_dtype<D, 1, PAGED>(kt, vt, a, s);
-    case 2: return by_dtype<D, 2, PAGED>(kt, vt, a, s);
-    case 4: return by_dtype<D, 4, PAGED>(kt, vt, a, s);
-    case 8: return by_dtype<D, 8, PAGED>(kt, vt, a, s);
+    case 1: return by_dtype<D, 1, PAGED, FUSED>(kt, vt, a, s);
+    case 2: return by_dtype<D, 2, PAGED, FUSED>(kt, vt, a, s);
+    case 4: return by_dtype<D, 4, PAGED, FUSED>(kt, vt, a, s);
+    case 8: return by_dtype<D, 8, PAGED, FUSED>(kt, vt, a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool PAGED>
-hipError_t dispatch(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a, hipStream_t stream) {
+template <bool PAGED, bool FUSED>
+hipError_t dispatch(int D, int G, int k_dtype, int v_dtype, const KernelArgs<FUSED>& a, hipStream_t stream) {
   switch (D) {
-    case 64: return by_group<64, PAGED>(G, k_dtype, v_dtype, a, stream);
-    case 128: return by_group<128, PAGED>(G, k_dtype, v_dtype, a, stream);
-    case 256: return by_group<256, PAGED>(G, k_dtype, v_dtype, a, stream);
+    case 64: return by_group<64, PAGED, FUSED>(G, k_dtype, v_dtype, a, stream);
+    case 128: return by_group<128, PAGED, FUSED>(G, k_dtype, v_dtype, a, stream);
+    case 256: return by_group<256, PAGED, FUSED>(G, k_dtype, v_dtype, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -7,7 +7,7 @@ namespace uaii {
 
 hipError_t launch_decode_partial_paged(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a,
                                        hipStream_t stream) {
-  return dispatch<true>(D, G, k_dtype, v_dtype, a, stream);
+  return dispatch<true, false>(D, G, k_dtype, v_dtype, a, stream);
 }
 
 }  // namespace uaii

@@ -79,6 +79,18 @@ struct CombineArgs {
   SeqTable t;
 };
 
+// The fused decode step: the producer, the partials and the combine in one
+// launch (see decode_partial_kernel.h).  a.q is unused (the queries are
+// computed in the kernel) and p.pos is unused (the new token of sequence b
+// sits at slot a.t.len[b] - 1).
+struct StepArgs {
+  AttnArgs a;
+  ProduceArgs p;
+  const float* sinks;  // [H] attention-sink logits, or nullptr
+  float* out;
+  int32_t* counters;   // [B][Hkv] arrival counters: zero on entry, zero on exit
+};
+
 hipError_t launch_kv_produce(const ProduceArgs& a, hipStream_t stream);
 // One wave per (work item, kv head): t.work_prefix[t.n_seq] * Hkv waves.
 hipError_t launch_decode_partial(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a,
@@ -86,5 +98,9 @@ hipError_t launch_decode_partial(int D, int G, int k_dtype, int v_dtype, const A
 hipError_t launch_decode_partial_paged(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a,
                                        hipStream_t stream);
 hipError_t launch_decode_combine(int D, int B, const CombineArgs& a, hipStream_t stream);
+// One wave per (work item, kv head), as launch_decode_partial.
+hipError_t launch_decode_step(int D, int G, int k_dtype, int v_dtype, const StepArgs& s, hipStream_t stream);
+hipError_t launch_decode_step_paged(int D, int G, int k_dtype, int v_dtype, const StepArgs& s,
+                                    hipStream_t stream);
 
 }  // namespace uaii

@@ -58,6 +58,9 @@ class DeviceStep:
         self.part_o = torch.empty((Bn, H, self.max_splits, d), dtype=torch.float32, device=device)
         self.part_lse = torch.empty((Bn, H, self.max_splits), dtype=torch.float32, device=device)
         self.out = torch.empty((Bn, H, d), dtype=torch.float32, device=device)
+        # Arrival counters of the single-launch step: zero once, and every
+        # completed step leaves them at zero.
+        self.counters = torch.zeros((Bn, Hkv), dtype=torch.int32, device=device)
 
         self.shape = B.Shape(Bn, H, Hkv, d)
         r = w.rope
@@ -106,6 +109,15 @@ class DeviceStep:
         self.produce()
         self.attn()
         self.combine()
+
+    def fused_step(self):
+        """The same step as one launch (uaii_decode_step)."""
+        B.decode_step(self.shape, self.rope, self.qk_norm, self.q_in.data_ptr(),
+                      self.k_in.data_ptr(), self.v_in.data_ptr(), self.seq_lens, self.cache,
+                      self.scale, self.w.window, self.w.softcap, self.split_size, self.max_splits,
+                      self.sinks.data_ptr() if self.sinks is not None else None,
+                      self.q_out.data_ptr(), self.part_o.data_ptr(), self.part_lse.data_ptr(),
+                      self.counters.data_ptr(), self.out.data_ptr(), self.stream())
 
     # -- host copies for checking ------------------------------------------------
     def host(self, t: torch.Tensor, dtype=None) -> np.ndarray:

@@ -11,6 +11,7 @@
  *   uaii_decode_combine  log-sum-exp combine of the partials
  *   uaii_decode_combine_sink  the same combine with a per-head attention
  *                        sink in the softmax denominator
+ *   uaii_decode_step     all of the above in a single launch
  *
  * Sources (page title, then section):
  *   [UAII]      "Universal AI Inference - Hugging Face decoder completeness"
@@ -267,6 +268,40 @@ uaii_status uaii_decode_combine_sink(const uaii_attn_shape *shape, const int32_t
                                      int32_t window, int32_t split_size, int32_t max_splits,
                                      const float *part_o, const float *part_lse,
                                      const float *sinks, float *out, void *stream);
+
+/* The whole decode step in one launch: uaii_kv_produce at positions
+ * seq_lens[b] - 1, then uaii_decode_attn, then uaii_decode_combine (or
+ * uaii_decode_combine_sink when sinks != NULL), with the same results.
+ * ([ALGENTA] Kernel path capabilities lists a KV-producer-fused decode
+ * partial; here the combine is folded in as well.)  Each wave computes the
+ * rotated queries of its kv head's group itself; the wave whose split holds
+ * the new token's slot stores the new K and V and merges that row from
+ * registers; the last split of each (sequence, kv head) to finish combines
+ * that group's heads.  A step whose keys fit in a few splits costs one
+ * launch instead of three.
+ *   q_in, k_in, v_in, rope, qk_norm   as uaii_kv_produce; the position of
+ *               sequence b is seq_lens[b] - 1
+ *   seq_lens, scale, window, softcap, split_size, max_splits   as
+ *               uaii_decode_attn
+ *   sinks       device [n_heads] f32, or NULL (no sink)
+ *   q_out       device, receives the rotated queries, as uaii_kv_produce
+ *   part_o, part_lse   device, sized as for uaii_decode_attn; they hold the
+ *               split partials afterwards
+ *   counters    device [batch][n_kv_heads] int32 arrival counters: all zero
+ *               before the first call (e.g. from a zero fill), and left at
+ *               zero by every call that completes, so one buffer serves any
+ *               number of consecutive calls.  Calls that share counters,
+ *               partials or cache slots must not run concurrently.
+ *   out         device [batch][n_heads][head_dim] f32 */
+uaii_status uaii_decode_step(const uaii_attn_shape *shape, const uaii_rope *rope,
+                             const uaii_qk_norm *qk_norm, const float *q_in,
+                             const float *k_in, const float *v_in,
+                             const int32_t *seq_lens, const uaii_kv_cache *cache,
+                             float scale, int32_t window, float softcap,
+                             int32_t split_size, int32_t max_splits,
+                             const float *sinks, float *q_out, float *part_o,
+                             float *part_lse, int32_t *counters, float *out,
+                             void *stream);
 
 #ifdef __cplusplus
 }

@@ -140,16 +140,32 @@ def check_slot(w: W.Workload, gpu: dict, ref: dict, q_gpu: np.ndarray, q_ref: np
     return res
 
 
-def run_gpu(inputs, split_size=None, paged=None):
+def run_gpu(inputs, split_size=None, paged=None, fused=False):
     """One step on the GPU with NaN-filled partial buffers (so unwritten
-    entries stay detectable)."""
+    entries stay detectable): the three calls, or with fused=True the
+    single-launch uaii_decode_step, run twice on the same inputs (the
+    second run must reproduce the first bit for bit, which also shows that
+    the arrival counters came back to zero)."""
     import torch
     from gqa_decode_attention_kv_amd.step import DeviceStep
     st = DeviceStep(inputs, split_size=split_size, paged=paged)
     st.part_o.fill_(float("nan"))
     st.part_lse.fill_(float("nan"))
-    st.step()
+    st.out.fill_(float("nan"))
+    if not fused:
+        st.step()
+        torch.cuda.synchronize()
+        return st
+    st.fused_step()
     torch.cuda.synchronize()
+    first = (st.out.clone(), st.q_out.clone())
+    assert int(st.counters.abs().max()) == 0, "arrival counters not returned to zero"
+    st.out.fill_(float("nan"))
+    st.fused_step()
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, first[0]), "second fused step differs from the first"
+    assert torch.equal(st.q_out, first[1])
+    assert int(st.counters.abs().max()) == 0, "arrival counters not returned to zero"
     return st
 
 
@@ -184,12 +200,14 @@ def compare_partials(st, ref, w, lens, pick=None, max_per_seq=None, rng=None):
     return worst
 
 
-def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0, block_size=None):
-    """Run one step on the GPU and in the oracle; compare every output element,
-    the produced cache rows (and that nothing else in the caches changed) and
+def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0, block_size=None,
+                    fused=False):
+    """Run one step on the GPU (three calls, or the single launch with
+    fused=True) and in the oracle; compare every output element, the
+    produced cache rows (and that nothing else in the caches changed) and
     the split partials.  Returns (max abs error, tolerance, class)."""
     lens = np.asarray(lens, dtype=np.int32)
-    say(f"case {w.name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
+    say(f"case {w.name}{' fused' if fused else ''}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
         f"K/V={w.k_dtype}/{w.v_dtype} lens={lens.tolist()[:8]} S={w.split_size} W={w.window} "
         f"cap={w.softcap} rope={w.rope.pairing}/{w.rope.scaling} norm={w.qk_norm.enabled} "
         f"sink={w.sink}")
@@ -205,7 +223,7 @@ def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0, bloc
         vs0, ks0 = inputs.v_scale, inputs.k_scale
     vs0 = vs0.copy() if vs0 is not None else None
     ks0 = ks0.copy() if ks0 is not None else None
-    st = run_gpu(inputs, paged=paged)
+    st = run_gpu(inputs, paged=paged, fused=fused)
     ref = OracleStep(inputs)
     out = st.out.cpu().numpy()
     want = ref.decode().reshape(out.shape)
@@ -231,17 +249,18 @@ def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0, bloc
     return err, tol, cls
 
 
-def check_full_size(w: W.Workload, block_size=None):
+def check_full_size(w: W.Workload, block_size=None, fused=False):
     """A named workload at its full size, in the launch configuration the
     benchmark times: every produced cache row, and a sample of outputs
     (4 heads per sequence; every head for B = 1) and of split partials (the
     first and last valid split of 2 heads per sequence) against the oracle."""
     say(f"full-size {w.name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
         f"cap={w.capacity} S={w.split_size} window={w.window} softcap={w.softcap} "
-        f"K/V={w.k_dtype}/{w.v_dtype} rope={w.rope.scaling} sink={w.sink} paged={block_size}")
+        f"K/V={w.k_dtype}/{w.v_dtype} rope={w.rope.scaling} sink={w.sink} paged={block_size} "
+        f"fused={fused}")
     inputs = W.make_inputs(w)
     paged = W.make_paged(inputs, block_size) if block_size else None
-    st = run_gpu(inputs, paged=paged)
+    st = run_gpu(inputs, paged=paged, fused=fused)
     ref = OracleStep(inputs, copy_cache=False)  # inputs are on the device already
     rng = np.random.default_rng(99)
     H = w.n_heads

@@ -86,6 +86,15 @@ def combine_sink(sh=None, lens=(10, 20), window=0, split=16, max_splits=4, sinks
     B.decode_combine_sink(sh or shape(), lens, window, split, max_splits, FAKE, FAKE, sinks, out, 0)
 
 
+def step(sh=None, rope=None, norm=None, ca=None, lens=(10, 20), scale=None, window=0, softcap=0.0,
+         split=16, max_splits=4, sinks=None, q_out=FAKE, counters=FAKE, out=FAKE):
+    sh = sh or shape()
+    rope = rope or B.Rope(B.ROPE_NEOX, B.ROPE_PLAIN, 1e4, 1.0, 1.0, 4.0, 8192)
+    scale = 1.0 / math.sqrt(sh.head_dim) if scale is None else scale
+    B.decode_step(sh, rope, norm, FAKE, FAKE, FAKE, lens, ca or cache(), scale, window, softcap,
+                  split, max_splits, sinks, q_out, FAKE, FAKE, counters, out, 0)
+
+
 def refused(fn, status, *needles):
     with pytest.raises(B.UaiiError) as ei:
         fn()
@@ -248,3 +257,43 @@ def test_paged_cache_refusals(case):
                   kw.get("num_blocks", 10))
     refused(lambda: attn(ca=c), status, *needles)
     refused(lambda: produce(ca=c, pos=(3, 4)), status, *needles)
+
+
+@host_only
+@pytest.mark.parametrize("case", [
+    ("head_dim 96", lambda: step(sh=shape(d=96)), NI, ["head_dim=96 is not supported"]),
+    ("batch 40", lambda: step(sh=shape(b=40), lens=[1] * 40), NI, ["batch=40"]),
+    ("theta 0", lambda: step(rope=B.Rope(0, 0, 0.0, 1, 1, 4, 8192)), INV, ["rope.theta=0"]),
+    ("scaling 4", lambda: step(rope=B.Rope(0, 4, 1e4, 1, 1, 4, 8192)), NI,
+     ["unsupported rope_scaling.type=4"]),
+    ("norm eps", lambda: step(norm=B.QKNorm(1, 0.0, 0, FAKE, FAKE)), INV, ["qk_norm.eps=0"]),
+    ("scale", lambda: step(scale=0.1), NI, ["scale=0.1"]),
+    ("window", lambda: step(window=-1), INV, ["window=-1"]),
+    ("softcap", lambda: step(softcap=-2.0), INV, ["softcap=-2"]),
+    ("len > cap", lambda: step(lens=(65, 5)), INV, ["seq_lens[0]=65"]),
+    ("len 0", lambda: step(lens=(0, 5)), INV, ["seq_lens[0]=0"]),
+    ("max_splits", lambda: step(lens=(10, 40), split=16, max_splits=2), INV, ["max_splits=2"]),
+    ("q_out null", lambda: step(q_out=None), INV, ["q_out is NULL"]),
+    ("counters null", lambda: step(counters=None), INV, ["counters is NULL"]),
+    ("counters misaligned", lambda: step(counters=FAKE + 2), INV, ["counters", "4-byte aligned"]),
+    ("sinks misaligned", lambda: step(sinks=FAKE + 2), INV, ["sinks", "4-byte aligned"]),
+    ("out null", lambda: step(out=None), INV, ["out is NULL"]),
+    ("vq8 no scale", lambda: step(ca=cache(vd=B.I8)), INV, ["v_scale is NULL"]),
+    ("paged block size", lambda: step(ca=B.KVCache(B.BF16, B.BF16, 64, FAKE, FAKE, None, FAKE, 8,
+                                                   8, 10)), NI, ["block_size=8"]),
+], ids=lambda c: c[0])
+def test_decode_step_refusals(case):
+    _, fn, status, needles = case
+    msg = refused(fn, status, *needles)
+    assert msg.startswith("uaii_decode_step: ")
+
+
+@host_only
+def test_decode_step_valid_call_reaches_the_launch():
+    """A valid single-launch step with and without sinks gets past
+    validation; with no GPU the launch fails with HIP's own text."""
+    for sinks in (None, FAKE):
+        with pytest.raises(B.UaiiError) as ei:
+            step(sinks=sinks)
+        assert ei.value.status == B.ERR_DEVICE
+        assert ei.value.message.startswith("uaii_decode_step: HIP error")

@@ -1,0 +1,110 @@
+"""GPU parity of the single-launch decode step (uaii_decode_step) against the
+CPU oracle, through the C ABI.
+
+uaii_decode_step runs the producer, the split-K partials and the combine in
+one kernel ("Algenta - Model support matrix", Kernel path capabilities: a
+KV-producer-fused decode partial; the combine is folded in as well).  It
+must give what the three calls give, so it is held to the same bar: every
+output element, produced cache row and split partial of the small cases of
+the base path, the variants and the paged layout, and the named workloads
+at full size with sampled outputs.  Each step runs twice, and the second
+run must reproduce the first bit for bit with the arrival counters back at
+zero.  Tolerances are those of the other parity tests.
+"""
+import numpy as np
+import pytest
+
+import parity as P
+import test_gpu_paged as TP
+import test_gpu_parity as TB
+import test_gpu_sweep as TS
+import test_gpu_variants as TV
+from gqa_decode_attention_kv_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gqa_decode_attention_kv_amd import binding
+    binding.load()
+
+
+SMALL = TB.SMALL + TV.SMALL
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[c[0].name for c in SMALL])
+def test_fused_small(spec):
+    w, lens = spec
+    P.run_and_compare(w, lens, fused=True)
+
+
+PAGED = TP.PAGED
+
+
+@pytest.mark.parametrize("spec", PAGED, ids=[c[0].name for c in PAGED])
+def test_fused_paged(spec):
+    w, lens, bs = spec
+    P.run_and_compare(w, lens, max_partials_per_seq=8, seed=1, block_size=bs, fused=True)
+
+
+CELLS = TS.CELLS[::2]
+
+
+@pytest.mark.parametrize("cell", CELLS, ids=[c[0].name for c in CELLS])
+def test_fused_sweep_cell(cell):
+    w, lens = cell
+    P.run_and_compare(w, lens, max_partials_per_seq=6, seed=int(w.seed[0]), fused=True)
+
+
+FULL = ["tiny", "llama3.2-1b", "gpt-oss-20b-sliding", "gemma3-27b-local", "gemma2-local",
+        "qwen3-vq8", W.HEADLINE]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fused_full_size(name):
+    P.check_full_size(W.WORKLOADS[name], fused=True)
+
+
+def test_fused_matches_three_calls():
+    """The single launch and the three calls agree: q_out and the produced
+    cache rows bit for bit, the outputs to f32 rounding (the last split
+    merges the new row in a different order)."""
+    w, lens = TB.SMALL[2]
+    inputs = W.make_inputs(w, seq_lens=lens)
+    a = P.run_gpu(inputs)
+    b = P.run_gpu(inputs, fused=True)
+    assert torch.equal(a.q_out, b.q_out)
+    for k in ("k", "v"):
+        assert np.array_equal(a.cache_rows()[k], b.cache_rows()[k])
+    assert float((a.out - b.out).abs().max()) < 1e-6
+
+
+def test_fused_refusal_writes_nothing():
+    """Invalid calls (no counters; a window below zero) are refused before
+    any launch: outputs, q_out, the cache and the counters are untouched."""
+    from gqa_decode_attention_kv_amd import binding as B
+    w, lens = TB.SMALL[1]
+    inputs = W.make_inputs(w, seq_lens=lens)
+    st = P.run_gpu(inputs, fused=True)
+    before = (st.out.clone(), st.q_out.clone(), st.cache_k.clone(), st.counters.clone())
+    args = dict(shape=st.shape, rope=st.rope, qk_norm=st.qk_norm, q_in=st.q_in.data_ptr(),
+                k_in=st.k_in.data_ptr(), v_in=st.v_in.data_ptr(), seq_lens=st.seq_lens,
+                cache=st.cache, scale=st.scale, window=w.window, softcap=w.softcap,
+                split_size=st.split_size, max_splits=st.max_splits, sinks=None,
+                q_out=st.q_out.data_ptr(), part_o=st.part_o.data_ptr(),
+                part_lse=st.part_lse.data_ptr(), counters=st.counters.data_ptr(),
+                out=st.out.data_ptr(), stream=st.stream())
+    with pytest.raises(B.UaiiError, match="counters"):
+        B.decode_step(**{**args, "counters": None})
+    with pytest.raises(B.UaiiError, match="window"):
+        B.decode_step(**{**args, "window": -1})
+    with pytest.raises(B.UaiiError, match="max_splits"):
+        B.decode_step(**{**args, "max_splits": 1})
+    torch.cuda.synchronize()
+    after = (st.out, st.q_out, st.cache_k, st.counters)
+    for x, y in zip(before, after):
+        assert torch.equal(x, y)
