@@ -331,6 +331,7 @@ uaii_status attn_args(const char* fn, const uaii_attn_shape* shape, const uaii_k
   a.q_mul = softcap > 0.0f ? s : s * log2e;
   a.softcap = softcap;
   build_table(shape->batch, seq_lens, window, split_size, &a.t);
+  a.coop = a.t.work_prefix[shape->batch] * shape->n_kv_heads < uaii::kCoopBelow ? 1 : 0;
   if (cache->block_table != nullptr) {
     a.block_table = cache->block_table;
     a.block_size = cache->block_size;
@@ -419,10 +420,35 @@ uaii_status uaii_decode_step(const uaii_attn_shape* shape, const uaii_rope* rope
   x.counters = counters;
   const int G = shape->n_heads / shape->n_kv_heads;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (cache->block_table != nullptr)
-    return device_status(
-        fn, uaii::launch_decode_step_paged(shape->head_dim, G, cache->k_dtype, cache->v_dtype, x, s));
-  return device_status(fn, uaii::launch_decode_step(shape->head_dim, G, cache->k_dtype, cache->v_dtype, x, s));
+  const int items = x.a.t.work_prefix[shape->batch] * shape->n_kv_heads;
+  if (items <= uaii::kStepOneLaunchMax) {
+    if (cache->block_table != nullptr)
+      return device_status(
+          fn, uaii::launch_decode_step_paged(shape->head_dim, G, cache->k_dtype, cache->v_dtype, x, s));
+    return device_status(fn,
+                         uaii::launch_decode_step(shape->head_dim, G, cache->k_dtype, cache->v_dtype, x, s));
+  }
+  // A large step: the producer, the partials and the combine back to back
+  // on the stream (the kernel boundaries order them; the counters are not
+  // touched and stay zero).
+  for (int b = 0; b < shape->batch; ++b) x.p.pos[b] = seq_lens[b] - 1;
+  st = device_status(fn, uaii::launch_kv_produce(x.p, s));
+  if (st != UAII_OK) return st;
+  st = device_status(fn, cache->block_table != nullptr
+                             ? uaii::launch_decode_partial_paged(shape->head_dim, G, cache->k_dtype,
+                                                                 cache->v_dtype, x.a, s)
+                             : uaii::launch_decode_partial(shape->head_dim, G, cache->k_dtype, cache->v_dtype,
+                                                           x.a, s));
+  if (st != UAII_OK) return st;
+  uaii::CombineArgs c{};
+  c.H = shape->n_heads;
+  c.max_splits = max_splits;
+  c.part_o = part_o;
+  c.part_lse = part_lse;
+  c.sinks = sinks;
+  c.out = out;
+  c.t = x.a.t;
+  return device_status(fn, uaii::launch_decode_combine(shape->head_dim, shape->batch, c, s));
 }
 
 }  // extern "C"

@@ -61,4 +61,61 @@ __device__ inline void combine_row(const float* lse, const float* po, int ns, bo
   for (int e = 0; e < EPL; ++e) out[lane + 64 * e] = num[e] / den;
 }
 
+// combine_row for the NH consecutive query heads of one kv-head group, with
+// the loads of all NH heads issued together (one wave): head j's split
+// log-sum-exps start at lse + j * lse_stride, its partial rows at
+// po + j * po_stride (plus this lane), its output at out + j * D.  sinks is
+// nullptr or points at the NH heads' sink logits.  U splits per head are in
+// flight at once, with NH * U * D/64 registers of partial rows.
+template <int D, int NH>
+__device__ inline void combine_group(const float* lse, int64_t lse_stride, const float* po, int64_t po_stride,
+                                     int ns, const float* sinks, float* out, int lane) {
+  constexpr int EPL = D / 64;
+  constexpr int U0 = 64 / (NH * EPL);
+  constexpr int U = U0 < 1 ? 1 : (U0 > 8 ? 8 : U0);
+  float M[NH], den[NH], num[NH][EPL];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    M[j] = sinks != nullptr ? sinks[j] : -INFINITY;
+    den[j] = sinks != nullptr ? 1.0f : 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) num[j][e] = 0.0f;
+  }
+  for (int s = 0; s < ns; s += U) {
+    float w[NH][U], v[NH][U][EPL];
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int su = min(s + u, ns - 1);
+        w[j][u] = lse[j * lse_stride + su];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[j][u][e] = po[j * po_stride + static_cast<int64_t>(su) * D + 64 * e];
+      }
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      float bm = w[j][0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) bm = fmaxf(bm, w[j][u]);  // clamped duplicates do not change it
+      const float m_new = fmaxf(M[j], bm);
+      const float alpha = (M[j] == -INFINITY) ? 0.0f : expf(M[j] - m_new);
+      den[j] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) num[j][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wu = (s + u < ns) ? expf(w[j][u] - m_new) : 0.0f;
+        den[j] += wu;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) num[j][e] = fmaf(wu, v[j][u][e], num[j][e]);
+      }
+      M[j] = m_new;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NH; ++j)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[j * D + lane + 64 * e] = num[j][e] / den[j];
+}
+
 }  // namespace uaii

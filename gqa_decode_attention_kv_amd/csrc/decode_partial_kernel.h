@@ -240,22 +240,36 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // Work item of this wave: (work index w, kv head); w names (sequence, split).
-  const int item = blockIdx.x * kWaves + wave;
+  // Work item (work index w, kv head); w names (sequence, split).  Alone,
+  // each wave of the work-group takes its own item; cooperatively, the
+  // work-group takes one item and its waves take consecutive quarters of
+  // the split's rows (part = wave), merged through LDS at the end.
+  const bool coop = a.coop != 0;
+  const int item = coop ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) * kWaves + wave;
+  const int part = coop ? wave : 0;
   const int total = a.t.work_prefix[a.t.n_seq] * a.Hkv;
-  if (item >= total) return;  // no barriers below: idle waves leave at once
+  // Idle waves leave at once.  Cooperative work-groups leave as a whole (the
+  // item is per work-group), so the one barrier below is reached by all or
+  // none of a work-group's waves.
+  if (item >= total) return;
   const int kvh = item % a.Hkv;
   const int w = item / a.Hkv;
   int b = 0;
   for (int i = 1; i < a.t.n_seq; ++i) b += (w >= a.t.work_prefix[i]) ? 1 : 0;
   const int sigma = a.t.first_split[b] + (w - a.t.work_prefix[b]);
-  const int r0 = max(sigma * a.split_size, a.t.lo[b]);
   // Cache rows [r0, r1) are read.  The fused step leaves out the new
-  // token's slot L - 1: the wave that holds it (has_new) merges it from
-  // registers after the last chunk.
+  // token's slot L - 1: the split that holds it (has_new) merges it from
+  // registers after its last chunk, in the wave of part 0.
   const int L = a.t.len[b];
   const bool has_new = FUSED && (sigma + 1) * a.split_size >= L;
-  const int r1 = min((sigma + 1) * a.split_size, FUSED ? L - 1 : L);
+  int r0 = max(sigma * a.split_size, a.t.lo[b]);
+  int r1 = min((sigma + 1) * a.split_size, FUSED ? L - 1 : L);
+  if (coop) {  // this wave's quarter, in whole 16-row tiles (possibly empty)
+    const int piece = ((max(r1 - r0, 0) + kWaves - 1) / kWaves + 15) & ~15;
+    r0 = min(r0 + part * piece, r1);
+    r1 = min(r0 + piece, r1);
+  }
+  const bool new_here = has_new && part == 0;
 
   // Contiguous: the (b, kvh) slab starts at row slab of the cache.  Paged:
   // row r lives in physical block block_table[b][r / bs] at offset r % bs.
@@ -280,7 +294,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
     float* qs = sc;  // G rows of D floats: the rotated queries
     pm::Angles<D> an;
     pm::rope_angles<D>(p, pos, lane, an);
-    const bool write_q = sigma == a.t.first_split[b];
+    const bool write_q = sigma == a.t.first_split[b] && part == 0;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int64_t hrow = static_cast<int64_t>(b) * a.H + kvh * G + g;
@@ -306,7 +320,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int e = 0; e < KE; ++e) q[g][e] = qs[g * D + kc * KE + e] * a.q_mul;
-    if (has_new) {
+    if (new_here) {
       const int64_t krow = static_cast<int64_t>(b) * a.Hkv + kvh;
       float kin[EPL], vin[EPL];
 #pragma unroll
@@ -621,7 +635,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
 
   // ---- fused step: merge the new token's row (scores from the prologue) ----
   if constexpr (FUSED) {
-    if (has_new) {
+    if (new_here) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float sl = capped_log2(s_new[g], capped, cap_c, cap_inv);
@@ -655,6 +669,51 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       acc[g][e] = (VT == kI8) ? fmaf(-128.0f, psum[g], x) : x;
     }
   }
+  // ---- cooperative item: part 0 merges the four parts' states -------------
+  if (coop) {
+    // This wave's area of LDS (free after the last chunk) holds its state:
+    // m[G], l[G], then the unnormalised accumulator [G][D].
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        sc[g] = m_run[g];
+        sc[G + g] = l_run[g];
+      }
+    }
+    if (vr == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) sc[2 * G + g * D + vc * VE + e] = acc[g][e];
+    }
+    __syncthreads();
+    if (part != 0) return;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) M = fmaxf(M, smem[q * (kLdsRows * G) + g]);
+      float l = 0.0f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) {
+        const float* st = smem + q * (kLdsRows * G);
+        const float mq = st[g];
+        // an empty part has m = -inf and contributes nothing
+        const float wq = (mq == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mq - M);
+        l = fmaf(wq, st[G + g], l);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(wq, st[2 * G + g * D + vc * VE + e], acc[g][e]);
+      }
+      m_run[g] = M;
+      l_run[g] = l;
+    }
+  }
+
   const int64_t row0 = (static_cast<int64_t>(b) * a.H + kvh * G) * a.max_splits + sigma;
   if (vr == 0) {
 #pragma unroll
@@ -686,14 +745,11 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
     if (ticket != ns - 1) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int s0 = a.t.first_split[b];
-    const bool has_sink = x->sinks != nullptr;
-#pragma unroll 1
-    for (int g = 0; g < G; ++g) {
-      const int h = kvh * G + g;
-      const int64_t crow = (static_cast<int64_t>(b) * a.H + h) * a.max_splits + s0;
-      combine_row<D>(a.part_lse + crow, a.part_o + crow * D + lane, ns, has_sink, has_sink ? x->sinks[h] : 0.0f,
-                     x->out + (static_cast<int64_t>(b) * a.H + h) * D, lane);
-    }
+    const int h0 = kvh * G;
+    const int64_t crow = (static_cast<int64_t>(b) * a.H + h0) * a.max_splits + s0;
+    combine_group<D, G>(a.part_lse + crow, a.max_splits, a.part_o + crow * D + lane,
+                        static_cast<int64_t>(a.max_splits) * D, ns, x->sinks != nullptr ? x->sinks + h0 : nullptr,
+                        x->out + (static_cast<int64_t>(b) * a.H + h0) * D, lane);
     if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -702,7 +758,7 @@ template <int D, int G, int KT, int VT, bool PAGED, bool FUSED>
 hipError_t launch_one(const KernelArgs<FUSED>& args, hipStream_t stream) {
   const AttnArgs& a = attn_of(args);
   const int items = a.t.work_prefix[a.t.n_seq] * a.Hkv;
-  const dim3 grid((items + kWaves - 1) / kWaves);
+  const dim3 grid(a.coop ? items : (items + kWaves - 1) / kWaves);
   hipLaunchKernelGGL((decode_partial_kernel<D, G, KT, VT, PAGED, FUSED>), grid, dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }

@@ -67,8 +67,31 @@ struct AttnArgs {
   // Paged cache only (see ProduceArgs); log2_bs = log2(block_size).
   const int32_t* block_table;
   int32_t block_size, log2_bs, max_blocks, num_blocks;
+  // 0: each wave of a work-group takes its own work item.  1: the four
+  // waves of a work-group share one item, a quarter of its rows each, and
+  // merge their softmax states in LDS (more waves in flight for small steps).
+  int32_t coop;
   SeqTable t;
 };
+
+// Steps with fewer (split, kv head) work items than this run cooperatively:
+// four waves per item keep more loads in flight when the grid alone would
+// leave most of the 1024 SIMDs idle.
+#ifndef UAII_COOP_BELOW
+#define UAII_COOP_BELOW 2048
+#endif
+constexpr int kCoopBelow = UAII_COOP_BELOW;
+
+// uaii_decode_step runs as one kernel up to this many (split, kv head) work
+// items, and as the three kernels back to back above it.  In one kernel,
+// every split's partial must be released at device scope before the last
+// split combines it: on gfx950 that is an L2 write-back per work item,
+// which costs more than two kernel boundaries once there are more than a
+// few hundred items.
+#ifndef UAII_STEP_ONE_LAUNCH_MAX
+#define UAII_STEP_ONE_LAUNCH_MAX 256
+#endif
+constexpr int kStepOneLaunchMax = UAII_STEP_ONE_LAUNCH_MAX;
 
 struct CombineArgs {
   int32_t H, max_splits;

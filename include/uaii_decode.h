@@ -277,8 +277,11 @@ uaii_status uaii_decode_combine_sink(const uaii_attn_shape *shape, const int32_t
  * rotated queries of its kv head's group itself; the wave whose split holds
  * the new token's slot stores the new K and V and merges that row from
  * registers; the last split of each (sequence, kv head) to finish combines
- * that group's heads.  A step whose keys fit in a few splits costs one
- * launch instead of three.
+ * that group's heads.  That costs a device-scope release per split, so only
+ * small steps run this way: up to 256 (split, kv head) work items, i.e.
+ * sum_b (splits of b) * n_kv_heads <= 256.  Larger steps run the producer,
+ * partial and combine kernels back to back on the stream, as the three
+ * calls would.
  *   q_in, k_in, v_in, rope, qk_norm   as uaii_kv_produce; the position of
  *               sequence b is seq_lens[b] - 1
  *   seq_lens, scale, window, softcap, split_size, max_splits   as
