@@ -92,6 +92,7 @@ class Workload:
     split_size: int = 512
     seed: tuple = (0,)
     sink: bool = False         # a per-head attention sink in the combine
+    chunk: int = 0             # prefill: new tokens per sequence (0: a decode step)
 
     @property
     def group(self) -> int:
@@ -185,6 +186,37 @@ WORKLOADS = {
 
 HEADLINE = "llama3.1-8b-b32-ctx8k"
 
+# Prefill (chunk) workloads: `chunk` new tokens per sequence, `lens` keys in
+# total (the chunk included), so lens - chunk tokens are already cached.
+# Prompt lengths 160, 256 and 550 are the throughput battery's canonical
+# prefill shapes on the Algenta page, with the Qwen3-1.7B (grouped-FA d128,
+# QK-norm) and Llama-3.2-1B (d64) shapes it names; the others are a batched
+# Llama-3.1-8B prompt, a chunk appended to an 8K context, and a Gemma-2
+# local layer (window and softcap, d256).
+PREFILL = {
+    "prefill-qwen3-1.7b-p550": Workload("prefill-qwen3-1.7b-p550", 1, 16, 8, 128, ("fixed", 550), 550,
+                                        BF16, BF16, Rope(NEOX, PLAIN, 1000000.0),
+                                        QKNorm(True, 1e-6, 0, 1.0, 0.1), seed=(20,), chunk=550),
+    "prefill-llama3.2-1b-p256": Workload("prefill-llama3.2-1b-p256", 1, 32, 8, 64, ("fixed", 256), 256,
+                                         BF16, BF16,
+                                         Rope(INTERLEAVED, LLAMA3, 500000.0, 32.0, 1.0, 4.0, 8192),
+                                         seed=(21,), chunk=256),
+    "prefill-llama3.1-8b-b8-p2048": Workload("prefill-llama3.1-8b-b8-p2048", 8, 32, 8, 128,
+                                             ("fixed", 2048), 2048, BF16, BF16,
+                                             Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
+                                             seed=(22,), chunk=2048),
+    "prefill-llama3.1-8b-b4-c512-ctx8k": Workload("prefill-llama3.1-8b-b4-c512-ctx8k", 4, 32, 8, 128,
+                                                  ("fixed", 8192), 8192, BF16, BF16,
+                                                  Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0,
+                                                       8192), seed=(23,), chunk=512),
+    "prefill-gemma2-local-b2-c1024": Workload("prefill-gemma2-local-b2-c1024", 2, 16, 8, 256,
+                                              ("fixed", 8192), 8192, BF16, BF16,
+                                              Rope(NEOX, PLAIN, 10000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),
+                                              window=4096, softcap=50.0, seed=(24,), chunk=1024),
+}
+
+PREFILL_HEADLINE = "prefill-llama3.1-8b-b8-p2048"
+
 
 def shrink(w: Workload, **kw) -> Workload:
     """A copy of w with some fields replaced (for small test variants)."""
@@ -222,32 +254,22 @@ def _normal(seed, shape) -> np.ndarray:
     return out
 
 
-def make_inputs(w: Workload, seq_lens=None) -> Inputs:
-    B, H, Hkv, d, cap = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.capacity
-    lens = w.seq_lens() if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
-    if lens.shape != (B,) or lens.min() < 1 or lens.max() > cap:
-        raise ValueError(f"{w.name}: seq_lens must be [{B}] within [1, {cap}]")
+def _fill_caches(w: Workload, lens: np.ndarray, first_new: np.ndarray):
+    """Caches [B][Hkv][cap][d] whose rows [lo_b, first_new[b]) hold seeded
+    values (lo_b: the window start of the token at first_new[b]) and every
+    other row the poison; returns (cache_k, cache_v, v_scale, k_scale)."""
+    B, Hkv, d, cap = w.batch, w.n_kv_heads, w.head_dim, w.capacity
     s = tuple(w.seed)
-    q_in = _normal([*s, 1], (B, H, d))
-    k_in = _normal([*s, 2], (B, Hkv, d))
-    v_in = _normal([*s, 3], (B, Hkv, d))
-    w_q = w_k = None
-    if w.qk_norm.enabled:
-        z = _normal([*s, 4], (2, d))
-        w_q = (w.qk_norm.w_mean + w.qk_norm.w_std * z[0]).astype(np.float32)
-        w_k = (w.qk_norm.w_mean + w.qk_norm.w_std * z[1]).astype(np.float32)
-
     cache_k = np.empty((B, Hkv, cap, d), dtype=STORAGE[w.k_dtype])
     cache_v = np.empty((B, Hkv, cap, d), dtype=STORAGE[w.v_dtype])
     v_scale = np.empty((B, Hkv, cap), dtype=np.float32) if w.v_dtype == I8 else None
     k_scale = np.empty((B, Hkv, cap), dtype=np.float32) if w.k_dtype == I8 else None
-    sinks = (2.0 + 3.0 * _normal([*s, 10], (H,))).astype(np.float32) if w.sink else None
 
     def fill(bu):
         b, u = bu
-        L = int(lens[b])
-        lo, _ = w.visible(L)
-        n = max(0, (L - 1) - lo)          # cached visible rows: [lo, L - 1)
+        first = int(first_new[b])
+        lo, _ = w.visible(first + 1)
+        n = max(0, first - lo)            # cached visible rows: [lo, first)
         for arr, dt in ((cache_k, w.k_dtype), (cache_v, w.v_dtype)):
             slab = arr[b, u]
             if dt == F32:
@@ -291,8 +313,84 @@ def make_inputs(w: Workload, seq_lens=None) -> Inputs:
     jobs = [(b, u) for b in range(B) for u in range(Hkv)]
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(fill, jobs))
+    return cache_k, cache_v, v_scale, k_scale
+
+
+def make_inputs(w: Workload, seq_lens=None) -> Inputs:
+    B, H, Hkv, d, cap = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.capacity
+    lens = w.seq_lens() if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
+    if lens.shape != (B,) or lens.min() < 1 or lens.max() > cap:
+        raise ValueError(f"{w.name}: seq_lens must be [{B}] within [1, {cap}]")
+    s = tuple(w.seed)
+    q_in = _normal([*s, 1], (B, H, d))
+    k_in = _normal([*s, 2], (B, Hkv, d))
+    v_in = _normal([*s, 3], (B, Hkv, d))
+    w_q = w_k = None
+    if w.qk_norm.enabled:
+        z = _normal([*s, 4], (2, d))
+        w_q = (w.qk_norm.w_mean + w.qk_norm.w_std * z[0]).astype(np.float32)
+        w_k = (w.qk_norm.w_mean + w.qk_norm.w_std * z[1]).astype(np.float32)
+
+    sinks = (2.0 + 3.0 * _normal([*s, 10], (H,))).astype(np.float32) if w.sink else None
+    cache_k, cache_v, v_scale, k_scale = _fill_caches(w, lens, (lens - 1).astype(np.int64))
     return Inputs(w, lens, (lens - 1).astype(np.int32), q_in, k_in, v_in, w_q, w_k,
                   cache_k, cache_v, v_scale, k_scale, sinks)
+
+
+@dataclass
+class PrefillInputs:
+    workload: Workload
+    seq_lens: np.ndarray      # [B] int32, keys incl. the chunk
+    start: np.ndarray         # [B] int32, position of the chunk's first token = L_b - T
+    q_in: np.ndarray          # [B][T][H][d] f32
+    k_in: np.ndarray          # [B][T][Hkv][d] f32
+    v_in: np.ndarray          # [B][T][Hkv][d] f32
+    w_q: np.ndarray | None
+    w_k: np.ndarray | None
+    cache_k: np.ndarray       # [B][Hkv][cap][d]
+    cache_v: np.ndarray
+    v_scale: np.ndarray | None
+    k_scale: np.ndarray | None = None
+    sinks: np.ndarray | None = None
+
+
+def make_prefill_inputs(w: Workload, seq_lens=None) -> PrefillInputs:
+    """Inputs of one chunk step: T = w.chunk new tokens per sequence (streams
+    1-3 drawn as [B][T][...]), cached rows [lo, L - T) seeded as for a decode
+    step (lo: the window start of the chunk's first token), the chunk's slots
+    and every other row poisoned."""
+    B, H, Hkv, d, cap, T = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.capacity, w.chunk
+    if T < 1:
+        raise ValueError(f"{w.name}: not a prefill workload (chunk={T})")
+    lens = w.seq_lens() if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
+    if lens.shape != (B,) or lens.min() < T or lens.max() > cap:
+        raise ValueError(f"{w.name}: seq_lens must be [{B}] within [{T}, {cap}]")
+    s = tuple(w.seed)
+    q_in = _normal([*s, 1], (B, T, H, d))
+    k_in = _normal([*s, 2], (B, T, Hkv, d))
+    v_in = _normal([*s, 3], (B, T, Hkv, d))
+    w_q = w_k = None
+    if w.qk_norm.enabled:
+        z = _normal([*s, 4], (2, d))
+        w_q = (w.qk_norm.w_mean + w.qk_norm.w_std * z[0]).astype(np.float32)
+        w_k = (w.qk_norm.w_mean + w.qk_norm.w_std * z[1]).astype(np.float32)
+    sinks = (2.0 + 3.0 * _normal([*s, 10], (H,))).astype(np.float32) if w.sink else None
+    start = (lens - T).astype(np.int32)
+    cache_k, cache_v, v_scale, k_scale = _fill_caches(w, lens, start.astype(np.int64))
+    return PrefillInputs(w, lens, start, q_in, k_in, v_in, w_q, w_k, cache_k, cache_v, v_scale,
+                         k_scale, sinks)
+
+
+def prefill_flops(w: Workload, seq_lens=None) -> int:
+    """Algorithmic flops of a chunk's attention: 4 d per (query head, visible
+    key) for the score and the weighted sum."""
+    lens = w.seq_lens() if seq_lens is None else np.asarray(seq_lens)
+    T, total = w.chunk, 0
+    for L in lens:
+        p = np.arange(int(L) - T, int(L), dtype=np.int64)   # positions of the chunk
+        lo = np.maximum(0, p + 1 - w.window) if w.window > 0 else np.zeros_like(p)
+        total += int(np.sum(p + 1 - lo))
+    return 4 * w.head_dim * w.n_heads * total
 
 
 @dataclass
@@ -316,7 +414,7 @@ def _poison_like(dtype) -> object:
             np.dtype(np.int8): np.int8(0)}[np.dtype(dtype)]
 
 
-def make_paged(inputs: Inputs, block_size: int, spare_blocks: int = 3) -> PagedInputs:
+def make_paged(inputs, block_size: int, spare_blocks: int = 3) -> PagedInputs:
     """Scatter the contiguous caches of ``inputs`` into block pools."""
     w = inputs.workload
     B, Hkv, d, cap = w.batch, w.n_kv_heads, w.head_dim, w.capacity

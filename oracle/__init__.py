@@ -256,6 +256,64 @@ class Oracle:
         return out, int(used)
 
 
+    # -- chunks of new tokens (prefill) ---------------------------------------
+    def kv_produce_chunk(self, *, rope: dict, norm: dict | None, q_in, k_in, v_in,
+                         start_positions, k_dtype: int, v_dtype: int, cache_k, cache_v,
+                         v_scale=None, k_scale=None):
+        """The producer for T new tokens per sequence ("Universal AI Inference"
+        P1.3: every token is rotated at its own absolute position and stored at
+        that slot): token t of sequence b is produced exactly as a single-token
+        producer produces it at position start_positions[b] + t.  q_in is
+        [B][T][H][d], k_in and v_in [B][T][Hkv][d]; returns q' [B][T][H][d]
+        (double) and writes the T slots of every (b, kv head) in place."""
+        B, T, H, d = q_in.shape
+        start = np.asarray(start_positions, dtype=np.int64)
+        q_out = np.zeros((B, T, H, d), dtype=np.float64)
+        for t in range(T):
+            q_out[:, t] = self.kv_produce(
+                rope=rope, norm=norm, q_in=np.ascontiguousarray(q_in[:, t]),
+                k_in=np.ascontiguousarray(k_in[:, t]), v_in=np.ascontiguousarray(v_in[:, t]),
+                positions=(start + t).astype(np.int32), k_dtype=k_dtype, v_dtype=v_dtype,
+                cache_k=cache_k, cache_v=cache_v, v_scale=v_scale, k_scale=k_scale)
+        return q_out
+
+    def prefill(self, *, q, cache_k, cache_v, v_scale=None, k_dtype, v_dtype, seq_lens,
+                window=0, softcap=0.0, sinks=None, k_scale=None, triples=None):
+        """Causal attention of a chunk: the T queries of sequence b sit at
+        positions L_b - T .. L_b - 1 and query t sees the keys up to its own
+        position, within its own window ("Universal AI Inference" P1.3 and
+        P1.4).  That is decode attention of query t over the first
+        L_b - T + t + 1 keys, which is what this computes.  q is
+        [B][T][H][d]; returns [B][T][H][d] double, or [n][d] for a list of
+        (b, t, h) triples."""
+        B, T, H, d = q.shape
+        lens = np.asarray(seq_lens, dtype=np.int64)
+
+        def prefix(t):  # keys that query t may see: positions 0 .. L - T + t
+            return (lens - T + t + 1).astype(np.int32)
+
+        if triples is None:
+            out = np.zeros((B, T, H, d), dtype=np.float64)
+            for t in range(T):
+                out[:, t] = self.decode(q=np.ascontiguousarray(q[:, t]), cache_k=cache_k,
+                                        cache_v=cache_v, v_scale=v_scale, k_scale=k_scale,
+                                        k_dtype=k_dtype, v_dtype=v_dtype,
+                                        seq_lens=prefix(t), window=window, softcap=softcap,
+                                        sinks=sinks)
+            return out
+        tr = np.asarray(triples, dtype=np.int64).reshape(-1, 3)
+        out = np.zeros((len(tr), d), dtype=np.float64)
+        for t in np.unique(tr[:, 1]):
+            sel = np.nonzero(tr[:, 1] == t)[0]
+            pairs = tr[sel][:, [0, 2]]
+            out[sel] = self.decode(q=np.ascontiguousarray(q[:, t]), cache_k=cache_k,
+                                   cache_v=cache_v, v_scale=v_scale, k_scale=k_scale,
+                                   k_dtype=k_dtype, v_dtype=v_dtype,
+                                   seq_lens=prefix(t), window=window, softcap=softcap,
+                                   sinks=sinks, pairs=pairs)
+        return out
+
+
 _default: Oracle | None = None
 
 

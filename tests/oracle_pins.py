@@ -890,4 +890,124 @@ def pin_produce_q8_keys(o):
     assert np.count_nonzero(k8) == np.count_nonzero(k8[np.arange(B), :, pos])
 
 
+# ---------------------------------------------------------------------------
+# Chunks of new tokens (prefill): ALGENTA Kernel path capabilities (grouped-FA
+# prefill); UAII P1.3 (positions follow the absolute KV index), P1.4 (window,
+# softcap)
+# ---------------------------------------------------------------------------
+
+def _prefill_matrix(q, K, V, lens, T, G, window, softcap, sinks):
+    """Causal attention of a chunk in matrix form (numpy, float64): one
+    masked score matrix per (sequence, head), a row-wise softmax with the
+    sink as an extra column carrying no value, then P V."""
+    B, _, H, d = q.shape
+    out = np.zeros(q.shape)
+    for b in range(B):
+        L = int(lens[b])
+        pos = np.arange(L - T, L)
+        lo = np.maximum(0, pos + 1 - window) if window > 0 else np.zeros(T, np.int64)
+        j = np.arange(L)
+        mask = (j[None, :] <= pos[:, None]) & (j[None, :] >= lo[:, None])
+        for h in range(H):
+            Kb = K[b, h // G, :L].astype(np.float64)
+            Vb = V[b, h // G, :L].astype(np.float64)
+            S = q[b, :, h].astype(np.float64) @ Kb.T / math.sqrt(d)
+            if softcap > 0:
+                S = softcap * np.tanh(S / softcap)
+            S = np.where(mask, S, -np.inf)
+            if sinks is not None:
+                S = np.concatenate([S, np.full((T, 1), float(sinks[h]))], axis=1)
+                Vx = np.concatenate([Vb, np.zeros((1, d))], axis=0)
+            else:
+                Vx = Vb
+            m = S.max(axis=1, keepdims=True)
+            P = np.exp(S - m)
+            out[b, :, h] = (P / P.sum(axis=1, keepdims=True)) @ Vx
+    return out
+
+
+def pin_prefill_matrix_form(o):
+    """The chunk's causal attention equals the masked matrix form: query t of
+    a chunk of T at the end of L keys sees keys lo_t .. L - T + t, for empty
+    and non-empty caches, with window, softcap and sink."""
+    B, T, H, Hkv, d, cap = 2, 5, 4, 2, 8, 12
+    rng = _rng(91)
+    K, V = _cache(B, Hkv, cap, d, 92)
+    q = rng.standard_normal((B, T, H, d))
+    lens = np.array([9, 5], np.int32)        # 4 cached tokens + 5; an empty cache + 5
+    sinks = rng.standard_normal(H)
+    for window in (0, 3, 1):
+        for softcap in (0.0, 1.5):
+            for sk in (None, sinks):
+                got = o.prefill(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32,
+                                seq_lens=lens, window=window, softcap=softcap, sinks=sk)
+                want = _prefill_matrix(q, K, V, lens, T, H // Hkv, window, softcap, sk)
+                assert np.allclose(got, want, rtol=0, atol=1e-12), (window, softcap, sk is None)
+
+
+def pin_prefill_causal(o):
+    """Query t never reads a key after its own position: poisoning every
+    later cache row leaves its output unchanged (and finite)."""
+    B, T, H, Hkv, d, cap = 1, 6, 2, 1, 16, 10
+    rng = _rng(93)
+    K, V = _cache(B, Hkv, cap, d, 94)
+    q = rng.standard_normal((B, T, H, d))
+    lens = np.array([10], np.int32)
+    full = o.prefill(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens)
+    for t in range(T):
+        p = 10 - T + t
+        Kp, Vp = K.copy(), V.copy()
+        Kp[:, :, p + 1:] = np.nan
+        Vp[:, :, p + 1:] = np.nan
+        got = o.prefill(q=q, cache_k=Kp, cache_v=Vp, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens,
+                        triples=[(0, t, h) for h in range(H)])
+        assert np.all(np.isfinite(got)) and np.array_equal(got, full[0, t]), t
+
+
+def pin_prefill_last_token_is_decode(o):
+    """The chunk's last query sees exactly what a decode step at L keys sees
+    (it is the newest token), for any chunk length."""
+    B, H, Hkv, d, cap = 2, 4, 2, 16, 20
+    rng = _rng(95)
+    K, V = _cache(B, Hkv, cap, d, 96)
+    lens = np.array([20, 13], np.int32)
+    for T in (1, 4, 13):
+        q = rng.standard_normal((B, T, H, d))
+        got = o.prefill(q=q, cache_k=K, cache_v=V, k_dtype=O.F32, v_dtype=O.F32, seq_lens=lens,
+                        window=6, softcap=2.0)
+        want = o.decode(q=np.ascontiguousarray(q[:, -1]), cache_k=K, cache_v=V, k_dtype=O.F32,
+                        v_dtype=O.F32, seq_lens=lens, window=6, softcap=2.0)
+        assert np.array_equal(got[:, -1], want), T
+
+
+def pin_chunk_producer(o):
+    """The chunk producer writes exactly the T slots start .. start + T - 1 of
+    every (b, kv head), and its token t is the single-token producer at
+    position start + t (here: with the tokens produced in reverse order)."""
+    B, T, H, Hkv, d, cap = 2, 4, 4, 2, 32, 12
+    rng = _rng(97)
+    qi = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    ki = rng.standard_normal((B, T, Hkv, d)).astype(np.float32)
+    vi = rng.standard_normal((B, T, Hkv, d)).astype(np.float32)
+    start = np.array([0, 8], np.int32)
+    rope = dict(pairing=O.INTERLEAVED, scaling=O.LLAMA3, theta=5e5, factor=8.0)
+    ck = np.full((B, Hkv, cap, d), 0x5555, np.uint16)
+    cv = np.full((B, Hkv, cap, d), 0x5555, np.uint16)
+    q = o.kv_produce_chunk(rope=rope, norm=None, q_in=qi, k_in=ki, v_in=vi, start_positions=start,
+                           k_dtype=O.BF16, v_dtype=O.BF16, cache_k=ck, cache_v=cv)
+    written = np.zeros((B, Hkv, cap), bool)
+    for b in range(B):
+        written[b, :, start[b]:start[b] + T] = True
+    assert np.all(ck[~written] == 0x5555) and np.all(cv[~written] == 0x5555)
+    ck2 = np.full_like(ck, 0x5555)
+    cv2 = np.full_like(cv, 0x5555)
+    for t in reversed(range(T)):
+        q2 = o.kv_produce(rope=rope, norm=None, q_in=np.ascontiguousarray(qi[:, t]),
+                          k_in=np.ascontiguousarray(ki[:, t]), v_in=np.ascontiguousarray(vi[:, t]),
+                          positions=start + t, k_dtype=O.BF16, v_dtype=O.BF16, cache_k=ck2,
+                          cache_v=cv2)
+        assert np.array_equal(q2, q[:, t]), t
+    assert np.array_equal(ck, ck2) and np.array_equal(cv, cv2)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

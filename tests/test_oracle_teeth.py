@@ -83,3 +83,51 @@ def test_mutant_fails_a_pin(tmp_path, name, old, new):
             failed.append(pin.__name__)
             break
     assert failed, f"mutant {name} passes every pin"
+
+
+# Mistakes planted in the Python layer of the oracle (the chunk functions),
+# by the same textual mutation, in a copy of the package loaded under
+# another name.
+PY_SRC = open(os.path.join(os.path.dirname(obuild.SOURCE), "__init__.py")).read()
+PY_MUTANTS = [
+    ("prefill_excludes_own_key", "return (lens - T + t + 1).astype(np.int32)",
+     "return (lens - T + t).astype(np.int32)"),
+    ("prefill_sees_next_key", "return (lens - T + t + 1).astype(np.int32)",
+     "return np.minimum(lens, lens - T + t + 2).astype(np.int32)"),
+    ("prefill_not_causal", "return (lens - T + t + 1).astype(np.int32)",
+     "return lens.astype(np.int32)"),
+    ("chunk_position_shifted", "positions=(start + t).astype(np.int32)",
+     "positions=(start + t + 1).astype(np.int32)"),
+    ("chunk_position_of_first_token", "positions=(start + t).astype(np.int32)",
+     "positions=start.astype(np.int32)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_python_mutant_fails_a_pin(tmp_path, name, old, new):
+    import importlib.util
+    import shutil
+    import sys
+    assert PY_SRC.count(old) == 1, f"{name}: anchor text not found exactly once"
+    pkg = tmp_path / f"oracle_{name}"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text(PY_SRC.replace(old, new))
+    shutil.copy(os.path.join(os.path.dirname(obuild.SOURCE), "build.py"), pkg / "build.py")
+    modname = f"oracle_{name}"
+    spec = importlib.util.spec_from_file_location(modname, pkg / "__init__.py",
+                                                  submodule_search_locations=[str(pkg)])
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[modname] = mod
+    try:
+        spec.loader.exec_module(mod)
+        mutant = mod.Oracle(oracle.load().path)
+        failed = []
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin(mutant)
+            except (AssertionError, ValueError, FloatingPointError, OverflowError):
+                failed.append(pin.__name__)
+                break
+        assert failed, f"mutant {name} passes every pin"
+    finally:
+        sys.modules.pop(modname, None)
