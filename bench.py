@@ -116,6 +116,133 @@ def cpu_baseline(inputs, min_seconds: float = 10.0, max_rounds: int = 8) -> dict
             "seq_steps_per_s": round(seqs_done / elapsed, 3)}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_cpu_baseline(inputs, q, min_seconds: float = 10.0) -> dict:
+    """Time the oracle's chunk attention on a bounded sample of (sequence,
+    token, head) queries of the workload, on this host's cores."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    w = inputs.workload
+    o = oracle.load()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+    rng = np.random.default_rng(5)
+    T, lens = w.chunk, inputs.seq_lens
+    flops, elapsed, n = 0, 0.0, 0
+    while elapsed < min_seconds and n < 64 * threads:
+        tr = [(int(rng.integers(w.batch)), int(rng.integers(T)), int(rng.integers(w.n_heads)))
+              for _ in range(threads)]
+
+        def one(x):
+            o.prefill(q=q, cache_k=inputs.cache_k, cache_v=inputs.cache_v, k_dtype=w.k_dtype,
+                      v_dtype=w.v_dtype, seq_lens=lens, window=w.window, softcap=w.softcap,
+                      sinks=inputs.sinks, triples=[x])
+
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, tr))
+        elapsed += time.perf_counter() - t0
+        for b, t, _ in tr:
+            p = int(lens[b]) - T + t
+            lo = max(0, p + 1 - w.window) if w.window > 0 else 0
+            flops += 4 * w.head_dim * (p + 1 - lo)
+        n += len(tr)
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{n} (sequence, token, head) queries of {w.name}, each its double-precision "
+                       f"attention over its causal prefix, {elapsed:.1f} s wall on {threads} threads")}
+
+
+def prefill_main(args) -> int:
+    """One JSON line for a chunk (prefill) workload: the chunk producer plus
+    the chunk's causal attention per step; roofline of the attention kernel
+    against the bf16 matrix-core peak."""
+    import numpy as np
+    import torch
+
+    from gqa_decode_attention_kv_amd import workloads as W
+    from gqa_decode_attention_kv_amd.step import DevicePrefill
+
+    name = args.prefill
+    w = W.PREFILL[name]
+    inputs = W.make_prefill_inputs(w)
+    st = DevicePrefill(inputs)
+    flops = W.prefill_flops(w, inputs.seq_lens)
+    t_w, n_w = time.perf_counter(), 0
+    while n_w < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
+        st.step()
+        n_w += 1
+        if n_w % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    K = args.steps
+    EVERY = 5
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range((K + EVERY - 1) // EVERY)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        st.produce()
+        if i % EVERY == 0:
+            ev[i // EVERY][0].record()
+            st.attn()
+            ev[i // EVERY][1].record()
+        else:
+            st.attn()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / K
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    assert torch.isfinite(st.out).all().item(), "non-finite output"
+    tflops_step = flops / (ms_step * 1e-3) / 1e12
+    tflops_attn = flops / (attn_ms * 1e-3) / 1e12
+    tokens = w.batch * w.chunk
+    result = {
+        "metric": "prefill chunk attention TFLOP/s (algorithmic) and tokens/s",
+        "value": round(tflops_step, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": n_w, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "batch": w.batch, "chunk": w.chunk,
+                   "ctx": int(inputs.seq_lens.max()), "n_heads": w.n_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "kv_cache": "bf16/bf16",
+                   "window": w.window, "softcap": w.softcap, "parallelism": "single-gpu"},
+        "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "flops_per_step": flops,
+        "attn_ms": round(attn_ms, 5),
+        "roofline": {"kernel": "prefill_attn_kernel", "bound": "mfma",
+                     "achieved": round(tflops_attn, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops_attn / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "note": "the kernel issues twice the algorithmic matrix flops (q and the "
+                             "softmax weights enter as a bf16 high part and remainder)"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        o = oracle.load()
+        ck, cv = inputs.cache_k.copy(), inputs.cache_v.copy()
+        norm = None
+        if w.qk_norm.enabled:
+            norm = dict(enabled=True, eps=w.qk_norm.eps, offset=w.qk_norm.offset,
+                        w_q=inputs.w_q, w_k=inputs.w_k)
+        q = o.kv_produce_chunk(rope=w.rope.as_dict(), norm=norm, q_in=inputs.q_in,
+                               k_in=inputs.k_in, v_in=inputs.v_in, start_positions=inputs.start,
+                               k_dtype=w.k_dtype, v_dtype=w.v_dtype, cache_k=ck, cache_v=cv)
+        inputs.cache_k, inputs.cache_v = ck, cv
+        result["cpu_baseline"] = prefill_cpu_baseline(inputs, q)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +256,8 @@ def main() -> int:
                     help="use the paged cache layout with this block size (0: contiguous)")
     ap.add_argument("--fused", action="store_true",
                     help="run the step as one launch (uaii_decode_step) instead of three calls")
+    ap.add_argument("--prefill", default=None, metavar="WORKLOAD",
+                    help="time a chunk (prefill) workload instead of the decode step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -148,6 +277,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.prefill:
+        return prefill_main(args)
     name = args.workload or W.HEADLINE
     w = W.WORKLOADS[name]
     t_gen = time.perf_counter()

@@ -287,6 +287,7 @@ uaii_status produce_args(const char* fn, const uaii_attn_shape* shape, const uai
   a.block_size = cache->block_table ? cache->block_size : 0;
   a.max_blocks = cache->block_table ? cache->max_blocks : 0;
   a.num_blocks = cache->block_table ? cache->num_blocks : 0;
+  a.T = 1;
   *out = a;
   return UAII_OK;
 }
@@ -393,6 +394,98 @@ uaii_status uaii_decode_attn(const uaii_attn_shape* shape, const uaii_kv_cache* 
         fn, uaii::launch_decode_partial_paged(shape->head_dim, G, cache->k_dtype, cache->v_dtype, a, s));
   return device_status(fn,
                        uaii::launch_decode_partial(shape->head_dim, G, cache->k_dtype, cache->v_dtype, a, s));
+}
+
+uaii_status uaii_kv_produce_chunk(const uaii_attn_shape* shape, const uaii_rope* rope,
+                                  const uaii_qk_norm* qk_norm, const float* q_in, const float* k_in,
+                                  const float* v_in, const int32_t* start_positions, int32_t n_tokens,
+                                  const uaii_kv_cache* cache, float* q_out, void* stream) {
+  const char* fn = "uaii_kv_produce_chunk";
+  g_error.clear();
+  uaii_status st = check_shape(fn, shape);
+  if (st != UAII_OK) return st;
+  st = check_cache(fn, cache);
+  if (st != UAII_OK) return st;
+  uaii::ProduceArgs a{};
+  st = produce_args(fn, shape, rope, qk_norm, q_in, k_in, v_in, cache, q_out, &a);
+  if (st != UAII_OK) return st;
+  REQUIRE(n_tokens >= 1, kInvalid, "n_tokens=%d is invalid (must be >= 1)", n_tokens);
+  REQUIRE(n_tokens <= 65535, kNotImpl, "n_tokens=%d is not supported (supported: 1..65535 per call)",
+          n_tokens);
+  REQUIRE(start_positions != nullptr, kInvalid,
+          "start_positions is NULL; pass a host array of batch=%d positions", shape->batch);
+  for (int b = 0; b < shape->batch; ++b)
+    REQUIRE(start_positions[b] >= 0 &&
+                static_cast<int64_t>(start_positions[b]) + n_tokens <= cache->capacity,
+            kInvalid, "start_positions[%d]=%d with n_tokens=%d is outside [0, capacity=%d]", b,
+            start_positions[b], n_tokens, cache->capacity);
+  a.T = n_tokens;
+  for (int b = 0; b < shape->batch; ++b) a.pos[b] = start_positions[b];
+  return device_status(fn, uaii::launch_kv_produce(a, static_cast<hipStream_t>(stream)));
+}
+
+uaii_status uaii_prefill_attn(const uaii_attn_shape* shape, const uaii_kv_cache* cache, const float* q,
+                              const int32_t* seq_lens, int32_t n_tokens, float scale, int32_t window,
+                              float softcap, const float* sinks, float* out, void* stream) {
+  const char* fn = "uaii_prefill_attn";
+  g_error.clear();
+  uaii_status st = check_shape(fn, shape);
+  if (st != UAII_OK) return st;
+  st = check_cache(fn, cache);
+  if (st != UAII_OK) return st;
+  REQUIRE(cache->k_dtype == UAII_BF16 && cache->v_dtype == UAII_BF16, kNotImpl,
+          "prefill over k_dtype=%d, v_dtype=%d is not supported (supported: bf16 keys and values, "
+          "k_dtype=v_dtype=1)",
+          cache->k_dtype, cache->v_dtype);
+  REQUIRE(n_tokens >= 1, kInvalid, "n_tokens=%d is invalid (must be >= 1)", n_tokens);
+  REQUIRE(n_tokens <= (1 << 20), kNotImpl, "n_tokens=%d is not supported (supported: 1..%d per call)",
+          n_tokens, 1 << 20);
+  REQUIRE(seq_lens != nullptr, kInvalid, "seq_lens is NULL; pass a host array of batch=%d lengths",
+          shape->batch);
+  REQUIRE(window >= 0, kInvalid, "window=%d is invalid (0 = no window, W > 0 keeps the last W keys)",
+          window);
+  for (int b = 0; b < shape->batch; ++b)
+    REQUIRE(seq_lens[b] >= n_tokens && seq_lens[b] <= cache->capacity, kInvalid,
+            "seq_lens[%d]=%d is outside [n_tokens=%d, capacity=%d] (keys including the chunk)", b,
+            seq_lens[b], n_tokens, cache->capacity);
+  REQUIRE(std::isfinite(softcap) && softcap >= 0.0f, kInvalid,
+          "softcap=%g is invalid (0 = none, c > 0 applies c*tanh(s/c))", static_cast<double>(softcap));
+  REQUIRE(std::isfinite(scale), kInvalid, "scale=%g is invalid (must be finite)", static_cast<double>(scale));
+  const double want = 1.0 / std::sqrt(static_cast<double>(shape->head_dim));
+  REQUIRE(std::fabs(static_cast<double>(scale) - want) <= 1e-6 * want, kNotImpl,
+          "scale=%.9g is not supported (supported: 1/sqrt(head_dim)=%.9g; a differing "
+          "query_pre_attn_scalar is refused)",
+          static_cast<double>(scale), want);
+  CHECK_PTR("q", q, 16);
+  CHECK_PTR("out", out, 16);
+  if (sinks != nullptr) CHECK_PTR("sinks", sinks, 4);
+
+  uaii::PrefillArgs a{};
+  a.H = shape->n_heads;
+  a.Hkv = shape->n_kv_heads;
+  a.cap = cache->capacity;
+  a.T = n_tokens;
+  a.window = window;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.q = q;
+  a.sinks = sinks;
+  a.out = out;
+  const float s = static_cast<float>(want);
+  a.q_mul = softcap > 0.0f ? s : s * 1.4426950408889634f;
+  a.softcap = softcap;
+  if (cache->block_table != nullptr) {
+    a.block_table = cache->block_table;
+    a.block_size = cache->block_size;
+    a.log2_bs = 0;
+    while ((1 << a.log2_bs) < cache->block_size) ++a.log2_bs;
+    a.max_blocks = cache->max_blocks;
+    a.num_blocks = cache->num_blocks;
+  }
+  for (int b = 0; b < shape->batch; ++b) a.len[b] = seq_lens[b];
+  const int G = shape->n_heads / shape->n_kv_heads;
+  return device_status(fn, uaii::launch_prefill_attn(shape->head_dim, G, shape->batch, a,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 uaii_status uaii_decode_step(const uaii_attn_shape* shape, const uaii_rope* rope, const uaii_qk_norm* qk_norm,

@@ -9,7 +9,8 @@
 // families: linear scaling); "FreeToken PR #722" (Changes: Llama-3 scaling
 // constants).
 //
-// The work is O(B * (H + Hkv) * d): one 64-lane wave per head vector.  The
+// The work is O(B * T * (H + Hkv) * d): one 64-lane wave per head vector of
+// each of the T tokens of each sequence (T = 1 for a decode step).  The
 // per-vector math lives in producer_math.h (shared with the fused step): the
 // norm and the rotation run in double precision and round once to the
 // stored format, so the stored key matches a double-precision definition to
@@ -30,18 +31,19 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
   const int lane = threadIdx.x;
   const int x = blockIdx.x;
   const int b = blockIdx.y;
-  const int pos = a.pos[b];
+  const int t = blockIdx.z;  // token of the chunk
+  const int pos = a.pos[b] + t;
+  const int64_t bt = static_cast<int64_t>(b) * a.T + t;
   const bool is_q = x < a.H;
   const int u = x - a.H;
 
   // Loads first; the data-independent angles below overlap with them.
-  const float* src = is_q ? a.q_in + (static_cast<int64_t>(b) * a.H + x) * D
-                          : a.k_in + (static_cast<int64_t>(b) * a.Hkv + u) * D;
+  const float* src = is_q ? a.q_in + (bt * a.H + x) * D : a.k_in + (bt * a.Hkv + u) * D;
   float xin[EPL], v[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) xin[e] = src[lane + 64 * e];
   if (!is_q) {
-    const float* vsrc = a.v_in + (static_cast<int64_t>(b) * a.Hkv + u) * D;
+    const float* vsrc = a.v_in + (bt * a.Hkv + u) * D;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) v[e] = vsrc[lane + 64 * e];
   }
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
   pm::norm_rope<D>(a, xin, is_q ? a.w_q : a.w_k, an, sx, lane, r);
 
   if (is_q) {
-    float* q = a.q_out + (static_cast<int64_t>(b) * a.H + x) * D;
+    float* q = a.q_out + (bt * a.H + x) * D;
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       if (!r.ok[j]) continue;
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
 }  // namespace
 
 hipError_t launch_kv_produce(const ProduceArgs& a, hipStream_t stream) {
-  const dim3 grid(a.H + a.Hkv, a.B);
+  const dim3 grid(a.H + a.Hkv, a.B, a.T);
   switch (a.D) {
     case 64: hipLaunchKernelGGL(kv_produce_kernel<64>, grid, dim3(64), 0, stream, a); break;
     case 128: hipLaunchKernelGGL(kv_produce_kernel<128>, grid, dim3(64), 0, stream, a); break;

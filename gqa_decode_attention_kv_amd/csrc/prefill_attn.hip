@@ -1,0 +1,291 @@
+// Chunk attention (prefill) for grouped-query attention on the matrix cores.
+//
+// Sources: "Algenta - Model support matrix" (Kernel path capabilities: a
+// grouped-FA prefill for d128 and d64 and a parametric prefill for
+// power-of-two head dims; Structural fact requirements: GQA ratio,
+// attention scale 1/sqrt(head_dim)); "Universal AI Inference - Hugging Face
+// decoder completeness" (P1.3: positions follow the absolute KV index; P1.4:
+// sliding window, logit softcap as a tanh clip); "llamay - Models and
+// formats" (Architectures: gpt-oss's per-head sink in the softmax
+// denominator).
+//
+// What is computed: the T queries of a chunk of sequence b sit at positions
+// L - T .. L - 1 (L = keys including the chunk, whose keys and values the
+// chunk producer has already written).  Query t attends causally: the keys
+// at positions lo_t .. L - T + t, where lo_t = max(0, L - T + t + 1 - W)
+// under a window of W keys (W = 0: none).  Softmax over scale * <q, k>,
+// softcapped if asked, optionally with a sink logit in the denominator.
+//
+// Design (gfx950, bf16 K and V):
+//   * One work-group of four waves per (64 query rows, kv head, sequence).
+//     The rows are (token, head) pairs t * G + g of one kv head's group, so
+//     the G heads that share a kv head share every K and V tile (grouped
+//     flash attention): each tile is read from HBM once per 64 rows.
+//   * Key tiles of 32 rows are staged in LDS by the whole work-group with
+//     16-byte loads (padded rows, so the matrix reads below do not collide
+//     on banks).
+//   * Each wave owns 16 query rows and computes the transposed scores
+//     S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (two 16-key blocks).  In the
+//     transposed form the score registers of a lane already hold what the
+//     PV product needs as its A operand (one query, eight keys), so the
+//     probabilities never go through LDS.
+//   * Online softmax per query in f32, in the log2 domain (q pre-multiplied
+//     by scale * log2 e); keys outside a query's causal window get weight 0.
+//   * Precision: q (f32) and the probabilities (f32) are each split into a
+//     bf16 high part and a bf16 remainder, and both parts are multiplied by
+//     the exact bf16 K or V: two MFMAs per product, about 16 significant bits
+//     per operand and f32 accumulation (plain bf16 rounding of q and p would
+//     cost about 3 significant digits of the output).
+// Arithmetic intensity is about 4 * 64 flop per K/V byte in LDS and one HBM
+// read of each tile per 64 rows: the kernel is bound by the matrix cores.
+#include <math.h>
+
+#include "launch.h"
+
+namespace uaii {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWavesP = 4;   // waves per work-group
+constexpr int kRowsP = 64;   // query rows per work-group (16 per wave)
+constexpr int kKeys = 32;    // keys per tile
+constexpr float kLog2eP = 1.4426950408889634f;
+
+__device__ inline float capped(float s, bool cap, float c, float c_inv) {
+  return cap ? c * tanhf(s * c_inv) * kLog2eP : s;
+}
+
+// Split 8 floats into bf16 high parts and bf16 remainders (x ~ hi + lo).
+__device__ inline void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = static_cast<__bf16>(x[j]);
+    hi[j] = h;
+    lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+  }
+}
+
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(256) void prefill_attn_kernel(const PrefillArgs a) {
+  constexpr int KSTEPS = D / 32;  // k-steps of the score product
+  constexpr int NB = D / 16;      // 16-column blocks of the output
+  constexpr int LS = D + 8;       // LDS row stride in bf16 elements (16-byte pad)
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kKeys * LS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kKeys * LS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qi = lane & 15;   // query column of this lane (and row of the A operand)
+  const int quad = lane >> 4;
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int T = a.T, L = a.len[b];
+  const int P0 = L - T;  // position of the chunk's first token
+  const int rows = T * G;
+  const int row0 = blockIdx.x * kRowsP;
+
+  // This lane's query (S^T column qi of its wave).
+  const int my_row = row0 + wave * 16 + qi;
+  const bool row_ok = my_row < rows;
+  const int my_t = row_ok ? my_row / G : T - 1;
+  const int my_g = row_ok ? my_row % G : 0;
+  const int my_p = P0 + my_t;
+  const int my_lo = (a.window > 0 && my_p + 1 > a.window) ? my_p + 1 - a.window : 0;
+
+  // Keys any row of the work-group attends: [lo_first, k_end).
+  const int t_first = row0 / G;
+  const int t_last = min((row0 + kRowsP - 1) / G, T - 1);
+  const int p_first = P0 + t_first;
+  const int lo_first = (a.window > 0 && p_first + 1 > a.window) ? p_first + 1 - a.window : 0;
+  const int k_end = P0 + t_last + 1;
+  const int k_begin = lo_first & ~(kKeys - 1);
+
+  // Queries: B operand of S^T = K Q^T, lane holds q[qi][ks*32 + 8*quad + j].
+  bf16x8 qh[KSTEPS], ql[KSTEPS];
+  {
+    const float* qp = a.q + ((static_cast<int64_t>(b) * T + my_t) * a.H + kvh * G + my_g) * D + 8 * quad;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qp + s * 32);
+      const float4 x1 = *reinterpret_cast<const float4*>(qp + s * 32 + 4);
+      const float x[8] = {x0.x * a.q_mul, x0.y * a.q_mul, x0.z * a.q_mul, x0.w * a.q_mul,
+                          x1.x * a.q_mul, x1.y * a.q_mul, x1.z * a.q_mul, x1.w * a.q_mul};
+      split8(x, qh[s], ql[s]);
+    }
+  }
+  const bool cap = a.softcap > 0.0f;
+  const float cap_c = a.softcap, cap_inv = cap ? 1.0f / a.softcap : 0.0f;
+
+  f32x4 o[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, l = 0.0f;  // running max and sum of this lane's query
+
+  const int64_t slab = PAGED ? 0 : (static_cast<int64_t>(b) * a.Hkv + kvh) * a.cap;
+  // Element offset of key row r of this (b, kv head).
+  auto row_off = [&](int r) -> int64_t {
+    if constexpr (PAGED) {
+      int pid = a.block_table[static_cast<int64_t>(b) * a.max_blocks + (r >> a.log2_bs)];
+      pid = min(max(pid, 0), a.num_blocks - 1);
+      return ((static_cast<int64_t>(pid) * a.Hkv + kvh) * a.block_size + (r & (a.block_size - 1))) * D;
+    } else {
+      return (slab + r) * D;
+    }
+  };
+
+  for (int k0 = k_begin; k0 < k_end; k0 += kKeys) {
+    // Stage the tile's K and V rows.  Rows outside [lo_first, k_end) are
+    // replaced by the nearest row inside (every row read holds a visible
+    // key of some query of the work-group); their weights are zero.
+    u32x4 kreg[kKeys * CPR / 256 > 0 ? kKeys * CPR / 256 : 1];
+    u32x4 vreg[kKeys * CPR / 256 > 0 ? kKeys * CPR / 256 : 1];
+    constexpr int LOADS = kKeys * CPR / 256;
+    static_assert(LOADS * 256 == kKeys * CPR, "tile must split evenly over the work-group");
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / CPR, col = (c % CPR) * 8;
+      const int64_t off = row_off(min(max(k0 + r, lo_first), k_end - 1)) + col;
+      kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) + off);
+      vreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v) + off);
+    }
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / CPR, col = (c % CPR) * 8;
+      *reinterpret_cast<u32x4*>(&ks[r * LS + col]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&vs[r * LS + col]) = vreg[i];
+    }
+    __syncthreads();
+
+    // S^T for keys k0 + mb*16 + (0..15) against this wave's 16 queries:
+    // lane holds keys k0 + mb*16 + 4*quad + j of query qi.
+    f32x4 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int st = 0; st < KSTEPS; ++st) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&ks[(mb * 16 + qi) * LS + st * 32 + 8 * quad]);
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[st], s[mb], 0, 0, 0);
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[st], s[mb], 0, 0, 0);
+      }
+    }
+
+    // Masked, capped scores; the tile max of each query.
+    float sv[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + mb * 16 + 4 * quad + j;
+        const bool vis = row_ok && key >= my_lo && key <= my_p;
+        const float x = vis ? capped(s[mb][j], cap, cap_c, cap_inv) : -INFINITY;
+        sv[mb * 4 + j] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // no key yet: keep weights 0
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);    // m = -inf gives 0
+    float p[8];
+    float ps = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
+      ps += p[e];
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * alpha + ps;
+    m = m_new;
+
+    // Rescale the accumulator: its rows are queries 4*quad + j, whose alpha
+    // lives in lane 4*quad + j.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float aj = __shfl(alpha, 4 * quad + j);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) o[n][j] *= aj;
+    }
+
+    // O += P V.  A operand: lane holds P[qi][k = 8*quad + e], where k < 4 of
+    // the lane's group maps to key 4*quad + e and k >= 4 to key 16 + 4*quad +
+    // (e - 4) (the same keys the lane's S^T registers hold); the B operand
+    // reads V rows in the same order.
+    bf16x8 ph, pl;
+    split8(p, ph, pl);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      bf16x8 vb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = (e < 4) ? 4 * quad + e : 16 + 4 * quad + (e - 4);
+        vb[e] = __builtin_bit_cast(__bf16, vs[r * LS + n * 16 + qi]);
+      }
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, o[n], 0, 0, 0);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[n], 0, 0, 0);
+    }
+  }
+
+  // Normalise (with the sink, if any) and write.  Accumulator rows are
+  // queries 4*quad + j of the wave; their m and l live in lane 4*quad + j.
+  float sink2 = -INFINITY;
+  if (a.sinks != nullptr && row_ok) sink2 = a.sinks[kvh * G + my_g] * kLog2eP;
+  const float m_fin = fmaxf(m, sink2);
+  const float keep = __builtin_amdgcn_exp2f(m - m_fin);
+  const float den = l * keep + __builtin_amdgcn_exp2f(sink2 - m_fin);
+  const float f = keep / den;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float fj = __shfl(f, 4 * quad + j);
+    const int r = row0 + wave * 16 + 4 * quad + j;
+    if (r < rows) {
+      const int t = r / G, g = r % G;
+      float* dst = a.out + ((static_cast<int64_t>(b) * T + t) * a.H + kvh * G + g) * D + qi;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) dst[n * 16] = o[n][j] * fj;
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_dg(int B, const PrefillArgs& a, hipStream_t stream) {
+  const dim3 grid((a.T * G + kRowsP - 1) / kRowsP, a.Hkv, B);
+  if (a.block_table != nullptr)
+    hipLaunchKernelGGL((prefill_attn_kernel<D, G, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_attn_kernel<D, G, false>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(int G, int B, const PrefillArgs& a, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_dg<D, 1>(B, a, stream);
+    case 2: return launch_dg<D, 2>(B, a, stream);
+    case 4: return launch_dg<D, 4>(B, a, stream);
+    case 8: return launch_dg<D, 8>(B, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_attn(int D, int G, int B, const PrefillArgs& a, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_d<64>(G, B, a, stream);
+    case 128: return launch_d<128>(G, B, a, stream);
+    case 256: return launch_d<256>(G, B, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace uaii

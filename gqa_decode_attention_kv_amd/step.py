@@ -150,3 +150,64 @@ class DeviceStep:
         s = self.v_scale[bi, :, idx].cpu().numpy() if self.v_scale is not None else None
         ks = self.k_scale[bi, :, idx].cpu().numpy() if self.k_scale is not None else None
         return dict(k=k, v=v, scale=s, k_scale=ks)
+
+
+class DevicePrefill:
+    """Device buffers of one layer's chunk step (T new tokens per sequence)
+    and the two calls that run it: the chunk producer, then the chunk's
+    causal attention."""
+
+    def __init__(self, inputs, device: str = "cuda", paged: PagedInputs | None = None):
+        if not torch.cuda.is_available():
+            raise RuntimeError("DevicePrefill needs a GPU (torch.cuda.is_available() is False)")
+        w: Workload = inputs.workload
+        self.w, self.inputs, self.device, self.paged = w, inputs, device, paged
+        self.T = int(w.chunk)
+        self.seq_lens = np.ascontiguousarray(inputs.seq_lens, dtype=np.int32)
+        self.start = np.ascontiguousarray(inputs.start, dtype=np.int32)
+        Bn, H, Hkv, d = w.batch, w.n_heads, w.n_kv_heads, w.head_dim
+        self.q_in = _dev(inputs.q_in, device)
+        self.k_in = _dev(inputs.k_in, device)
+        self.v_in = _dev(inputs.v_in, device)
+        self.cache_k = _dev(paged.pool_k if paged else inputs.cache_k, device)
+        self.cache_v = _dev(paged.pool_v if paged else inputs.cache_v, device)
+        self.block_table = _dev(paged.block_table, device) if paged else None
+        self.sinks = _dev(inputs.sinks, device) if inputs.sinks is not None else None
+        self.w_q = _dev(inputs.w_q, device) if inputs.w_q is not None else None
+        self.w_k = _dev(inputs.w_k, device) if inputs.w_k is not None else None
+        self.q_out = torch.empty((Bn, self.T, H, d), dtype=torch.float32, device=device)
+        self.out = torch.empty((Bn, self.T, H, d), dtype=torch.float32, device=device)
+        self.shape = B.Shape(Bn, H, Hkv, d)
+        r = w.rope
+        self.rope = B.Rope(r.pairing, r.scaling, r.theta, r.factor, r.low, r.high, r.orig,
+                           int(r.truncate), r.attn_factor)
+        n = w.qk_norm
+        self.qk_norm = (B.QKNorm(1, n.eps, n.offset, self.w_q.data_ptr(), self.w_k.data_ptr())
+                        if n.enabled else None)
+        if paged:
+            self.cache = B.KVCache(w.k_dtype, w.v_dtype, paged.capacity, self.cache_k.data_ptr(),
+                                   self.cache_v.data_ptr(), None, self.block_table.data_ptr(),
+                                   paged.block_size, paged.max_blocks, paged.num_blocks, None)
+        else:
+            self.cache = B.KVCache(w.k_dtype, w.v_dtype, w.capacity, self.cache_k.data_ptr(),
+                                   self.cache_v.data_ptr(), None, None, 0, 0, 0, None)
+        self.scale = 1.0 / math.sqrt(d)
+
+    @staticmethod
+    def stream() -> int:
+        return torch.cuda.current_stream().cuda_stream
+
+    def produce(self):
+        B.kv_produce_chunk(self.shape, self.rope, self.qk_norm, self.q_in.data_ptr(),
+                           self.k_in.data_ptr(), self.v_in.data_ptr(), self.start, self.T,
+                           self.cache, self.q_out.data_ptr(), self.stream())
+
+    def attn(self):
+        B.prefill_attn(self.shape, self.cache, self.q_out.data_ptr(), self.seq_lens, self.T,
+                       self.scale, self.w.window, self.w.softcap,
+                       self.sinks.data_ptr() if self.sinks is not None else None,
+                       self.out.data_ptr(), self.stream())
+
+    def step(self):
+        self.produce()
+        self.attn()

@@ -13,6 +13,11 @@
  *                        sink in the softmax denominator
  *   uaii_decode_step     all of the above in a single launch
  *
+ * and, for a chunk of new tokens per sequence (prefill):
+ *
+ *   uaii_kv_produce_chunk  the producer for T tokens per sequence
+ *   uaii_prefill_attn      causal attention of the chunk's queries
+ *
  * Sources (page title, then section):
  *   [UAII]      "Universal AI Inference - Hugging Face decoder completeness"
  *   [ALGENTA]   "Algenta - Model support matrix"
@@ -305,6 +310,53 @@ uaii_status uaii_decode_step(const uaii_attn_shape *shape, const uaii_rope *rope
                              const float *sinks, float *q_out, float *part_o,
                              float *part_lse, int32_t *counters, float *out,
                              void *stream);
+
+/* --------------------------------------------------------------------------
+ * Chunks of new tokens (prefill)
+ * ------------------------------------------------------------------------ */
+
+/* The KV producer for a chunk of n_tokens = T new tokens per sequence:
+ * token t of sequence b is at position start_positions[b] + t, and each
+ * token is produced exactly as uaii_kv_produce produces one (norm, RoPE at
+ * its own position, append at its own slot).  With T = 1 it is
+ * uaii_kv_produce.
+ *   q_in, q_out        device [batch][T][n_heads][head_dim] f32
+ *   k_in, v_in         device [batch][T][n_kv_heads][head_dim] f32
+ *   start_positions    host [batch]; start + T <= capacity
+ *   n_tokens           1..65535
+ * Slots start .. start + T - 1 of each (b, kv head) are written. */
+uaii_status uaii_kv_produce_chunk(const uaii_attn_shape *shape, const uaii_rope *rope,
+                                  const uaii_qk_norm *qk_norm, const float *q_in,
+                                  const float *k_in, const float *v_in,
+                                  const int32_t *start_positions, int32_t n_tokens,
+                                  const uaii_kv_cache *cache, float *q_out, void *stream);
+
+/* Causal attention of a chunk ([ALGENTA] Kernel path capabilities:
+ * grouped-FA prefill and parametric prefill).  The chunk's T queries of
+ * sequence b sit at positions L - T .. L - 1 with L = seq_lens[b]; their keys
+ * and values are already in the cache (uaii_kv_produce_chunk).  Query t
+ * attends the keys at positions lo .. L - T + t, lo = max(0, L - T + t + 1 -
+ * window) with a window (0: lo = 0):
+ *   s_j = scale * <q[b][t][h], K[b][h / G][j]>, then c * tanh(s_j / c) if
+ *         softcap c > 0
+ *   out[b][t][h] = sum_j e^(s_j - m) v_j / (sum_j e^(s_j - m) [+ e^(sink_h - m)])
+ * with m the largest of the s_j (and sink_h).  This is uaii_decode_attn +
+ * uaii_decode_combine(_sink) of each query over its own prefix, in one
+ * launch on the matrix cores.
+ *   cache     bf16 keys and values (other dtypes are refused), contiguous
+ *             or paged
+ *   q         device [batch][T][n_heads][head_dim] f32 (q_out of the chunk
+ *             producer)
+ *   seq_lens  host [batch], each in [T, capacity]
+ *   n_tokens  1..2^20
+ *   sinks     device [n_heads] f32, or NULL (no sink)
+ *   out       device [batch][T][n_heads][head_dim] f32
+ * Accumulation is f32; q and the softmax weights enter the matrix products
+ * as a bf16 pair (high part and remainder), K and V as stored. */
+uaii_status uaii_prefill_attn(const uaii_attn_shape *shape, const uaii_kv_cache *cache,
+                              const float *q, const int32_t *seq_lens, int32_t n_tokens,
+                              float scale, int32_t window, float softcap,
+                              const float *sinks, float *out, void *stream);
 
 #ifdef __cplusplus
 }

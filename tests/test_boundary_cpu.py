@@ -297,3 +297,70 @@ def test_decode_step_valid_call_reaches_the_launch():
             step(sinks=sinks)
         assert ei.value.status == B.ERR_DEVICE
         assert ei.value.message.startswith("uaii_decode_step: HIP error")
+
+
+def produce_chunk(sh=None, ca=None, start=(0, 4), n=8, q_out=FAKE):
+    sh = sh or shape()
+    rope = B.Rope(B.ROPE_NEOX, B.ROPE_PLAIN, 1e4, 1.0, 1.0, 4.0, 8192)
+    B.kv_produce_chunk(sh, rope, None, FAKE, FAKE, FAKE, start, n, ca or cache(), q_out, 0)
+
+
+def prefill(sh=None, ca=None, lens=(10, 20), n=8, scale=None, window=0, softcap=0.0, sinks=None,
+            q=FAKE, out=FAKE):
+    sh = sh or shape()
+    scale = 1.0 / math.sqrt(sh.head_dim) if scale is None else scale
+    B.prefill_attn(sh, ca or cache(), q, lens, n, scale, window, softcap, sinks, out, 0)
+
+
+@host_only
+@pytest.mark.parametrize("case", [
+    ("n_tokens 0", lambda: produce_chunk(n=0), INV, ["n_tokens=0"]),
+    ("n_tokens too many", lambda: produce_chunk(n=70000), NI, ["n_tokens=70000", "1..65535"]),
+    ("start + n > cap", lambda: produce_chunk(start=(0, 60)), INV,
+     ["start_positions[1]=60 with n_tokens=8", "capacity=64"]),
+    ("start negative", lambda: produce_chunk(start=(-1, 0)), INV, ["start_positions[0]=-1"]),
+    ("start null", lambda: B.load().uaii_kv_produce_chunk(
+        B.Shape(2, 8, 2, 128), B.Rope(0, 0, 1e4, 1, 1, 4, 8192), None, FAKE, FAKE, FAKE, None, 4,
+        cache(), FAKE, None), None, []),
+    ("q_out null", lambda: produce_chunk(q_out=None), INV, ["q_out is NULL"]),
+    ("head_dim", lambda: produce_chunk(sh=shape(d=32)), NI, ["head_dim=32"]),
+], ids=lambda c: c[0])
+def test_kv_produce_chunk_refusals(case):
+    name, fn, status, needles = case
+    if status is None:
+        assert fn() == INV
+        assert "start_positions is NULL" in B.last_error()
+        return
+    msg = refused(fn, status, *needles)
+    assert msg.startswith("uaii_kv_produce_chunk: ")
+
+
+@host_only
+@pytest.mark.parametrize("case", [
+    ("f32 cache", lambda: prefill(ca=cache(kd=B.F32, vd=B.F32)), NI,
+     ["prefill over k_dtype=0, v_dtype=0 is not supported", "bf16"]),
+    ("vq8 cache", lambda: prefill(ca=cache(vd=B.I8, s=FAKE)), NI, ["v_dtype=2"]),
+    ("len < n_tokens", lambda: prefill(lens=(5, 20)), INV, ["seq_lens[0]=5", "n_tokens=8"]),
+    ("len > cap", lambda: prefill(lens=(65, 20)), INV, ["seq_lens[0]=65"]),
+    ("n_tokens 0", lambda: prefill(n=0), INV, ["n_tokens=0"]),
+    ("window", lambda: prefill(window=-2), INV, ["window=-2"]),
+    ("softcap", lambda: prefill(softcap=float("nan")), INV, ["softcap=nan"]),
+    ("scale", lambda: prefill(scale=0.2), NI, ["scale=0.2"]),
+    ("q null", lambda: prefill(q=None), INV, ["q is NULL"]),
+    ("out misaligned", lambda: prefill(out=FAKE + 4), INV, ["out", "16-byte aligned"]),
+    ("sinks misaligned", lambda: prefill(sinks=FAKE + 1), INV, ["sinks", "4-byte aligned"]),
+    ("gqa 3", lambda: prefill(sh=shape(h=6, hkv=2)), NI, ["n_heads/n_kv_heads=3"]),
+], ids=lambda c: c[0])
+def test_prefill_attn_refusals(case):
+    _, fn, status, needles = case
+    msg = refused(fn, status, *needles)
+    assert msg.startswith("uaii_prefill_attn: ")
+
+
+@host_only
+def test_prefill_valid_calls_reach_the_launch():
+    for fn in (lambda: prefill(), lambda: prefill(sinks=FAKE, window=3, softcap=5.0),
+               lambda: produce_chunk()):
+        with pytest.raises(B.UaiiError) as ei:
+            fn()
+        assert ei.value.status == B.ERR_DEVICE

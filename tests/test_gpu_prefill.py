@@ -1,0 +1,221 @@
+"""GPU parity of the chunk (prefill) path against the CPU oracle, through the
+C ABI: uaii_kv_produce_chunk writes the chunk's T tokens, uaii_prefill_attn
+computes their causal attention on the matrix cores.
+
+* Small cases compare every output element, every produced cache row (and
+  that no other row changed) and the rotated queries; they cover head dims
+  64/128/256, GQA ratios 1-8, empty and non-empty caches, ragged batches,
+  windows (1, inside the chunk, wider than the context), softcap, sinks,
+  one-token chunks, several key tiles and the paged layout.
+* The prefill workloads run at full size with sampled (sequence, token,
+  head) outputs and every produced row.
+* The chunk's attention agrees with the decode path run token by token.
+Tolerance on the output: 2e-3 absolute (bf16 K/V, f32 accumulation), the
+bf16 bar of the decode path.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import parity as P
+from gqa_decode_attention_kv_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gqa_decode_attention_kv_amd import binding
+    binding.load()
+
+
+def case(name, d, G, Hkv, T, lens, window=0, softcap=0.0, rope=None, norm=None, sink=False,
+         seed=0, bs=None):
+    lens = tuple(int(x) for x in lens)
+    qn = W.QKNorm(False) if norm is None else W.QKNorm(True, 1e-6, norm, 1.0 - norm, 0.1)
+    w = W.Workload(name, len(lens), Hkv * G, Hkv, d, ("fixed", lens[0]), max(lens) + 3, W.BF16,
+                   W.BF16, rope or W.Rope(W.NEOX, W.PLAIN, 1e4), qn, window, softcap, 512,
+                   (4000 + seed,), sink, T)
+    return w, np.array(lens, np.int32), bs
+
+
+LLAMA3 = W.Rope(W.INTERLEAVED, W.LLAMA3, 5e5, 8.0)
+
+SMALL = [
+    case("d128-g4-empty-cache", 128, 4, 2, 100, [100, 100], seed=1),
+    case("d128-g2-chunk-after-cache", 128, 2, 2, 70, [300, 71], rope=LLAMA3, seed=2),
+    case("d64-g8-one-kv-head", 64, 8, 1, 33, [97], seed=3),
+    case("d256-g2-window-softcap-norm", 256, 2, 2, 90, [250, 90], window=50, softcap=50.0, norm=1,
+         seed=4),
+    case("d128-g1-window1", 128, 1, 3, 20, [40], window=1, seed=5),
+    case("d64-g4-sink", 64, 4, 2, 65, [130, 200], sink=True, seed=6),
+    case("d128-g4-one-token", 128, 4, 2, 1, [500, 3], seed=7),
+    case("d128-g8-several-tiles", 128, 8, 1, 257, [1000], norm=0, seed=8),
+    case("d64-g1-window-wider", 64, 1, 4, 40, [70, 45], window=5000, seed=9),
+    case("d128-g4-window-in-chunk", 128, 4, 2, 150, [400, 160], window=37, softcap=20.0, seed=10),
+    case("d256-g8-sink-window", 256, 8, 1, 24, [64], window=30, sink=True, seed=11),
+    case("d128-g4-b32-ragged", 128, 4, 2, 16,
+         np.random.default_rng(12).integers(16, 201, 32), rope=LLAMA3, seed=12),
+    case("d128-g4-paged-bs16", 128, 4, 2, 100, [333, 120], window=200, seed=13, bs=16),
+    case("d64-g2-paged-bs64-sink", 64, 2, 2, 50, [50, 260], sink=True, seed=14, bs=64),
+]
+
+
+def run_gpu(inputs, paged=None):
+    from gqa_decode_attention_kv_amd.step import DevicePrefill
+    st = DevicePrefill(inputs, paged=paged)
+    st.out.fill_(float("nan"))
+    st.step()
+    torch.cuda.synchronize()
+    return st
+
+
+def oracle_side(inputs, copy_cache=True):
+    o = oracle.load()
+    w = inputs.workload
+    ck = inputs.cache_k.copy() if copy_cache else inputs.cache_k
+    cv = inputs.cache_v.copy() if copy_cache else inputs.cache_v
+    norm = None
+    if w.qk_norm.enabled:
+        norm = dict(enabled=True, eps=w.qk_norm.eps, offset=w.qk_norm.offset, w_q=inputs.w_q,
+                    w_k=inputs.w_k)
+    q = o.kv_produce_chunk(rope=w.rope.as_dict(), norm=norm, q_in=inputs.q_in, k_in=inputs.k_in,
+                           v_in=inputs.v_in, start_positions=inputs.start, k_dtype=w.k_dtype,
+                           v_dtype=w.v_dtype, cache_k=ck, cache_v=cv)
+    return o, q, ck, cv
+
+
+def chunk_rows(st, cache):
+    """[B][Hkv][T][d] view of the chunk's slots (contiguous or through the table)."""
+    w = st.w
+    out = []
+    for b in range(w.batch):
+        pos = st.start[b] + np.arange(st.T)
+        if st.paged:
+            bs = st.paged.block_size
+            blk = st.paged.block_table[b, pos // bs]
+            out.append(np.stack([cache[blk, u, pos % bs] for u in range(w.n_kv_heads)]))
+        else:
+            out.append(cache[b][:, pos])
+    return np.stack(out)
+
+
+def check_rows(st, ref_q, ck, cv):
+    w = st.w
+    q = st.q_out.cpu().numpy()
+    qerr = np.max(np.abs(q - ref_q)) / np.max(np.abs(ref_q))
+    assert qerr <= 1e-6, f"q_out relative error {qerr:.3g}"
+    gk = chunk_rows(st, st.cache_k.cpu().numpy().view(np.uint16))
+    gv = chunk_rows(st, st.cache_v.cpu().numpy().view(np.uint16))
+    rk = np.stack([ck[b][:, st.start[b] + np.arange(st.T)] for b in range(w.batch)])
+    rv = np.stack([cv[b][:, st.start[b] + np.arange(st.T)] for b in range(w.batch)])
+    assert P.bf16_ulps(gk, rk).max() <= 1, "produced K differs by more than 1 bf16 ulp"
+    assert np.array_equal(gv, rv), "produced V differs (must be bit-exact)"
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[c[0].name for c in SMALL])
+def test_prefill_small(spec):
+    w, lens, bs = spec
+    P.say(f"prefill case {w.name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
+          f"T={w.chunk} lens={lens.tolist()[:8]} W={w.window} cap={w.softcap} sink={w.sink} "
+          f"paged={bs}")
+    inputs = W.make_prefill_inputs(w, seq_lens=lens)
+    paged = W.make_paged(inputs, bs) if bs else None
+    before = (paged.pool_k.copy(), paged.pool_v.copy()) if paged else (inputs.cache_k.copy(),
+                                                                      inputs.cache_v.copy())
+    st = run_gpu(inputs, paged)
+    o, q, ck, cv = oracle_side(inputs)
+    check_rows(st, q, ck, cv)
+    # nothing but the chunk's slots changed
+    for dev, host in ((st.cache_k, before[0]), (st.cache_v, before[1])):
+        g = dev.cpu().numpy().view(np.uint16)
+        mask = np.ones(g.shape[:3], bool)
+        for b in range(w.batch):
+            pos = st.start[b] + np.arange(st.T)
+            if paged:
+                blk = paged.block_table[b, pos // paged.block_size]
+                mask[blk, :, pos % paged.block_size] = False
+            else:
+                mask[b, :, pos] = False
+        assert np.array_equal(g[mask], host[mask]), "cache rows outside the chunk changed"
+    want = o.prefill(q=q, cache_k=ck, cache_v=cv, k_dtype=w.k_dtype, v_dtype=w.v_dtype,
+                     seq_lens=lens, window=w.window, softcap=w.softcap, sinks=inputs.sinks)
+    out = st.out.cpu().numpy()
+    err = float(np.max(np.abs(out - want)))
+    P.say(f"  max abs err {err:.3g} (tol {TOL})")
+    assert np.all(np.isfinite(out)) and err <= TOL, err
+
+
+@pytest.mark.parametrize("name", list(W.PREFILL))
+def test_prefill_full_size(name):
+    w = W.PREFILL[name]
+    P.say(f"prefill full-size {name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
+          f"T={w.chunk} L={w.lens} W={w.window} cap={w.softcap}")
+    inputs = W.make_prefill_inputs(w)
+    st = run_gpu(inputs)
+    o, q, ck, cv = oracle_side(inputs, copy_cache=False)
+    check_rows(st, q, ck, cv)
+    rng = np.random.default_rng(7)
+    T = w.chunk
+    tr = [(b, t, int(rng.integers(w.n_heads))) for b in range(w.batch) for t in (0, T - 1)]
+    tr += [(int(rng.integers(w.batch)), int(rng.integers(T)), int(rng.integers(w.n_heads)))
+           for _ in range(48)]
+    want = o.prefill(q=q, cache_k=ck, cache_v=cv, k_dtype=w.k_dtype, v_dtype=w.v_dtype,
+                     seq_lens=inputs.seq_lens, window=w.window, softcap=w.softcap,
+                     sinks=inputs.sinks, triples=tr)
+    out = st.out.cpu().numpy()
+    got = np.stack([out[b, t, h] for b, t, h in tr])
+    err = float(np.max(np.abs(got - want)))
+    P.say(f"  sampled {len(tr)} outputs: max abs err {err:.3g} (tol {TOL})")
+    assert np.all(np.isfinite(out)) and err <= TOL, err
+
+
+def test_prefill_matches_decode_token_by_token():
+    """Each chunk query's output equals the decode path's (partials and
+    combine, f32 vector arithmetic) for the same query at the same length."""
+    from gqa_decode_attention_kv_amd import binding as B
+    w, lens, _ = SMALL[1]
+    inputs = W.make_prefill_inputs(w, seq_lens=lens)
+    st = run_gpu(inputs)
+    T, S = st.T, 64
+    max_splits = int(-(-int(lens.max()) // S))
+    part_o = torch.empty((w.batch, w.n_heads, max_splits, w.head_dim), device="cuda")
+    part_lse = torch.empty((w.batch, w.n_heads, max_splits), device="cuda")
+    out = torch.empty((w.batch, w.n_heads, w.head_dim), device="cuda")
+    worst = 0.0
+    for t in range(T):
+        q = st.q_out[:, t].contiguous()
+        Lt = (lens - T + t + 1).astype(np.int32)
+        B.decode_attn(st.shape, st.cache, q.data_ptr(), Lt, st.scale, w.window, w.softcap, S,
+                      max_splits, part_o.data_ptr(), part_lse.data_ptr(), st.stream())
+        B.decode_combine(st.shape, Lt, w.window, S, max_splits, part_o.data_ptr(),
+                         part_lse.data_ptr(), out.data_ptr(), st.stream())
+        torch.cuda.synchronize()
+        worst = max(worst, float((out - st.out[:, t]).abs().max()))
+    P.say(f"  prefill vs decode, {T} tokens: max abs difference {worst:.3g}")
+    assert worst <= 2e-4, worst
+
+
+def test_prefill_refusals_write_nothing():
+    """An f32 cache (not supported by the chunk kernel) and a length shorter
+    than the chunk are refused before any launch; nothing is written."""
+    from gqa_decode_attention_kv_amd import binding as B
+    w, lens, _ = SMALL[0]
+    inputs = W.make_prefill_inputs(w, seq_lens=lens)
+    st = run_gpu(inputs)
+    before = st.out.clone()
+    f32_cache = B.KVCache(B.F32, B.F32, st.cache.capacity, st.cache.k, st.cache.v, None, None, 0,
+                          0, 0, None)
+    with pytest.raises(B.UaiiError, match="prefill over k_dtype=0"):
+        B.prefill_attn(st.shape, f32_cache, st.q_out.data_ptr(), st.seq_lens, st.T, st.scale, 0,
+                       0.0, None, st.out.data_ptr(), st.stream())
+    with pytest.raises(B.UaiiError, match="seq_lens"):
+        B.prefill_attn(st.shape, st.cache, st.q_out.data_ptr(), st.seq_lens - st.T, st.T, st.scale,
+                       0, 0.0, None, st.out.data_ptr(), st.stream())
+    torch.cuda.synchronize()
+    assert torch.equal(before, st.out)
