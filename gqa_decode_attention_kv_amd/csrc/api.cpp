@@ -176,6 +176,56 @@ uaii_status check_lens(const char* fn, const uaii_attn_shape* s, const int32_t* 
   return UAII_OK;
 }
 
+// Rotary frequency g_i of every pair i < d/2 over the full head, with the
+// scheme's scaling ("Universal AI Inference - Hugging Face decoder
+// completeness", P0.2: plain theta, Llama-3 scaling matching Hugging Face,
+// YaRN; "FreeToken PR #722", Changes: Llama-3 band constants; "Algenta -
+// Model support matrix", Decoder families: linear scaling).  f_i =
+// theta^(-2i/d).  Llama-3: with wavelength 2 pi / f, keep f below
+// original/high, divide by factor above original/low, blend linearly in
+// original/wavelength between.  Linear: f / factor.  YaRN: blend f / factor
+// and f with a weight linear in the pair index between the indices that
+// turn beta_fast and beta_slow times over the original context (rounded
+// outwards when truncate is set).  Evaluated once per call in double.
+void rope_freqs(const uaii_rope* r, int d, double* g) {
+  const double pi = 3.14159265358979323846;
+  double c_lo = 0.0, c_hi = 1.0;
+  if (r->scaling == UAII_ROPE_YARN) {
+    const double orig = static_cast<double>(r->original_max_position);
+    c_lo = d * std::log(orig / (2.0 * pi * r->high_freq_factor)) / (2.0 * std::log(r->theta));
+    c_hi = d * std::log(orig / (2.0 * pi * r->low_freq_factor)) / (2.0 * std::log(r->theta));
+    if (r->truncate) {
+      c_lo = std::floor(c_lo);
+      c_hi = std::ceil(c_hi);
+    }
+    c_lo = std::max(c_lo, 0.0);
+    c_hi = std::min(c_hi, d - 1.0);
+    if (c_hi == c_lo) c_hi += 0.001;
+  }
+  for (int i = 0; i < d / 2; ++i) {
+    const double f = std::pow(r->theta, -2.0 * static_cast<double>(i) / static_cast<double>(d));
+    double gi = f;
+    if (r->scaling == UAII_ROPE_LINEAR) {
+      gi = f / r->factor;
+    } else if (r->scaling == UAII_ROPE_YARN) {
+      const double t = std::min(std::max((static_cast<double>(i) - c_lo) / (c_hi - c_lo), 0.0), 1.0);
+      gi = t * f / r->factor + (1.0 - t) * f;
+    } else if (r->scaling == UAII_ROPE_LLAMA3) {
+      const double orig = static_cast<double>(r->original_max_position);
+      const double wavelen = 2.0 * pi / f;
+      if (wavelen < orig / r->high_freq_factor) {
+        gi = f;
+      } else if (wavelen > orig / r->low_freq_factor) {
+        gi = f / r->factor;
+      } else {
+        const double mu = (orig / wavelen - r->low_freq_factor) / (r->high_freq_factor - r->low_freq_factor);
+        gi = (1.0 - mu) * f / r->factor + mu * f;
+      }
+    }
+    g[i] = gi;
+  }
+}
+
 // Checks the producer's arguments (rope, norm, inputs, q_out) and fills
 // everything in ProduceArgs except the positions.  Shape and cache are
 // checked by the caller.
@@ -240,33 +290,12 @@ uaii_status produce_args(const char* fn, const uaii_attn_shape* shape, const uai
   a.Hkv = shape->n_kv_heads;
   a.D = shape->head_dim;
   a.pairing = rope->pairing;
-  a.scaling = rope->scaling;
-  a.theta = rope->theta;
-  a.factor = rope->factor;
-  a.low = rope->low_freq_factor;
-  a.high = rope->high_freq_factor;
-  a.orig = static_cast<double>(rope->original_max_position);
+  rope_freqs(rope, shape->head_dim, a.freq);
   a.attn_factor = 1.0;
-  if (rope->scaling == UAII_ROPE_YARN) {
-    // Blend band in pair indices; the same quantities for every pair, so
-    // they are computed once here (host double precision).
-    const double pi = 3.14159265358979323846;
-    const double d = static_cast<double>(shape->head_dim);
-    double lo = d * std::log(a.orig / (2.0 * pi * rope->high_freq_factor)) / (2.0 * std::log(rope->theta));
-    double hi = d * std::log(a.orig / (2.0 * pi * rope->low_freq_factor)) / (2.0 * std::log(rope->theta));
-    if (rope->truncate) {
-      lo = std::floor(lo);
-      hi = std::ceil(hi);
-    }
-    lo = std::max(lo, 0.0);
-    hi = std::min(hi, d - 1.0);
-    if (hi == lo) hi += 0.001;
-    a.c_lo = lo;
-    a.c_hi = hi;
+  if (rope->scaling == UAII_ROPE_YARN)
     a.attn_factor = rope->attention_factor > 0.0
                         ? rope->attention_factor
                         : (rope->factor <= 1.0 ? 1.0 : 0.1 * std::log(rope->factor) + 1.0);
-  }
   a.norm_enabled = norm ? 1 : 0;
   a.norm_offset = norm ? qk_norm->offset : 0;
   a.norm_eps = norm ? qk_norm->eps : 0.0f;
@@ -288,6 +317,7 @@ uaii_status produce_args(const char* fn, const uaii_attn_shape* shape, const uai
   a.max_blocks = cache->block_table ? cache->max_blocks : 0;
   a.num_blocks = cache->block_table ? cache->num_blocks : 0;
   a.T = 1;
+  a.hpw = 1;
   *out = a;
   return UAII_OK;
 }
@@ -420,6 +450,9 @@ uaii_status uaii_kv_produce_chunk(const uaii_attn_shape* shape, const uaii_rope*
             kInvalid, "start_positions[%d]=%d with n_tokens=%d is outside [0, capacity=%d]", b,
             start_positions[b], n_tokens, cache->capacity);
   a.T = n_tokens;
+  // Several tokens: each wave rotates up to 8 head vectors of a token with
+  // one evaluation of that token's angles.
+  a.hpw = n_tokens > 1 ? std::min(8, shape->n_heads + shape->n_kv_heads) : 1;
   for (int b = 0; b < shape->batch; ++b) a.pos[b] = start_positions[b];
   return device_status(fn, uaii::launch_kv_produce(a, static_cast<hipStream_t>(stream)));
 }

@@ -9,8 +9,8 @@
 // families: linear scaling); "FreeToken PR #722" (Changes: Llama-3 scaling
 // constants).
 //
-// The work is O(B * T * (H + Hkv) * d): one 64-lane wave per head vector of
-// each of the T tokens of each sequence (T = 1 for a decode step).  The
+// The work is O(B * T * (H + Hkv) * d): one 64-lane wave per hpw head vectors
+// of one of the T tokens of a sequence (T = 1 and hpw = 1 for a decode step).  The
 // per-vector math lives in producer_math.h (shared with the fused step): the
 // norm and the rotation run in double precision and round once to the
 // stored format, so the stored key matches a double-precision definition to
@@ -29,50 +29,67 @@ __global__ __launch_bounds__(64) void kv_produce_kernel(ProduceArgs a) {
   constexpr int NP = pm::Shape<D>::NP;
   __shared__ double sx[D];
   const int lane = threadIdx.x;
-  const int x = blockIdx.x;
   const int b = blockIdx.y;
   const int t = blockIdx.z;  // token of the chunk
   const int pos = a.pos[b] + t;
   const int64_t bt = static_cast<int64_t>(b) * a.T + t;
-  const bool is_q = x < a.H;
-  const int u = x - a.H;
+  // Head vectors [x0, x1) of this token: q heads 0..H-1, then kv heads.
+  const int x0 = blockIdx.x * a.hpw;
+  const int x1 = min(x0 + a.hpw, a.H + a.Hkv);
 
-  // Loads first; the data-independent angles below overlap with them.
-  const float* src = is_q ? a.q_in + (bt * a.H + x) * D : a.k_in + (bt * a.Hkv + u) * D;
-  float xin[EPL], v[EPL];
+  // Input rows of head vector x (and, for a kv head, its value row).
+  auto load = [&](int x, float (&xin)[EPL], float (&v)[EPL]) {
+    const bool is_q = x < a.H;
+    const int u = x - a.H;
+    const float* src = is_q ? a.q_in + (bt * a.H + x) * D : a.k_in + (bt * a.Hkv + u) * D;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) xin[e] = src[lane + 64 * e];
-  if (!is_q) {
-    const float* vsrc = a.v_in + (bt * a.Hkv + u) * D;
+    for (int e = 0; e < EPL; ++e) xin[e] = src[lane + 64 * e];
+    if (!is_q) {
+      const float* vsrc = a.v_in + (bt * a.Hkv + u) * D;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) v[e] = vsrc[lane + 64 * e];
-  }
+      for (int e = 0; e < EPL; ++e) v[e] = vsrc[lane + 64 * e];
+    }
+  };
 
+  // The first loads overlap with the angles, which depend only on the
+  // position; each later head's loads overlap with the previous head.
+  float xin[EPL] = {}, v[EPL] = {};
+  load(x0, xin, v);
   pm::Angles<D> an;
   pm::rope_angles<D>(a, pos, lane, an);
-  pm::Rotated<D> r;
-  pm::norm_rope<D>(a, xin, is_q ? a.w_q : a.w_k, an, sx, lane, r);
-
-  if (is_q) {
-    float* q = a.q_out + (bt * a.H + x) * D;
+  for (int x = x0; x < x1; ++x) {
+    float nx[EPL] = {}, nv[EPL] = {};
+    if (x + 1 < x1) load(x + 1, nx, nv);
+    const bool is_q = x < a.H;
+    const int u = x - a.H;
+    pm::Rotated<D> r;
+    pm::norm_rope<D>(a, xin, is_q ? a.w_q : a.w_k, an, sx, lane, r);
+    if (is_q) {
+      float* q = a.q_out + (bt * a.H + x) * D;
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      if (!r.ok[j]) continue;
-      q[r.ia[j]] = static_cast<float>(r.ya[j]);
-      q[r.ib[j]] = static_cast<float>(r.yb[j]);
+      for (int j = 0; j < NP; ++j) {
+        if (!r.ok[j]) continue;
+        q[r.ia[j]] = static_cast<float>(r.ya[j]);
+        q[r.ib[j]] = static_cast<float>(r.yb[j]);
+      }
+    } else {
+      const int64_t slot = pm::cache_slot<D>(a, b, u, pos);
+      float kst[2 * NP], vst[EPL];
+      pm::store_key<D>(a, r, slot, lane, kst);
+      pm::store_value<D>(a, v, slot, lane, vst);
     }
-    return;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      xin[e] = nx[e];
+      v[e] = nv[e];
+    }
   }
-  const int64_t slot = pm::cache_slot<D>(a, b, u, pos);
-  float kst[2 * NP], vst[EPL];
-  pm::store_key<D>(a, r, slot, lane, kst);
-  pm::store_value<D>(a, v, slot, lane, vst);
 }
 
 }  // namespace
 
 hipError_t launch_kv_produce(const ProduceArgs& a, hipStream_t stream) {
-  const dim3 grid(a.H + a.Hkv, a.B, a.T);
+  const dim3 grid((a.H + a.Hkv + a.hpw - 1) / a.hpw, a.B, a.T);
   switch (a.D) {
     case 64: hipLaunchKernelGGL(kv_produce_kernel<64>, grid, dim3(64), 0, stream, a); break;
     case 128: hipLaunchKernelGGL(kv_produce_kernel<128>, grid, dim3(64), 0, stream, a); break;

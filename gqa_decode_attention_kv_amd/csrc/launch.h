@@ -9,10 +9,10 @@
 namespace uaii {
 
 constexpr int kMaxBatch = 32;
+constexpr int kMaxPairs = 128;  // rotation pairs of the largest head (d = 256)
 
 enum : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
 enum : int { kNeox = 0, kInterleaved = 1 };
-enum : int { kPlain = 0, kLlama3 = 1, kLinear = 2, kYarn = 3 };
 
 // Per-sequence schedule of one decode step.  Work item w of the partial
 // kernel belongs to sequence b with work_prefix[b] <= w < work_prefix[b + 1];
@@ -28,11 +28,12 @@ struct SeqTable {
 
 struct ProduceArgs {
   int32_t B, H, Hkv, D;
-  int32_t pairing, scaling;
-  double theta, factor, low, high, orig;
-  // YaRN: blend band over pair indices [c_lo, c_hi] and the factor that
-  // multiplies the rotated q and k (1 for the other schemes).
-  double c_lo, c_hi, attn_factor;
+  int32_t pairing;
+  // Rotary frequency g_i of pair i (plain, Llama-3, linear or YaRN), the same
+  // for every token of a call, so the host evaluates the scheme once.
+  double freq[kMaxPairs];
+  // The factor that multiplies the rotated q and k (YaRN; 1 otherwise).
+  double attn_factor;
   int32_t norm_enabled, norm_offset;
   float norm_eps;
   const float* w_q;
@@ -53,6 +54,9 @@ struct ProduceArgs {
   // Tokens per sequence: q_in, q_out [B][T][H][D], k_in, v_in [B][T][Hkv][D];
   // token t of sequence b sits at position pos[b] + t.  T = 1 for decode.
   int32_t T;
+  // Head vectors per wave of the standalone producer: the wave evaluates the
+  // token's rotation angles once and applies them to hpw consecutive heads.
+  int32_t hpw;
   int32_t pos[kMaxBatch];
 };
 

@@ -25,8 +25,6 @@
 namespace uaii {
 namespace pm {
 
-constexpr double kTwoPi = 6.283185307179586476925286766559;
-
 __device__ inline double wave_sum_d(double x) {
   for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
   return x;
@@ -67,31 +65,14 @@ __device__ inline uint16_t bf16_from_double(double x) {
 
 __device__ inline float bf16_to_float(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-// Rotary frequency of pair i (full head): plain, Llama-3, linear or YaRN.
-// YaRN's blend band [c_lo, c_hi] in pair indices comes from the host.
-__device__ inline double rope_freq(const ProduceArgs& a, int i) {
-#pragma clang fp contract(off)
-  const double f = pow(a.theta, -2.0 * static_cast<double>(i) / static_cast<double>(a.D));
-  if (a.scaling == kLinear) return f / a.factor;
-  if (a.scaling == kYarn) {
-    const double t = fmin(fmax((static_cast<double>(i) - a.c_lo) / (a.c_hi - a.c_lo), 0.0), 1.0);
-    return t * f / a.factor + (1.0 - t) * f;
-  }
-  if (a.scaling != kLlama3) return f;
-  const double wavelen = kTwoPi / f;
-  if (wavelen < a.orig / a.high) return f;
-  if (wavelen > a.orig / a.low) return f / a.factor;
-  const double mu = (a.orig / wavelen - a.low) / (a.high - a.low);
-  return (1.0 - mu) * f / a.factor + mu * f;
-}
-
 template <int D>
 struct Shape {
   static constexpr int EPL = D / 64;             // elements per lane
   static constexpr int NP = (D / 2 + 63) / 64;   // rotation pairs per lane
 };
 
-// cos and sin of pos * g_i for this lane's pairs i = lane + 64 j.
+// cos and sin of pos * g_i for this lane's pairs i = lane + 64 j (g_i from
+// the host's frequency table).
 template <int D>
 struct Angles {
   double cs[Shape<D>::NP], sn[Shape<D>::NP];
@@ -105,7 +86,7 @@ __device__ inline void rope_angles(const ProduceArgs& a, int pos, int lane, Angl
     const int i = lane + 64 * j;
     an.cs[j] = 1.0;
     an.sn[j] = 0.0;
-    if (i < D / 2) sincos(static_cast<double>(pos) * rope_freq(a, i), &an.sn[j], &an.cs[j]);
+    if (i < D / 2) sincos(static_cast<double>(pos) * a.freq[i], &an.sn[j], &an.cs[j]);
   }
 }
 
