@@ -21,14 +21,18 @@
 //     The rows are (token, head) pairs t * G + g of one kv head's group, so
 //     the G heads that share a kv head share every K and V tile (grouped
 //     flash attention): each tile is read from HBM once per 64 rows.
-//   * Key tiles of 32 rows are staged in LDS by the whole work-group with
-//     16-byte loads (padded rows, so the matrix reads below do not collide
-//     on banks).
+//   * Key tiles of 32 rows of K and V are staged in LDS by the whole
+//     work-group with 16-byte loads (padded rows, so the matrix reads below
+//     do not collide on banks).  (Loading the next tile into registers
+//     during the current tile's products was measured slower: the extra
+//     registers cost a wave per SIMD.)
 //   * Each wave owns 16 query rows and computes the transposed scores
 //     S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (two 16-key blocks).  In the
 //     transposed form the score registers of a lane already hold what the
 //     PV product needs as its A operand (one query, eight keys), so the
-//     probabilities never go through LDS.
+//     probabilities never go through LDS; V, which that product needs one
+//     dim across eight keys per lane, is read with gfx950's transposing LDS
+//     load.
 //   * Online softmax per query in f32, in the log2 domain (q pre-multiplied
 //     by scale * log2 e); keys outside a query's causal window get weight 0.
 //   * Precision: q (f32) and the probabilities (f32) are each split into a
@@ -48,6 +52,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kWavesP = 4;   // waves per work-group
 constexpr int kRowsP = 64;   // query rows per work-group (16 per wave)
@@ -72,8 +79,10 @@ template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(256) void prefill_attn_kernel(const PrefillArgs a) {
   constexpr int KSTEPS = D / 32;  // k-steps of the score product
   constexpr int NB = D / 16;      // 16-column blocks of the output
-  constexpr int LS = D + 8;       // LDS row stride in bf16 elements (16-byte pad)
-  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int LS = D + 8;       // K and V tiles: LDS row stride in bf16 elements (16-byte pad)
+  constexpr int CPR = D / 8;      // 16-byte chunks per key row
+  constexpr int LOADS = kKeys * CPR / 256;
+  static_assert(LOADS * 256 == kKeys * CPR, "tile must split evenly over the work-group");
   __shared__ __attribute__((aligned(16))) uint16_t ks[kKeys * LS];
   __shared__ __attribute__((aligned(16))) uint16_t vs[kKeys * LS];
 
@@ -136,15 +145,12 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const PrefillArgs a) 
       return (slab + r) * D;
     }
   };
-
-  for (int k0 = k_begin; k0 < k_end; k0 += kKeys) {
-    // Stage the tile's K and V rows.  Rows outside [lo_first, k_end) are
-    // replaced by the nearest row inside (every row read holds a visible
-    // key of some query of the work-group); their weights are zero.
-    u32x4 kreg[kKeys * CPR / 256 > 0 ? kKeys * CPR / 256 : 1];
-    u32x4 vreg[kKeys * CPR / 256 > 0 ? kKeys * CPR / 256 : 1];
-    constexpr int LOADS = kKeys * CPR / 256;
-    static_assert(LOADS * 256 == kKeys * CPR, "tile must split evenly over the work-group");
+  // This thread's share of a tile: LOADS 16-byte chunks of K and of V.
+  // Rows outside [lo_first, k_end) are replaced by the nearest row inside
+  // (every row read holds a visible key of some query of the work-group);
+  // their weights are zero.
+  u32x4 kreg[LOADS], vreg[LOADS];
+  auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int c = tid + 256 * i;
@@ -153,6 +159,15 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const PrefillArgs a) 
       kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) + off);
       vreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v) + off);
     }
+  };
+
+  // Tiles every row of the work-group sees whole need no mask.
+  const int p_last = P0 + t_last;
+  const int lo_last = (a.window > 0 && p_last + 1 > a.window) ? p_last + 1 - a.window : 0;
+  const bool rows_full = row0 + kRowsP <= rows;
+
+  for (int k0 = k_begin; k0 < k_end; k0 += kKeys) {
+    load_tile(k0);
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -177,19 +192,31 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const PrefillArgs a) 
       }
     }
 
-    // Masked, capped scores; the tile max of each query.
+    // Masked, capped scores; the tile max of each query.  A tile inside
+    // every row's visible range (the common case) skips the mask.
     float sv[8];
     float mt = -INFINITY;
+    if (rows_full && k0 >= lo_last && k0 + kKeys - 1 <= p_first) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + mb * 16 + 4 * quad + j;
-        const bool vis = row_ok && key >= my_lo && key <= my_p;
-        const float x = vis ? capped(s[mb][j], cap, cap_c, cap_inv) : -INFINITY;
-        sv[mb * 4 + j] = x;
-        mt = fmaxf(mt, x);
-      }
+        for (int j = 0; j < 4; ++j) {
+          const float x = capped(s[mb][j], cap, cap_c, cap_inv);
+          sv[mb * 4 + j] = x;
+          mt = fmaxf(mt, x);
+        }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = k0 + mb * 16 + 4 * quad + j;
+          const bool vis = row_ok && key >= my_lo && key <= my_p;
+          const float x = vis ? capped(s[mb][j], cap, cap_c, cap_inv) : -INFINITY;
+          sv[mb * 4 + j] = x;
+          mt = fmaxf(mt, x);
+        }
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m, mt);
@@ -205,31 +232,38 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const PrefillArgs a) 
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
     l = l * alpha + ps;
+    const bool grew = m_new > m;
     m = m_new;
 
     // Rescale the accumulator: its rows are queries 4*quad + j, whose alpha
-    // lives in lane 4*quad + j.
+    // lives in lane 4*quad + j.  Skipped when no query's max grew (every
+    // alpha is 1, or 0 for a query with no key yet, whose row is still 0).
+    if (__builtin_amdgcn_ballot_w64(grew) != 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float aj = __shfl(alpha, 4 * quad + j);
+      for (int j = 0; j < 4; ++j) {
+        const float aj = __shfl(alpha, 4 * quad + j);
 #pragma unroll
-      for (int n = 0; n < NB; ++n) o[n][j] *= aj;
+        for (int n = 0; n < NB; ++n) o[n][j] *= aj;
+      }
     }
 
     // O += P V.  A operand: lane holds P[qi][k = 8*quad + e], where k < 4 of
     // the lane's group maps to key 4*quad + e and k >= 4 to key 16 + 4*quad +
-    // (e - 4) (the same keys the lane's S^T registers hold); the B operand
-    // reads V rows in the same order.
+    // (e - 4) (the same keys the lane's S^T registers hold).  The B operand
+    // needs V at those keys in dim n*16 + qi: two transposing LDS reads
+    // (ds_read_b64_tr_b16).  Within each 16-lane group, the reading lane s
+    // points at 4 dims (n*16 + 4*(s%4) ..) of key base + s/4, and lane i
+    // receives dim n*16 + i of keys base .. base + 3.
     bf16x8 ph, pl;
     split8(p, ph, pl);
+    const int tr_row = 4 * quad + (qi >> 2), tr_col = 4 * (qi & 3);
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      bf16x8 vb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = (e < 4) ? 4 * quad + e : 16 + 4 * quad + (e - 4);
-        vb[e] = __builtin_bit_cast(__bf16, vs[r * LS + n * 16 + qi]);
-      }
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vs[tr_row * LS + n * 16 + tr_col]));
+      const s16x4 v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vs[(16 + tr_row) * LS + n * 16 + tr_col]));
+      const s16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, vv);
       o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, o[n], 0, 0, 0);
       o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[n], 0, 0, 0);
     }
