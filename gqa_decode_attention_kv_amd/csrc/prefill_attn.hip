@@ -75,8 +75,13 @@ __device__ inline void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
   }
 }
 
-template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(256) void prefill_attn_kernel(const PrefillArgs a) {
+// amdgpu_waves_per_eu(2, 2): a register budget of 256 per lane.  Without it
+// the allocator kept the output accumulator in AGPRs and copied it to VGPRs
+// and back on every tile (64 moves per 32 keys); with it every instantiation
+// stays in VGPRs (d128: 122, which still runs four waves per SIMD).
+template <int D, int G, bool PAGED, bool CAP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(
+    const PrefillArgs a) {
   constexpr int KSTEPS = D / 32;  // k-steps of the score product
   constexpr int NB = D / 16;      // 16-column blocks of the output
   constexpr int LS = D + 8;       // K and V tiles: LDS row stride in bf16 elements (16-byte pad)
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const PrefillArgs a) 
       split8(x, qh[s], ql[s]);
     }
   }
-  const bool cap = a.softcap > 0.0f;
+  constexpr bool cap = CAP;  // softcap (the tanh clip) compiled in or out
   const float cap_c = a.softcap, cap_inv = cap ? 1.0f / a.softcap : 0.0f;
 
   f32x4 o[NB];
@@ -290,13 +295,21 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const PrefillArgs a) 
   }
 }
 
+template <int D, int G, bool PAGED>
+void launch_dgp(const dim3& grid, const PrefillArgs& a, hipStream_t stream) {
+  if (a.softcap > 0.0f)
+    hipLaunchKernelGGL((prefill_attn_kernel<D, G, PAGED, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_attn_kernel<D, G, PAGED, false>), grid, dim3(256), 0, stream, a);
+}
+
 template <int D, int G>
 hipError_t launch_dg(int B, const PrefillArgs& a, hipStream_t stream) {
   const dim3 grid((a.T * G + kRowsP - 1) / kRowsP, a.Hkv, B);
   if (a.block_table != nullptr)
-    hipLaunchKernelGGL((prefill_attn_kernel<D, G, true>), grid, dim3(256), 0, stream, a);
+    launch_dgp<D, G, true>(grid, a, stream);
   else
-    hipLaunchKernelGGL((prefill_attn_kernel<D, G, false>), grid, dim3(256), 0, stream, a);
+    launch_dgp<D, G, false>(grid, a, stream);
   return hipGetLastError();
 }
 
