@@ -44,7 +44,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+PREFILL_SRCS = [os.path.join(CSRC, f) for f in ("prefill_attn.hip", "launch.h")]
+
+
+def prefill_source_hash() -> str:
+    h = hashlib.sha256()
+    for path in PREFILL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, source_hash=None):
     """HBM bytes per partial-kernel launch from the committed counter runs, if
     they were taken on the current kernel source."""
     try:
@@ -53,7 +64,8 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     rec = t.get(workload)
-    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    want = source_hash if source_hash is not None else kernel_source_hash()
+    if not rec or rec.get("kernel_source_sha256_16") != want:
         return None
     return rec.get("bytes_per_launch")
 
@@ -222,7 +234,9 @@ def prefill_main(args) -> int:
         "roofline": {"kernel": "prefill_attn_kernel", "bound": "mfma",
                      "achieved": round(tflops_attn, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops_attn / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "traffic": measured_traffic(name, prefill_source_hash()),
+                     "algorithmic_flops_per_launch": flops,
+                     "kernel_source_sha256_16": prefill_source_hash(),
                      "note": "the kernel issues twice the algorithmic matrix flops (q and the "
                              "softmax weights enter as a bf16 high part and remainder)"},
     }
@@ -277,6 +291,16 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_probe:
+        # A plain 1 GiB device copy: the counters' reading of it calibrates
+        # FETCH_SIZE and WRITE_SIZE against known bytes.
+        n = 1 << 28  # 1 GiB of f32
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: copy probe moved {n * 4} bytes each way", file=sys.stderr, flush=True)
+        del src, dst
     if args.prefill:
         return prefill_main(args)
     name = args.workload or W.HEADLINE
@@ -288,15 +312,6 @@ def main() -> int:
     paged = W.make_paged(inputs, args.paged) if args.paged else None
     st = DeviceStep(inputs, split_size=args.split_size, paged=paged)
     kv_bytes = w.kv_bytes()
-
-    if args.copy_probe:
-        n = 1 << 28  # 1 GiB of f32
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"bench: copy probe moved {n * 4} bytes each way", file=sys.stderr, flush=True)
-        del src, dst
 
     # Warm-up: at least --warmup steps and --min-warmup-s seconds.  The first
     # tens of milliseconds of GPU work in a process can run several times
