@@ -44,7 +44,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-PREFILL_SRCS = [os.path.join(CSRC, f) for f in ("prefill_attn.hip", "launch.h")]
+PREFILL_SRCS = [os.path.join(CSRC, f) for f in ("prefill_attn.hip", "prefill_args.h")]
 
 
 def prefill_source_hash() -> str:

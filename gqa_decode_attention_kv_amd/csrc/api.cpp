@@ -18,6 +18,7 @@
 #include <string>
 
 #include "launch.h"
+#include "prefill_args.h"
 
 namespace {
 

@@ -121,26 +121,8 @@ struct StepArgs {
   int32_t* counters;   // [B][Hkv] arrival counters: zero on entry, zero on exit
 };
 
-// Chunk attention (prefill): the T chunk queries of sequence b sit at
-// positions len[b] - T .. len[b] - 1, their keys already in the cache; query
-// t attends the keys [lo_t, len[b] - T + t] (lo_t from the window).
-struct PrefillArgs {
-  int32_t H, Hkv, cap, T, window;
-  const void* k;
-  const void* v;
-  const float* q;      // [B][T][H][D], rotated queries
-  const float* sinks;  // [H] or nullptr
-  float* out;          // [B][T][H][D]
-  float q_mul;         // multiplies q on load: scale*log2(e), or scale with a softcap
-  float softcap;
-  const int32_t* block_table;  // paged cache, or nullptr
-  int32_t block_size, log2_bs, max_blocks, num_blocks;
-  int32_t len[kMaxBatch];
-};
-
 hipError_t launch_kv_produce(const ProduceArgs& a, hipStream_t stream);
-// One work-group per (64 query rows, kv head, sequence); bf16 K and V.
-hipError_t launch_prefill_attn(int D, int G, int B, const PrefillArgs& a, hipStream_t stream);
+
 // One wave per (work item, kv head): t.work_prefix[t.n_seq] * Hkv waves.
 hipError_t launch_decode_partial(int D, int G, int k_dtype, int v_dtype, const AttnArgs& a,
                                  hipStream_t stream);

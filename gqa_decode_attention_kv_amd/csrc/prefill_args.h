@@ -1,0 +1,29 @@
+// Interface between the C-ABI host code (api.cpp) and the chunk (prefill)
+// attention kernel (prefill_attn.hip).  Passed to the kernel by value.
+#pragma once
+
+#include "launch.h"
+
+namespace uaii {
+
+// Chunk attention (prefill): the T chunk queries of sequence b sit at
+// positions len[b] - T .. len[b] - 1, their keys already in the cache; query
+// t attends the keys [lo_t, len[b] - T + t] (lo_t from the window).
+struct PrefillArgs {
+  int32_t H, Hkv, cap, T, window;
+  const void* k;
+  const void* v;
+  const float* q;      // [B][T][H][D], rotated queries
+  const float* sinks;  // [H] or nullptr
+  float* out;          // [B][T][H][D]
+  float q_mul;         // multiplies q on load: scale*log2(e), or scale with a softcap
+  float softcap;
+  const int32_t* block_table;  // paged cache, or nullptr
+  int32_t block_size, log2_bs, max_blocks, num_blocks;
+  int32_t len[kMaxBatch];
+};
+
+// One work-group per (64 query rows, kv head, sequence); bf16 K and V.
+hipError_t launch_prefill_attn(int D, int G, int B, const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace uaii

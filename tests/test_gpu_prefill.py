@@ -6,7 +6,8 @@ computes their causal attention on the matrix cores.
   that no other row changed) and the rotated queries; they cover head dims
   64/128/256, GQA ratios 1-8, empty and non-empty caches, ragged batches,
   windows (1, inside the chunk, wider than the context), softcap, sinks,
-  one-token chunks, several key tiles and the paged layout.
+  one-token chunks, several key tiles, the paged layout, and both kernel
+  shapes (16 and 32 query rows per wave).
 * The prefill workloads run at full size with sampled (sequence, token,
   head) outputs and every produced row.
 * The chunk's attention agrees with the decode path run token by token.
@@ -63,6 +64,12 @@ SMALL = [
          np.random.default_rng(12).integers(16, 201, 32), rope=LLAMA3, seed=12),
     case("d128-g4-paged-bs16", 128, 4, 2, 100, [333, 120], window=200, seed=13, bs=16),
     case("d64-g2-paged-bs64-sink", 64, 2, 2, 50, [50, 260], sink=True, seed=14, bs=64),
+    # Grids of at least 512 work-groups run with 32 rows per wave: ragged
+    # row tails, windows, sinks, softcap and paging on that path too.
+    case("d128-g4-b32-two-blocks-ragged", 128, 4, 8, 72,
+         np.random.default_rng(15).integers(72, 301, 32), window=100, sink=True, seed=15),
+    case("d64-g8-b32-two-blocks-paged", 64, 8, 8, 40,
+         np.random.default_rng(16).integers(40, 201, 32), softcap=30.0, seed=16, bs=16),
 ]
 
 
