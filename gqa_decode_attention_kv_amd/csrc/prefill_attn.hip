@@ -24,9 +24,9 @@
 //     flash attention): each tile is read from HBM once per work-group.
 //   * Key tiles of 32 rows of K and V are staged in LDS by the whole
 //     work-group with 16-byte loads (padded rows, so the matrix reads below
-//     do not collide on banks).  (Loading the next tile into registers
-//     during the current tile's products was measured slower: the extra
-//     registers cost a wave per SIMD.)
+//     do not collide on banks).  The next tile's loads go to registers while
+//     the current tile's products run (16 registers at d128; with two query
+//     blocks per wave the kernel runs two waves per SIMD either way).
 //   * Each wave owns 32 query rows (16 at d256 or in small grids) and
 //     computes the transposed
 //     scores S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (two 16-key blocks);
@@ -194,8 +194,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  load_tile(k_begin);
   for (int k0 = k_begin; k0 < k_end; k0 += kKeys) {
-    load_tile(k0);
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -205,6 +205,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       *reinterpret_cast<u32x4*>(&vs[r * LS + col]) = vreg[i];
     }
     __syncthreads();
+    // The next tile's loads are in flight during this tile's products.
+    if (k0 + kKeys < k_end) load_tile(k0 + kKeys);
 
     // S^T for keys k0 + mb*16 + (0..15) against the wave's query blocks:
     // lane holds keys k0 + mb*16 + 4*quad + j of query qi of block q.
