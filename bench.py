@@ -44,7 +44,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-PREFILL_SRCS = [os.path.join(CSRC, f) for f in ("prefill_attn.hip", "prefill_args.h")]
+PREFILL_SRCS = [os.path.join(CSRC, f) for f in ("prefill_kernel.h", "prefill_attn.hip", "prefill_args.h")]
 
 
 def prefill_source_hash() -> str:
@@ -155,9 +155,9 @@ def prefill_cpu_baseline(inputs, q, min_seconds: float = 10.0) -> dict:
               for _ in range(threads)]
 
         def one(x):
-            o.prefill(q=q, cache_k=inputs.cache_k, cache_v=inputs.cache_v, k_dtype=w.k_dtype,
-                      v_dtype=w.v_dtype, seq_lens=lens, window=w.window, softcap=w.softcap,
-                      sinks=inputs.sinks, triples=[x])
+            o.prefill(q=q, cache_k=inputs.cache_k, cache_v=inputs.cache_v, v_scale=inputs.v_scale,
+                      k_scale=inputs.k_scale, k_dtype=w.k_dtype, v_dtype=w.v_dtype, seq_lens=lens,
+                      window=w.window, softcap=w.softcap, sinks=inputs.sinks, triples=[x])
 
         t0 = time.perf_counter()
         with ThreadPoolExecutor(threads) as ex:
@@ -226,7 +226,9 @@ def prefill_main(args) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "batch": w.batch, "chunk": w.chunk,
                    "ctx": int(inputs.seq_lens.max()), "n_heads": w.n_heads,
-                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "kv_cache": "bf16/bf16",
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "kv_cache": {(1, 1): "bf16/bf16", (1, 2): "bf16/int8(vq8)",
+                                (2, 2): "q8"}[(w.k_dtype, w.v_dtype)],
                    "window": w.window, "softcap": w.softcap, "parallelism": "single-gpu"},
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "flops_per_step": flops,
@@ -244,14 +246,17 @@ def prefill_main(args) -> int:
         import oracle
         o = oracle.load()
         ck, cv = inputs.cache_k.copy(), inputs.cache_v.copy()
+        vs = inputs.v_scale.copy() if inputs.v_scale is not None else None
+        ks = inputs.k_scale.copy() if inputs.k_scale is not None else None
         norm = None
         if w.qk_norm.enabled:
             norm = dict(enabled=True, eps=w.qk_norm.eps, offset=w.qk_norm.offset,
                         w_q=inputs.w_q, w_k=inputs.w_k)
         q = o.kv_produce_chunk(rope=w.rope.as_dict(), norm=norm, q_in=inputs.q_in,
                                k_in=inputs.k_in, v_in=inputs.v_in, start_positions=inputs.start,
-                               k_dtype=w.k_dtype, v_dtype=w.v_dtype, cache_k=ck, cache_v=cv)
-        inputs.cache_k, inputs.cache_v = ck, cv
+                               k_dtype=w.k_dtype, v_dtype=w.v_dtype, cache_k=ck, cache_v=cv,
+                               v_scale=vs, k_scale=ks)
+        inputs.cache_k, inputs.cache_v, inputs.v_scale, inputs.k_scale = ck, cv, vs, ks
         result["cpu_baseline"] = prefill_cpu_baseline(inputs, q)
     print(json.dumps(result), flush=True)
     return 0

@@ -467,9 +467,12 @@ uaii_status uaii_prefill_attn(const uaii_attn_shape* shape, const uaii_kv_cache*
   if (st != UAII_OK) return st;
   st = check_cache(fn, cache);
   if (st != UAII_OK) return st;
-  REQUIRE(cache->k_dtype == UAII_BF16 && cache->v_dtype == UAII_BF16, kNotImpl,
-          "prefill over k_dtype=%d, v_dtype=%d is not supported (supported: bf16 keys and values, "
-          "k_dtype=v_dtype=1)",
+  REQUIRE((cache->k_dtype == UAII_BF16 && cache->v_dtype == UAII_BF16) ||
+              (cache->k_dtype == UAII_BF16 && cache->v_dtype == UAII_I8) ||
+              (cache->k_dtype == UAII_I8 && cache->v_dtype == UAII_I8),
+          kNotImpl,
+          "prefill over k_dtype=%d, v_dtype=%d is not supported (supported: bf16 keys with bf16 or int8 "
+          "values, or int8 keys and values: (1,1), (1,2), (2,2))",
           cache->k_dtype, cache->v_dtype);
   REQUIRE(n_tokens >= 1, kInvalid, "n_tokens=%d is invalid (must be >= 1)", n_tokens);
   REQUIRE(n_tokens <= (1 << 20), kNotImpl, "n_tokens=%d is not supported (supported: 1..%d per call)",
@@ -505,6 +508,8 @@ uaii_status uaii_prefill_attn(const uaii_attn_shape* shape, const uaii_kv_cache*
   a.q = q;
   a.sinks = sinks;
   a.out = out;
+  a.k_scale = cache->k_dtype == UAII_I8 ? cache->k_scale : nullptr;
+  a.v_scale = cache->v_dtype == UAII_I8 ? cache->v_scale : nullptr;
   const float s = static_cast<float>(want);
   a.q_mul = softcap > 0.0f ? s : s * 1.4426950408889634f;
   a.softcap = softcap;
@@ -518,8 +523,8 @@ uaii_status uaii_prefill_attn(const uaii_attn_shape* shape, const uaii_kv_cache*
   }
   for (int b = 0; b < shape->batch; ++b) a.len[b] = seq_lens[b];
   const int G = shape->n_heads / shape->n_kv_heads;
-  return device_status(fn, uaii::launch_prefill_attn(shape->head_dim, G, shape->batch, a,
-                                                     static_cast<hipStream_t>(stream)));
+  return device_status(fn, uaii::launch_prefill_attn(shape->head_dim, G, shape->batch, cache->k_dtype,
+                                                     cache->v_dtype, a, static_cast<hipStream_t>(stream)));
 }
 
 uaii_status uaii_decode_step(const uaii_attn_shape* shape, const uaii_rope* rope, const uaii_qk_norm* qk_norm,

@@ -171,6 +171,10 @@ class DevicePrefill:
         self.v_in = _dev(inputs.v_in, device)
         self.cache_k = _dev(paged.pool_k if paged else inputs.cache_k, device)
         self.cache_v = _dev(paged.pool_v if paged else inputs.cache_v, device)
+        src_s = paged.pool_scale if paged else inputs.v_scale
+        src_ks = paged.pool_k_scale if paged else inputs.k_scale
+        self.v_scale = _dev(src_s, device) if src_s is not None else None
+        self.k_scale = _dev(src_ks, device) if src_ks is not None else None
         self.block_table = _dev(paged.block_table, device) if paged else None
         self.sinks = _dev(inputs.sinks, device) if inputs.sinks is not None else None
         self.w_q = _dev(inputs.w_q, device) if inputs.w_q is not None else None
@@ -184,13 +188,15 @@ class DevicePrefill:
         n = w.qk_norm
         self.qk_norm = (B.QKNorm(1, n.eps, n.offset, self.w_q.data_ptr(), self.w_k.data_ptr())
                         if n.enabled else None)
+        vs_ptr = self.v_scale.data_ptr() if self.v_scale is not None else None
+        ks_ptr = self.k_scale.data_ptr() if self.k_scale is not None else None
         if paged:
             self.cache = B.KVCache(w.k_dtype, w.v_dtype, paged.capacity, self.cache_k.data_ptr(),
-                                   self.cache_v.data_ptr(), None, self.block_table.data_ptr(),
-                                   paged.block_size, paged.max_blocks, paged.num_blocks, None)
+                                   self.cache_v.data_ptr(), vs_ptr, self.block_table.data_ptr(),
+                                   paged.block_size, paged.max_blocks, paged.num_blocks, ks_ptr)
         else:
             self.cache = B.KVCache(w.k_dtype, w.v_dtype, w.capacity, self.cache_k.data_ptr(),
-                                   self.cache_v.data_ptr(), None, None, 0, 0, 0, None)
+                                   self.cache_v.data_ptr(), vs_ptr, None, 0, 0, 0, ks_ptr)
         self.scale = 1.0 / math.sqrt(d)
 
     @staticmethod

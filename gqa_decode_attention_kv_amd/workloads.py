@@ -209,6 +209,12 @@ PREFILL = {
                                                   ("fixed", 8192), 8192, BF16, BF16,
                                                   Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0,
                                                        8192), seed=(23,), chunk=512),
+    # The Qwen3 shape's vq8 cache (bf16 keys, int8 values with an f32 scale
+    # per token): a 512-token chunk appended to 15872 cached tokens.
+    "prefill-qwen3-vq8-b4-c512-ctx16k": Workload("prefill-qwen3-vq8-b4-c512-ctx16k", 4, 32, 8, 128,
+                                                 ("fixed", 16384), 16384, BF16, I8,
+                                                 Rope(NEOX, PLAIN, 1000000.0),
+                                                 QKNorm(True, 1e-6, 0, 1.0, 0.1), seed=(25,), chunk=512),
     "prefill-gemma2-local-b2-c1024": Workload("prefill-gemma2-local-b2-c1024", 2, 16, 8, 256,
                                               ("fixed", 8192), 8192, BF16, BF16,
                                               Rope(NEOX, PLAIN, 10000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),

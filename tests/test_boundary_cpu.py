@@ -338,8 +338,11 @@ def test_kv_produce_chunk_refusals(case):
 @host_only
 @pytest.mark.parametrize("case", [
     ("f32 cache", lambda: prefill(ca=cache(kd=B.F32, vd=B.F32)), NI,
-     ["prefill over k_dtype=0, v_dtype=0 is not supported", "bf16"]),
-    ("vq8 cache", lambda: prefill(ca=cache(vd=B.I8, s=FAKE)), NI, ["v_dtype=2"]),
+     ["prefill over k_dtype=0, v_dtype=0 is not supported", "(1,1), (1,2), (2,2)"]),
+    ("bf16 keys, f32 values", lambda: prefill(ca=cache(kd=B.BF16, vd=B.F32)), NI, ["v_dtype=0"]),
+    ("f32 keys, int8 values", lambda: prefill(ca=cache(kd=B.F32, vd=B.I8, s=FAKE)), NI,
+     ["k_dtype=0, v_dtype=2"]),
+    ("vq8 without scales", lambda: prefill(ca=cache(vd=B.I8)), INV, ["v_scale is NULL"]),
     ("len < n_tokens", lambda: prefill(lens=(5, 20)), INV, ["seq_lens[0]=5", "n_tokens=8"]),
     ("len > cap", lambda: prefill(lens=(65, 20)), INV, ["seq_lens[0]=65"]),
     ("n_tokens 0", lambda: prefill(n=0), INV, ["n_tokens=0"]),
@@ -360,6 +363,8 @@ def test_prefill_attn_refusals(case):
 @host_only
 def test_prefill_valid_calls_reach_the_launch():
     for fn in (lambda: prefill(), lambda: prefill(sinks=FAKE, window=3, softcap=5.0),
+               lambda: prefill(ca=cache(vd=B.I8, s=FAKE)),
+               lambda: prefill(ca=cache(kd=B.I8, vd=B.I8, s=FAKE, ks=FAKE)),
                lambda: produce_chunk()):
         with pytest.raises(B.UaiiError) as ei:
             fn()
