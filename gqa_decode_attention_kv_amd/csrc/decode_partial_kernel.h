@@ -204,7 +204,7 @@ __device__ inline const StepArgs* step_of(const StepArgs& s) { return &s; }
 // amdgpu_waves_per_eu(2, 8): at least two waves per SIMD.  Without the hint
 // the allocator spends registers freely (the vq8 kernel spilled into AGPRs at
 // one wave per SIMD); with it the bf16 d128 kernel fits three waves per SIMD.
-template <int D, int G, int KT, int VT, bool PAGED, bool FUSED>
+template <int D, int G, int KT, int VT, bool PAGED, bool FUSED, bool ILV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 decode_partial_kernel(const KernelArgs<FUSED> args) {
   const AttnArgs& a = attn_of(args);
@@ -242,9 +242,9 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
 
   // Work item (work index w, kv head); w names (sequence, split).  Alone,
   // each wave of the work-group takes its own item; cooperatively, the
-  // work-group takes one item and its waves take consecutive quarters of
-  // the split's rows (part = wave), merged through LDS at the end.
-  const bool coop = a.coop != 0;
+  // work-group takes one item and its waves (part = wave) share the split's
+  // rows as described below, merged through LDS at the end.
+  const bool coop = ILV || a.coop != 0;
   const int item = coop ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) * kWaves + wave;
   const int part = coop ? wave : 0;
   const int total = a.t.work_prefix[a.t.n_seq] * a.Hkv;
@@ -264,11 +264,50 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   const bool has_new = FUSED && (sigma + 1) * a.split_size >= L;
   int r0 = max(sigma * a.split_size, a.t.lo[b]);
   int r1 = min((sigma + 1) * a.split_size, FUSED ? L - 1 : L);
-  if (coop) {  // this wave's quarter, in whole 16-row tiles (possibly empty)
-    const int piece = ((max(r1 - r0, 0) + kWaves - 1) / kWaves + 15) & ~15;
-    r0 = min(r0 + part * piece, r1);
-    r1 = min(r0 + piece, r1);
+  // A wave walks rows [r0, r1) in chunks; row x of a chunk that starts at
+  // row c is cache row chunk_row(c) + xrow(x).  Alone, a wave reads its rows
+  // in order (chunk_row(c) = c, xrow(x) = x).  Cooperative work-groups split
+  // the item among their four waves:
+  //   * ILV (contiguous caches): the waves interleave blocks of BR rows, the
+  //     rows of one load (wave `part` takes blocks part, part + 4, ...), so
+  //     the work-group reads the split as one sequential stream, measured
+  //     faster than four separate streams.  The wave's own rows become
+  //     local rows [0, n), local row l being cache row
+  //     R0 + 4 BR (l / BR) + BR part + l % BR;
+  //   * otherwise (paged caches, the fused step): each wave takes a quarter
+  //     in whole 16-row tiles.
+  constexpr int BR = KRPL > VRPL ? KRPL : VRPL;
+  const int R0 = r0;
+  if (coop) {
+    const int N = max(r1 - r0, 0);
+    if constexpr (ILV) {
+      const int nb = (N + BR - 1) / BR;  // blocks of the item, the last one possibly partial
+      const int mine = nb > part ? (nb - 1 - part) / kWaves + 1 : 0;
+      int n = mine * BR;
+      if (mine > 0 && (nb - 1) % kWaves == part) n -= nb * BR - N;
+      r0 = 0;
+      r1 = n;
+    } else {  // this wave's quarter, in whole 16-row tiles (possibly empty)
+      const int piece = ((N + kWaves - 1) / kWaves + 15) & ~15;
+      r0 = min(r0 + part * piece, r1);
+      r1 = min(r0 + piece, r1);
+    }
   }
+  // Chunk starts are multiples of kRowsPerChunk local rows, hence of BR.
+  auto chunk_row = [&](int c) -> int {
+    if constexpr (ILV) {
+      return R0 + kWaves * c + BR * part;
+    } else {
+      return c;
+    }
+  };
+  auto xrow = [&](int x) -> int {
+    if constexpr (ILV) {
+      return x + static_cast<int>(static_cast<uint32_t>(x) / BR) * (BR * (kWaves - 1));
+    } else {
+      return x;
+    }
+  };
   const bool new_here = has_new && part == 0;
 
   // Contiguous: the (b, kvh) slab starts at row slab of the cache.  Paged:
@@ -417,8 +456,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
     const int TV0 = PAGED ? (a0 & ~(VRPL - 1)) : a0;
     const int nk = (a0 + nrows - TK0 + KRPL - 1) / KRPL;  // K tiles of KRPL rows
     const int nv = (a0 + nrows - TV0 + VRPL - 1) / VRPL;  // V tiles of VRPL rows
-    const char* kblk = kbase + static_cast<int64_t>(a0) * (D * KB);
-    const char* vblk = vbase + static_cast<int64_t>(a0) * (D * VB);
+    const char* kblk = kbase + static_cast<int64_t>(chunk_row(a0)) * (D * KB);
+    const char* vblk = vbase + static_cast<int64_t>(chunk_row(a0)) * (D * VB);
     // Paged: lane j holds the physical id of logical block j0 + j (a chunk
     // spans at most 512 / 16 + 1 blocks); ids outside the pool are clamped.
     int j0 = 0, idreg = 0;
@@ -441,7 +480,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         const int row = min(max(R + kr, a0), last);
         return tile_base(a.k, R, D * KB) + static_cast<uint32_t>((row - R) * (D * KB) + kc * KLB);
       } else {
-        return kblk + static_cast<uint32_t>(min(t * KRPL + kr, nrows - 1) * (D * KB) + kc * KLB);
+        return kblk + static_cast<uint32_t>(xrow(min(t * KRPL + kr, nrows - 1)) * (D * KB) + kc * KLB);
       }
     };
     auto vaddr = [&](int t) -> const char* {
@@ -450,7 +489,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         const int row = min(max(R + vr, a0), last);
         return tile_base(a.v, R, D * VB) + static_cast<uint32_t>((row - R) * (D * VB) + vc * VLB);
       } else {
-        return vblk + static_cast<uint32_t>(min(t * VRPL + vr, nrows - 1) * (D * VB) + vc * VLB);
+        return vblk + static_cast<uint32_t>(xrow(min(t * VRPL + vr, nrows - 1)) * (D * VB) + vc * VLB);
       }
     };
 
@@ -461,7 +500,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         const int pid = __shfl(idreg, (row >> a.log2_bs) - j0);
         return pool[(static_cast<int64_t>(pid) * a.Hkv + kvh) * a.block_size + (row & (a.block_size - 1))];
       } else {
-        return contiguous[a0 + min(lane + 64 * i, nrows - 1)];
+        return contiguous[chunk_row(a0) + xrow(min(lane + 64 * i, nrows - 1))];
       }
     };
     // int8 caches: the chunk's per-token scales are requested now; key scales
@@ -754,12 +793,22 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   }
 }
 
+// Cooperative launches of the partials over contiguous caches use the
+// interleaved instantiation (ILV); everything else the plain one.
 template <int D, int G, int KT, int VT, bool PAGED, bool FUSED>
 hipError_t launch_one(const KernelArgs<FUSED>& args, hipStream_t stream) {
   const AttnArgs& a = attn_of(args);
   const int items = a.t.work_prefix[a.t.n_seq] * a.Hkv;
   const dim3 grid(a.coop ? items : (items + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL((decode_partial_kernel<D, G, KT, VT, PAGED, FUSED>), grid, dim3(kThreads), 0, stream, args);
+  if constexpr (!PAGED && !FUSED) {
+    if (a.coop) {
+      hipLaunchKernelGGL((decode_partial_kernel<D, G, KT, VT, PAGED, FUSED, true>), grid, dim3(kThreads), 0, stream,
+                         args);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_partial_kernel<D, G, KT, VT, PAGED, FUSED, false>), grid, dim3(kThreads), 0, stream,
+                     args);
   return hipGetLastError();
 }
 

@@ -142,20 +142,20 @@ WORKLOADS = {
                                    split_size=384, seed=(3,)),
     "qwen3-vq8": Workload("qwen3-vq8", 16, 32, 8, 128, ("fixed", 16384), 16384, BF16, I8,
                           Rope(NEOX, PLAIN, 1000000.0),
-                          QKNorm(True, 1e-6, 0, 1.0, 0.1), split_size=1024, seed=(4,)),
+                          QKNorm(True, 1e-6, 0, 1.0, 0.1), split_size=4096, seed=(4,)),
     "gemma2-local": Workload("gemma2-local", 8, 16, 8, 256, ("fixed", 32768), 32768, BF16, BF16,
                              Rope(NEOX, PLAIN, 10000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),
-                             window=4096, softcap=50.0, split_size=128, seed=(5, 0)),
+                             window=4096, softcap=50.0, split_size=512, seed=(5, 0)),
     "gemma2-global": Workload("gemma2-global", 8, 16, 8, 256, ("fixed", 32768), 32768, BF16, BF16,
                               Rope(NEOX, PLAIN, 1000000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),
-                              window=0, softcap=50.0, split_size=1024, seed=(5, 1)),
+                              window=0, softcap=50.0, split_size=4096, seed=(5, 1)),
     # The measured workload: B=32 sequences of 8192 keys, 32/8 heads, d=128, bf16 KV.
-    # Split size 1024 (tuned): 8 splits per sequence, 2048 waves, one per wave slot
-    # of the GPU at the partial kernel's occupancy.
+    # Split size 4096 (tuned): 2 splits per sequence, 512 work items, each taken
+    # by one cooperative work-group of four waves (two work-groups per CU).
     "llama3.1-8b-b32-ctx8k": Workload("llama3.1-8b-b32-ctx8k", 32, 32, 8, 128, ("fixed", 8192),
                                       8192, BF16, BF16,
                                       Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
-                                      split_size=1024, seed=(6,)),
+                                      split_size=4096, seed=(6,)),
     # The headline shape with the q8 cache (int8 keys and values, one f32
     # scale each per token per kv head).
     "llama3.1-8b-q8": Workload("llama3.1-8b-q8", 32, 32, 8, 128, ("fixed", 8192), 8192, I8, I8,
@@ -177,10 +177,10 @@ WORKLOADS = {
     # theta 1e4 and a 1024-key window.
     "gemma3-27b-global": Workload("gemma3-27b-global", 8, 32, 16, 128, ("fixed", 32768), 32768,
                                   BF16, BF16, Rope(NEOX, LINEAR, 1000000.0, 8.0),
-                                  QKNorm(True, 1e-6, 1, 0.0, 0.1), split_size=1024, seed=(9, 0)),
+                                  QKNorm(True, 1e-6, 1, 0.0, 0.1), split_size=8192, seed=(9, 0)),
     "gemma3-27b-local": Workload("gemma3-27b-local", 8, 32, 16, 128, ("fixed", 32768), 32768,
                                  BF16, BF16, Rope(NEOX, PLAIN, 10000.0),
-                                 QKNorm(True, 1e-6, 1, 0.0, 0.1), window=1024, split_size=128,
+                                 QKNorm(True, 1e-6, 1, 0.0, 0.1), window=1024, split_size=256,
                                  seed=(9, 1)),
 }
 
