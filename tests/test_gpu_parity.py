@@ -67,6 +67,18 @@ SMALL = [
          window=1500, softcap=30.0, seed=17),
     case("f32-d64-g2-softcap", 64, 2, 2, W.F32, W.F32, [500], 96, softcap=5.0, norm=1, seed=18),
     case("vq8-d256-g2-softcap", 256, 2, 2, W.BF16, W.I8, [900, 513], 512, softcap=50.0, seed=19),
+    # Long cooperative items (the four waves of a work-group interleave row
+    # blocks of one load each): more than one 512-row chunk per wave, ragged
+    # tails, a window that starts inside a split, and every block height
+    # (1 row at f32 d256 up to 8 at q8 d128 and bf16 d64 G8).
+    case("bf16-d128-g4-long-items", 128, 4, 2, W.BF16, W.BF16, [2999, 4097, 5000], 4096, seed=20),
+    case("vq8-d128-g4-long-items", 128, 4, 2, W.BF16, W.I8, [3001, 2050], 4096, norm=0, seed=21),
+    case("bf16-d256-g2-long-window", 256, 2, 2, W.BF16, W.BF16, [6000, 2300], 3000, window=5000,
+         softcap=50.0, seed=22),
+    case("q8-d128-g4-long-items", 128, 4, 2, W.I8, W.I8, [4500], 4096, seed=23),
+    case("f32-d64-g8-long-items", 64, 8, 1, W.F32, W.F32, [3333], 4096, seed=24),
+    case("f32-d256-g2-long-items", 256, 2, 1, W.F32, W.F32, [2500, 2049], 2048, seed=25),
+    case("bf16-d64-g8-long-items", 64, 8, 1, W.BF16, W.BF16, [2600, 31], 2600, seed=26),
 ]
 
 
