@@ -121,10 +121,13 @@ uaii_status check_cache(const char* fn, const uaii_kv_cache* c) {
 
 bool finite_pos(double x) { return std::isfinite(x) && x > 0.0; }
 
-// Visible keys [lo, L) and the splits [first, last] that intersect them.
+// Visible keys [lo, L) and the splits [first, last] that intersect them,
+// and the launch order of the splits (SeqTable: body splits first, then
+// the last splits by decreasing visible keys).
 void build_table(int B, const int32_t* lens, int32_t window, int32_t split, uaii::SeqTable* t) {
   std::memset(t, 0, sizeof *t);
-  int32_t prefix = 0;
+  int32_t prefix = 0, body = 0;
+  int32_t tail_rows[uaii::kMaxBatch];
   for (int b = 0; b < B; ++b) {
     const int32_t L = lens[b];
     const int32_t lo = (window > 0 && L > window) ? L - window : 0;
@@ -134,9 +137,16 @@ void build_table(int B, const int32_t* lens, int32_t window, int32_t split, uaii
     t->first_split[b] = first;
     t->work_prefix[b] = prefix;
     prefix += last - first + 1;
+    t->body_prefix[b] = body;
+    body += last - first;
+    tail_rows[b] = L - std::max(last * split, lo);
+    t->tail_order[b] = b;
   }
   t->work_prefix[B] = prefix;
+  t->body_prefix[B] = body;
   t->n_seq = B;
+  std::stable_sort(t->tail_order, t->tail_order + B,
+                   [&](int32_t x, int32_t y) { return tail_rows[x] > tail_rows[y]; });
 }
 
 uaii_status device_status(const char* fn, hipError_t e) {

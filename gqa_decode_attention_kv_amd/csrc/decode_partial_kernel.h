@@ -252,11 +252,18 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   // item is per work-group), so the one barrier below is reached by all or
   // none of a work-group's waves.
   if (item >= total) return;
+  // Work index w in launch order (SeqTable): body splits, then last splits.
   const int kvh = item % a.Hkv;
   const int w = item / a.Hkv;
-  int b = 0;
-  for (int i = 1; i < a.t.n_seq; ++i) b += (w >= a.t.work_prefix[i]) ? 1 : 0;
-  const int sigma = a.t.first_split[b] + (w - a.t.work_prefix[b]);
+  const int n_body = a.t.body_prefix[a.t.n_seq];
+  int b = 0, sigma = 0;
+  if (w < n_body) {
+    for (int i = 1; i < a.t.n_seq; ++i) b += (w >= a.t.body_prefix[i]) ? 1 : 0;
+    sigma = a.t.first_split[b] + (w - a.t.body_prefix[b]);
+  } else {
+    b = a.t.tail_order[w - n_body];
+    sigma = a.t.first_split[b] + (a.t.work_prefix[b + 1] - a.t.work_prefix[b]) - 1;
+  }
   // Cache rows [r0, r1) are read.  The fused step leaves out the new
   // token's slot L - 1: the split that holds it (has_new) merges it from
   // registers after its last chunk, in the wave of part 0.

@@ -14,16 +14,26 @@ constexpr int kMaxPairs = 128;  // rotation pairs of the largest head (d = 256)
 enum : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
 enum : int { kNeox = 0, kInterleaved = 1 };
 
-// Per-sequence schedule of one decode step.  Work item w of the partial
-// kernel belongs to sequence b with work_prefix[b] <= w < work_prefix[b + 1];
-// it is split first_split[b] + (w - work_prefix[b]).  Visible keys of b are
-// [lo[b], len[b]).
+// Per-sequence schedule of one decode step.  Sequence b has splits
+// first_split[b] .. first_split[b] + n_b - 1, n_b = work_prefix[b + 1] -
+// work_prefix[b] (the splits that hold visible keys, [lo[b], len[b])).
+//
+// Launch order of the partial kernel's work index w, longest first: the
+// "body" splits (all but the last of each sequence, whole splits apart from
+// a window's first one) come first, sequence by sequence, w in
+// [body_prefix[b], body_prefix[b + 1]) being split first_split[b] + w -
+// body_prefix[b]; then the last splits, which ragged lengths leave short,
+// w = body_prefix[n_seq] + k being the last split of sequence tail_order[k]
+// (sequences by the last split's visible keys, most first).  The hardware
+// dispatches work-groups in order, so the short items fill in at the end.
 struct SeqTable {
   int32_t n_seq;
   int32_t work_prefix[kMaxBatch + 1];
   int32_t first_split[kMaxBatch];
   int32_t lo[kMaxBatch];
   int32_t len[kMaxBatch];
+  int32_t body_prefix[kMaxBatch + 1];
+  int32_t tail_order[kMaxBatch];
 };
 
 struct ProduceArgs {

@@ -139,7 +139,7 @@ WORKLOADS = {
     "llama3.1-8b-ragged": Workload("llama3.1-8b-ragged", 32, 32, 8, 128, ("uniform", 512, 8192),
                                    8192, BF16, BF16,
                                    Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
-                                   split_size=384, seed=(3,)),
+                                   split_size=512, seed=(3,)),
     "qwen3-vq8": Workload("qwen3-vq8", 16, 32, 8, 128, ("fixed", 16384), 16384, BF16, I8,
                           Rope(NEOX, PLAIN, 1000000.0),
                           QKNorm(True, 1e-6, 0, 1.0, 0.1), split_size=4096, seed=(4,)),
