@@ -18,7 +18,13 @@
 //   * one wave64 per (sequence, kv head, split) work item, taken from a
 //     flattened per-sequence work table, so ragged batches and windows only
 //     launch waves that hold visible keys; four independent waves share a
-//     work-group but never synchronise (no barriers, no cross-wave merge);
+//     work-group but never synchronise (no barriers, no cross-wave merge).
+//     The table launches the items longest first (every sequence's body
+//     splits, then the last splits by decreasing length);
+//   * steps with fewer than 2048 items run cooperatively instead: the four
+//     waves of a work-group share one item, interleaving one-load row blocks
+//     on contiguous caches (one sequential stream per work-group) or taking
+//     quarters on paged ones, and merge their softmax states in LDS;
 //   * the G query heads that share the kv head are held in registers, so
 //     every K and V byte is read from HBM exactly once per group;
 //   * int8 values use 8-byte loads (see Elem);
