@@ -62,7 +62,29 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kKeys = 32;    // keys per tile
+// The softmax reference of a query moves only when a tile's max exceeds it
+// by more than this many powers of two (weights stay below 2^kSlack).
+constexpr float kSlack = 8.0f;
 constexpr float kLog2eP = 1.4426950408889634f;
+
+// max / sum of x over lanes l and l ^ 16, then over l and l ^ 32, with
+// gfx950's row swaps (v_permlane16_swap, v_permlane32_swap): swapping a
+// register with itself leaves {x[l], x[l ^ 16]} (resp. l ^ 32) in the two
+// results, in the same order in both lanes of a pair, so both get the same
+// value.  Plain VALU instead of an LDS permute.
+__device__ inline float pair_max_16_32(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float pair_sum_16_32(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline float capped(float s, bool cap, float c, float c_inv) {
   return cap ? c * tanhf(s * c_inv) * kLog2eP : s;
@@ -351,9 +373,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             mt = fmaxf(mt, x);
           }
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m[q], mt);
+      mt = pair_max_16_32(mt);
+      // m is a reference, not always the running max: it moves only when a
+      // tile's max exceeds it by more than kSlack (log2 units), so the
+      // weights stay below 2^kSlack and most tiles need no rescale.  The
+      // final normalisation divides by l, which carries the same reference.
+      const bool bump = mt > m[q] + kSlack;  // m = -inf: any visible key bumps
+      const float m_new = bump ? mt : m[q];
       const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // no key yet: keep weights 0
       const float alpha = __builtin_amdgcn_exp2f(m[q] - m_use);  // m = -inf gives 0
       float p[8];
@@ -363,16 +389,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         p[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
         ps += p[e];
       }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
+      ps = pair_sum_16_32(ps);
       l[q] = l[q] * alpha + ps;
-      const bool grew = m_new > m[q];
       m[q] = m_new;
       // Rescale the accumulator: its rows are queries 4*quad + j, whose
-      // alpha lives in lane 4*quad + j.  Skipped when no query's max grew
-      // (every alpha is 1, or 0 for a query with no key yet, whose row is
-      // still 0).
-      if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+      // alpha lives in lane 4*quad + j.  Skipped when no query's reference
+      // moved (every alpha is 1, or 0 for a query with no key yet, whose row
+      // is still 0).
+      if (__builtin_amdgcn_ballot_w64(bump) != 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float aj = __shfl(alpha, 4 * quad + j);
