@@ -49,6 +49,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "prefill_args.h"
 
 namespace uaii {
@@ -145,22 +147,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int KSTEPS = D / 32;  // k-steps of the score product
   constexpr int NB = D / 16;      // 16-column blocks of the output
   constexpr int LS = D + 8;       // K and V tiles: LDS row stride in bf16 elements (16-byte pad)
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kKeys * LS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[kKeys * LS];
-  // int8 caches: the tile's per-token key and value scales.
-  __shared__ float ksc[KT == kI8 ? kKeys : 1];
-  __shared__ float vsc[VT == kI8 ? kKeys : 1];
+  // Two-deep rings of K and V tiles (and, for int8 caches, the tiles'
+  // per-token key and value scales).  K runs one tile ahead of V.
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKeys * LS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kKeys * LS];
+  __shared__ float ksc[2][KT == kI8 ? kKeys : 1];
+  __shared__ float vsc[2][VT == kI8 ? kKeys : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int qi = lane & 15;   // query column of this lane (and row of the A operand)
   const int quad = lane >> 4;
-  const int b = blockIdx.z, kvh = blockIdx.y;
+  // Work-group order.  The hardware hands work-group L (x fastest) to XCD
+  // L % 8.  Remapped so that all row groups of one (sequence, kv head), which
+  // read the same K and V prefix, run on one XCD and share its L2, and so
+  // that within it the longest row groups (the last queries of the causal
+  // chunk see the most keys) start first and the short ones fill the tail.
+  const int n_x = gridDim.x, n_sets = gridDim.y * gridDim.z, n_wg = n_x * n_sets;
+  const int wg = blockIdx.x + n_x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int lam = (n_wg % 8 == 0) ? (wg % 8) * (n_wg / 8) + wg / 8 : wg;
+  const int set = lam / n_x;
+  const int b = set / gridDim.y, kvh = set % gridDim.y;
+  const int gx = n_x - 1 - lam % n_x;
   const int T = a.T, L = a.len[b];
   const int P0 = L - T;  // position of the chunk's first token
   const int rows = T * G;
-  const int row0 = blockIdx.x * ROWS;
+  const int row0 = gx * ROWS;
   const int wrow0 = row0 + wave * 16 * QB;  // first row of this wave
 
   // This lane's query in each block q (S^T column qi of block q).
@@ -230,90 +243,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       return (slab + r) * D;
     }
   };
-  // This thread's share of a tile: 16-byte chunks of K and of V (and, for
-  // int8 caches, one scale).  Rows outside [lo_first, k_end) are replaced by
-  // the nearest row inside (every row read holds a visible key of some query
-  // of the work-group); their weights are zero.
-  u32x4 kreg[SK::NL], vreg[SV::NL];
-  float sreg = 0.0f;
+  // This thread's share of a tile: 16-byte chunks of K or of V (and, for
+  // int8 caches, one scale: threads 0..31 a key's, 32..63 a value's).  Rows
+  // outside [lo_first, k_end) are replaced by the nearest row inside (every
+  // row read holds a visible key of some query of the work-group); their
+  // weights are zero.
   auto clamp_row = [&](int r) { return min(max(r, lo_first), k_end - 1); };
-  auto load_tile = [&](int k0) {
+  auto load_k = [&](int k0, u32x4 (&kr)[SK::NL], float& sr) {
 #pragma unroll
     for (int i = 0; i < SK::NL; ++i) {
       const int c = tid + 256 * i;
       if (SK::NL * 256 == SK::TOTAL || c < SK::TOTAL) {
         const int r = c / SK::CPR, cc = c % SK::CPR;
         const int64_t off = row_off(clamp_row(k0 + r)) * KEB + cc * 16;
-        kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k) + off);
+        kr[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k) + off);
       }
     }
+    if constexpr (KT == kI8) {
+      if (tid < kKeys && a.k_scale != nullptr) sr = a.k_scale[row_off(clamp_row(k0 + tid)) / D];
+    }
+  };
+  auto load_v = [&](int k0, u32x4 (&vr)[SV::NL], float& sr) {
 #pragma unroll
     for (int i = 0; i < SV::NL; ++i) {
       const int c = tid + 256 * i;
       if (SV::NL * 256 == SV::TOTAL || c < SV::TOTAL) {
         const int r = c / SV::CPR, cc = c % SV::CPR;
         const int64_t off = row_off(clamp_row(k0 + r)) * VEB + cc * 16;
-        vreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v) + off);
+        vr[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v) + off);
       }
-    }
-    if constexpr (KT == kI8 || VT == kI8) {
-      // threads 0..31: key scales, 32..63: value scales, of rows k0 + (tid % 32)
-      const bool is_k = tid < kKeys;
-      const float* pool = is_k ? a.k_scale : a.v_scale;
-      if (tid < 2 * kKeys && pool != nullptr) sreg = pool[row_off(clamp_row(k0 + (tid & (kKeys - 1)))) / D];
-    }
-  };
-  // Write the staged registers to LDS (int8 codes widened to bf16).
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < SK::NL; ++i) {
-      const int c = tid + 256 * i;
-      if (SK::NL * 256 == SK::TOTAL || c < SK::TOTAL) {
-        const int r = c / SK::CPR, cc = c % SK::CPR;
-        if constexpr (KT == kI8) {
-          u32x4 lo, hi;
-          widen_i8(kreg[i], lo, hi);
-          *reinterpret_cast<u32x4*>(&ks[r * LS + cc * 16]) = lo;
-          *reinterpret_cast<u32x4*>(&ks[r * LS + cc * 16 + 8]) = hi;
-        } else {
-          *reinterpret_cast<u32x4*>(&ks[r * LS + cc * 8]) = kreg[i];
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < SV::NL; ++i) {
-      const int c = tid + 256 * i;
-      if (SV::NL * 256 == SV::TOTAL || c < SV::TOTAL) {
-        const int r = c / SV::CPR, cc = c % SV::CPR;
-        if constexpr (VT == kI8) {
-          u32x4 lo, hi;
-          widen_i8(vreg[i], lo, hi);
-          *reinterpret_cast<u32x4*>(&vs[r * LS + cc * 16]) = lo;
-          *reinterpret_cast<u32x4*>(&vs[r * LS + cc * 16 + 8]) = hi;
-        } else {
-          *reinterpret_cast<u32x4*>(&vs[r * LS + cc * 8]) = vreg[i];
-        }
-      }
-    }
-    if constexpr (KT == kI8) {
-      if (tid < kKeys) ksc[tid] = sreg;
     }
     if constexpr (VT == kI8) {
-      if (tid >= kKeys && tid < 2 * kKeys) vsc[tid - kKeys] = sreg;
+      if (tid >= kKeys && tid < 2 * kKeys && a.v_scale != nullptr)
+        sr = a.v_scale[row_off(clamp_row(k0 + tid - kKeys)) / D];
+    }
+  };
+  // Write staged registers to LDS buffer `buf` (int8 codes widened to bf16).
+  auto store_rows = [&](auto& sh, const u32x4* rg, auto stage, auto eb) {
+    using S = decltype(stage);
+    constexpr bool i8 = decltype(eb)::value == 1;
+#pragma unroll
+    for (int i = 0; i < S::NL; ++i) {
+      const int c = tid + 256 * i;
+      if (S::NL * 256 == S::TOTAL || c < S::TOTAL) {
+        const int r = c / S::CPR, cc = c % S::CPR;
+        if constexpr (i8) {
+          u32x4 lo, hi;
+          widen_i8(rg[i], lo, hi);
+          *reinterpret_cast<u32x4*>(&sh[r * LS + cc * 16]) = lo;
+          *reinterpret_cast<u32x4*>(&sh[r * LS + cc * 16 + 8]) = hi;
+        } else {
+          *reinterpret_cast<u32x4*>(&sh[r * LS + cc * 8]) = rg[i];
+        }
+      }
+    }
+  };
+  auto store_k = [&](const u32x4 (&kr)[SK::NL], float sr, int buf) {
+    store_rows(ks[buf], kr, SK{}, std::integral_constant<int, KEB>{});
+    if constexpr (KT == kI8) {
+      if (tid < kKeys) ksc[buf][tid] = sr;
+    }
+  };
+  auto store_v = [&](const u32x4 (&vr)[SV::NL], float sr, int buf) {
+    store_rows(vs[buf], vr, SV{}, std::integral_constant<int, VEB>{});
+    if constexpr (VT == kI8) {
+      if (tid >= kKeys && tid < 2 * kKeys) vsc[buf][tid - kKeys] = sr;
     }
   };
 
-  load_tile(k_begin);
-  for (int k0 = k_begin; k0 < k_end; k0 += kKeys) {
-    __syncthreads();  // the previous tile's LDS reads are done
-    store_tile();
-    __syncthreads();
-    // The next tile's loads are in flight during this tile's products.
-    if (k0 + kKeys < k_end) load_tile(k0 + kKeys);
-
-    // S^T for keys k0 + mb*16 + (0..15) against the wave's query blocks:
-    // lane holds keys k0 + mb*16 + 4*quad + j of query qi of block q.
-    f32x4 s[QB][2];
+  // S^T for the 32 keys of the K tile in buffer `buf` against the wave's
+  // query blocks: lane holds keys mb*16 + 4*quad + j of query qi of block q.
+  // int8 keys: each raw score is q . code; the key's scale makes it q . k.
+  auto scores = [&](int buf, f32x4 (&s)[QB][2]) {
 #pragma unroll
     for (int q = 0; q < QB; ++q)
 #pragma unroll
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int st = 0; st < KSTEPS; ++st) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&ks[(mb * 16 + qi) * LS + st * 32 + 8 * quad]);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&ks[buf][(mb * 16 + qi) * LS + st * 32 + 8 * quad]);
 #pragma unroll
         for (int q = 0; q < QB; ++q) {
           s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[q][st], s[q][mb], 0, 0, 0);
@@ -330,87 +331,126 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-
-    // int8 keys: each raw score is q . code; the key's scale makes it q . k.
     if constexpr (KT == kI8) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float kscale = ksc[mb * 16 + 4 * quad + j];
+          const float kscale = ksc[buf][mb * 16 + 4 * quad + j];
 #pragma unroll
           for (int q = 0; q < QB; ++q) s[q][mb][j] *= kscale;
         }
     }
+  };
 
-    // Per block: masked, capped scores, online softmax, rescale; the
-    // weights as the PV product's A operand.  A tile inside every row's
-    // visible range (the common case) skips the mask.
+  // Software pipeline over tiles j = 0 .. n_tiles - 1 (keys k_begin + 32 j):
+  // iteration j computes the softmax and PV product of tile j and, from the
+  // other K buffer, the scores of tile j + 1, which are independent of the
+  // softmax, so the matrix products overlap its vector work.  LDS holds K(j),
+  // V(j) in buffer j % 2 and K(j + 1), V(j + 1) in the other one; iteration j
+  // stages K(j + 2) into buffer j % 2 (K(j) was read in iteration j - 1) and
+  // V(j + 1) into buffer (j + 1) % 2 (V(j - 1)'s), so one barrier per tile
+  // suffices.  Past the last tile the clamped rows are loaded and their
+  // scores computed but never used.
+  const int n_tiles = (k_end - k_begin + kKeys - 1) / kKeys;
+  u32x4 kreg[SK::NL], vreg[SV::NL];
+  float sreg = 0.0f;
+  {
+    u32x4 k0r[SK::NL], v0r[SV::NL], k1r[SK::NL];
+    float s0 = 0.0f, s1 = 0.0f;
+    load_k(k_begin, k0r, s0);
+    load_v(k_begin, v0r, s0);
+    load_k(k_begin + kKeys, k1r, s1);
+    load_k(k_begin + 2 * kKeys, kreg, sreg);
+    load_v(k_begin + kKeys, vreg, sreg);
+    store_k(k0r, s0, 0);
+    store_v(v0r, s0, 0);
+    store_k(k1r, s1, 1);
+  }
+  __syncthreads();
+  f32x4 s[QB][2];
+  scores(0, s);
+  __syncthreads();  // every wave has read K(0) before iteration 0 replaces it
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int k0 = k_begin + j * kKeys;
+    store_k(kreg, sreg, j & 1);
+    store_v(vreg, sreg, (j + 1) & 1);
+    load_k(k0 + 3 * kKeys, kreg, sreg);
+    load_v(k0 + 2 * kKeys, vreg, sreg);
+
+    // Tile j: capped scores, and the mask unless every row of the
+    // work-group sees the whole tile (the common case).
+    float sv[QB][8];
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[q][e] = capped(s[q][e >> 2][e & 3], cap, cap_c, cap_inv);
     const bool full = rows_full && k0 >= lo_last && k0 + kKeys - 1 <= p_first;
+    if (!full) {
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = k0 + (e >> 2) * 16 + 4 * quad + (e & 3);
+          const bool vis = row_ok[q] && key >= my_lo[q] && key <= my_p[q];
+          sv[q][e] = vis ? sv[q][e] : -INFINITY;
+        }
+    }
+
+    f32x4 sn[QB][2];
+    scores((j + 1) & 1, sn);
+
+    // Online softmax of tile j; the weights as the PV product's A operand.
     bf16x8 ph[QB], pl[QB];
+    float alpha[QB];
+    bool bump[QB];
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      float sv[8];
-      float mt = -INFINITY;
-      if (full) {
+      float mt = sv[q][0];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = capped(s[q][mb][j], cap, cap_c, cap_inv);
-            sv[mb * 4 + j] = x;
-            mt = fmaxf(mt, x);
-          }
-      } else {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = k0 + mb * 16 + 4 * quad + j;
-            const bool vis = row_ok[q] && key >= my_lo[q] && key <= my_p[q];
-            const float x = vis ? capped(s[q][mb][j], cap, cap_c, cap_inv) : -INFINITY;
-            sv[mb * 4 + j] = x;
-            mt = fmaxf(mt, x);
-          }
-      }
+      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[q][e]);
       mt = pair_max_16_32(mt);
       // m is a reference, not always the running max: it moves only when a
       // tile's max exceeds it by more than kSlack (log2 units), so the
       // weights stay below 2^kSlack and most tiles need no rescale.  The
       // final normalisation divides by l, which carries the same reference.
-      const bool bump = mt > m[q] + kSlack;  // m = -inf: any visible key bumps
-      const float m_new = bump ? mt : m[q];
+      bump[q] = mt > m[q] + kSlack;  // m = -inf: any visible key bumps
+      const float m_new = bump[q] ? mt : m[q];
       const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // no key yet: keep weights 0
-      const float alpha = __builtin_amdgcn_exp2f(m[q] - m_use);  // m = -inf gives 0
+      alpha[q] = __builtin_amdgcn_exp2f(m[q] - m_use);           // m = -inf gives 0
       float p[8];
       float ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
+        p[e] = __builtin_amdgcn_exp2f(sv[q][e] - m_use);
         ps += p[e];
       }
       ps = pair_sum_16_32(ps);
-      l[q] = l[q] * alpha + ps;
+      l[q] = l[q] * alpha[q] + ps;
       m[q] = m_new;
-      // Rescale the accumulator: its rows are queries 4*quad + j, whose
-      // alpha lives in lane 4*quad + j.  Skipped when no query's reference
-      // moved (every alpha is 1, or 0 for a query with no key yet, whose row
-      // is still 0).
-      if (__builtin_amdgcn_ballot_w64(bump) != 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float aj = __shfl(alpha, 4 * quad + j);
-#pragma unroll
-          for (int n = 0; n < NB; ++n) o[q][n][j] *= aj;
-        }
-      }
       // int8 values: the weight of key j carries its value scale (the
       // codes are the V operand), the sum l does not.
       if constexpr (VT == kI8) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] *= vsc[(e < 4) ? 4 * quad + e : 16 + 4 * quad + (e - 4)];
+        for (int e = 0; e < 8; ++e) p[e] *= vsc[j & 1][(e < 4) ? 4 * quad + e : 16 + 4 * quad + (e - 4)];
       }
       split8(p, ph[q], pl[q]);
+    }
+    // Rescale the accumulator: its rows are queries 4*quad + j, whose alpha
+    // lives in lane 4*quad + j.  Skipped when no query's reference moved
+    // (every alpha is 1, or 0 for a query with no key yet, whose row is
+    // still 0).
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      if (__builtin_amdgcn_ballot_w64(bump[q]) != 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float aj = __shfl(alpha[q], 4 * quad + jj);
+#pragma unroll
+          for (int n = 0; n < NB; ++n) o[q][n][jj] *= aj;
+        }
+      }
     }
 
     // O += P V.  A operand: lane holds P[qi][k = 8*quad + e], where k < 4 of
@@ -420,12 +460,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // (ds_read_b64_tr_b16).  Within each 16-lane group, the reading lane s
     // points at 4 dims (n*16 + 4*(s%4) ..) of key base + s/4, and lane i
     // receives dim n*16 + i of keys base .. base + 3.
+    const uint16_t* vb_ = vs[j & 1];
     const int tr_row = 4 * quad + (qi >> 2), tr_col = 4 * (qi & 3);
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vs[tr_row * LS + n * 16 + tr_col]));
+      const s16x4 v0 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[tr_row * LS + n * 16 + tr_col]));
       const s16x4 v1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vs[(16 + tr_row) * LS + n * 16 + tr_col]));
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[(16 + tr_row) * LS + n * 16 + tr_col]));
       const s16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       const bf16x8 vb = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
@@ -434,6 +476,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         o[q][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[q], vb, o[q][n], 0, 0, 0);
       }
     }
+    __syncthreads();  // tile j's buffers are read; the stores above are visible
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) s[q][mb] = sn[q][mb];
   }
 
   // Normalise (with the sink, if any) and write.  Accumulator rows are
