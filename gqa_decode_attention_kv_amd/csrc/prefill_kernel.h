@@ -49,8 +49,6 @@
 
 #include <math.h>
 
-#include <type_traits>
-
 #include "prefill_args.h"
 
 namespace uaii {
@@ -58,6 +56,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -67,6 +67,7 @@ constexpr int kKeys = 32;    // keys per tile
 // The softmax reference of a query moves only when a tile's max exceeds it
 // by more than this many powers of two (weights stay below 2^kSlack).
 constexpr float kSlack = 8.0f;
+constexpr float kSlackW = 256.0f;  // 2^kSlack
 constexpr float kLog2eP = 1.4426950408889634f;
 
 // max / sum of x over lanes l and l ^ 16, then over l and l ^ 32, with
@@ -74,11 +75,16 @@ constexpr float kLog2eP = 1.4426950408889634f;
 // register with itself leaves {x[l], x[l ^ 16]} (resp. l ^ 32) in the two
 // results, in the same order in both lanes of a pair, so both get the same
 // value.  Plain VALU instead of an LDS permute.
+// The max of two scores is med3(a, b, +inf): one instruction, where fmaxf
+// on the swapped registers would first quiet possible signalling NaNs (the
+// scores are never NaN for finite inputs).
+__device__ inline float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
 __device__ inline float pair_max_16_32(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ inline float pair_sum_16_32(float x) {
@@ -92,14 +98,22 @@ __device__ inline float capped(float s, bool cap, float c, float c_inv) {
   return cap ? c * tanhf(s * c_inv) * kLog2eP : s;
 }
 
-// Split 8 floats into bf16 high parts and bf16 remainders (x ~ hi + lo).
+// Split 8 floats into bf16 high parts (round to nearest even) and bf16
+// remainders (x ~ hi + lo).  Pairs are converted with one packed convert;
+// the high parts come back to f32 from the packed word by a shift and a
+// mask.
 __device__ inline void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = static_cast<__bf16>(x[j]);
-    hi[j] = h;
-    lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2 hp = __builtin_convertvector(f32x2{x[2 * k], x[2 * k + 1]}, bf16x2);
+    h[k] = __builtin_bit_cast(uint32_t, hp);
+    const float r0 = x[2 * k] - __uint_as_float(h[k] << 16);
+    const float r1 = x[2 * k + 1] - __uint_as_float(h[k] & 0xFFFF0000u);
+    l[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
   }
+  hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
 // QB blocks of 16 query rows per wave.  With QB = 2 each K and V operand
@@ -146,11 +160,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   using SV = Stage<D, VEB>;
   constexpr int KSTEPS = D / 32;  // k-steps of the score product
   constexpr int NB = D / 16;      // 16-column blocks of the output
-  constexpr int LS = D + 8;       // K and V tiles: LDS row stride in bf16 elements (16-byte pad)
-  // Two-deep rings of K and V tiles (and, for int8 caches, the tiles'
-  // per-token key and value scales).  K runs one tile ahead of V.
+  // LDS row strides in bf16 elements.  K (16-byte pad): a 16-lane group of
+  // 16-byte reads, one per row, covers the banks once.  V (32-byte pad):
+  // the transposing reads take 8 bytes from each of 8 rows per 32 lanes,
+  // and rows 8 banks apart cover the banks once.
+  constexpr int LS = D + 8;
+  constexpr int LSV = D + 16;
+  // Two buffers of K and V tiles (and, for int8 caches, the tiles' per-token
+  // key and value scales): one is read while the next tile is staged.
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKeys * LS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kKeys * LS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kKeys * LSV];
   __shared__ float ksc[2][KT == kI8 ? kKeys : 1];
   __shared__ float vsc[2][VT == kI8 ? kKeys : 1];
 
@@ -225,11 +244,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int q = 0; q < QB; ++q)
 #pragma unroll
     for (int n = 0; n < NB; ++n) o[q][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m[QB], l[QB];  // running max and sum of this lane's queries
+  // Softmax state of this lane's query in each block: the reference m (-inf
+  // until the query's first visible key; rows past the end, which see no
+  // key, start at 0 so that they never hold the wave on the exact path), and
+  // this lane's share of the weight sum relative to m (the lanes of a query
+  // hold different keys; their shares are added at the end).
+  float m[QB], l[QB];
+  uint64_t unref[QB];  // lanes whose query has no reference yet (wave-uniform)
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
-    m[q] = -INFINITY;
+    m[q] = row_ok[q] ? -INFINITY : 0.0f;
     l[q] = 0.0f;
+    unref[q] = __builtin_amdgcn_ballot_w64(row_ok[q]);
   }
 
   const int64_t slab = PAGED ? 0 : (static_cast<int64_t>(b) * a.Hkv + kvh) * a.cap;
@@ -243,87 +269,144 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       return (slab + r) * D;
     }
   };
-  // This thread's share of a tile: 16-byte chunks of K or of V (and, for
+  // This thread's share of a tile: 16-byte chunks of K and of V (and, for
   // int8 caches, one scale: threads 0..31 a key's, 32..63 a value's).  Rows
   // outside [lo_first, k_end) are replaced by the nearest row inside (every
   // row read holds a visible key of some query of the work-group); their
-  // weights are zero.
+  // weights are zero.  A tile of a contiguous cache that lies inside that
+  // range (all but the first and last) is addressed as one uniform base plus
+  // a fixed per-thread offset.
+  u32x4 kreg[SK::NL], vreg[SV::NL];
+  float sreg = 0.0f;
+  const char* kslab = static_cast<const char*>(a.k) + slab * D * KEB;
+  const char* vslab = static_cast<const char*>(a.v) + slab * D * VEB;
   auto clamp_row = [&](int r) { return min(max(r, lo_first), k_end - 1); };
-  auto load_k = [&](int k0, u32x4 (&kr)[SK::NL], float& sr) {
+  auto load_tile = [&](int k0) {
+    if (!PAGED && k0 >= lo_first && k0 + kKeys <= k_end) {
+      const char* kt = kslab + static_cast<int64_t>(k0) * (D * KEB);
+      const char* vt = vslab + static_cast<int64_t>(k0) * (D * VEB);
+#pragma unroll
+      for (int i = 0; i < SK::NL; ++i) {
+        const int c = tid + 256 * i;
+        if (SK::NL * 256 == SK::TOTAL || c < SK::TOTAL)
+          kreg[i] = *reinterpret_cast<const u32x4*>(kt + static_cast<uint32_t>(c / SK::CPR * (D * KEB) + c % SK::CPR * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < SV::NL; ++i) {
+        const int c = tid + 256 * i;
+        if (SV::NL * 256 == SV::TOTAL || c < SV::TOTAL)
+          vreg[i] = *reinterpret_cast<const u32x4*>(vt + static_cast<uint32_t>(c / SV::CPR * (D * VEB) + c % SV::CPR * 16));
+      }
+      if constexpr (KT == kI8 || VT == kI8) {
+        const bool is_k = tid < kKeys;
+        const float* pool = is_k ? a.k_scale : a.v_scale;
+        if (tid < 2 * kKeys && pool != nullptr) sreg = pool[slab + k0 + (tid & (kKeys - 1))];
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < SK::NL; ++i) {
       const int c = tid + 256 * i;
       if (SK::NL * 256 == SK::TOTAL || c < SK::TOTAL) {
         const int r = c / SK::CPR, cc = c % SK::CPR;
         const int64_t off = row_off(clamp_row(k0 + r)) * KEB + cc * 16;
-        kr[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k) + off);
+        kreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k) + off);
       }
     }
-    if constexpr (KT == kI8) {
-      if (tid < kKeys && a.k_scale != nullptr) sr = a.k_scale[row_off(clamp_row(k0 + tid)) / D];
-    }
-  };
-  auto load_v = [&](int k0, u32x4 (&vr)[SV::NL], float& sr) {
 #pragma unroll
     for (int i = 0; i < SV::NL; ++i) {
       const int c = tid + 256 * i;
       if (SV::NL * 256 == SV::TOTAL || c < SV::TOTAL) {
         const int r = c / SV::CPR, cc = c % SV::CPR;
         const int64_t off = row_off(clamp_row(k0 + r)) * VEB + cc * 16;
-        vr[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v) + off);
+        vreg[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v) + off);
       }
     }
-    if constexpr (VT == kI8) {
-      if (tid >= kKeys && tid < 2 * kKeys && a.v_scale != nullptr)
-        sr = a.v_scale[row_off(clamp_row(k0 + tid - kKeys)) / D];
+    if constexpr (KT == kI8 || VT == kI8) {
+      const bool is_k = tid < kKeys;
+      const float* pool = is_k ? a.k_scale : a.v_scale;
+      if (tid < 2 * kKeys && pool != nullptr) sreg = pool[row_off(clamp_row(k0 + (tid & (kKeys - 1)))) / D];
     }
   };
-  // Write staged registers to LDS buffer `buf` (int8 codes widened to bf16).
-  auto store_rows = [&](auto& sh, const u32x4* rg, auto stage, auto eb) {
-    using S = decltype(stage);
-    constexpr bool i8 = decltype(eb)::value == 1;
+  // Write the staged registers to LDS buffer `buf` (int8 codes widened to
+  // bf16).
+  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < S::NL; ++i) {
+    for (int i = 0; i < SK::NL; ++i) {
       const int c = tid + 256 * i;
-      if (S::NL * 256 == S::TOTAL || c < S::TOTAL) {
-        const int r = c / S::CPR, cc = c % S::CPR;
-        if constexpr (i8) {
+      if (SK::NL * 256 == SK::TOTAL || c < SK::TOTAL) {
+        const int r = c / SK::CPR, cc = c % SK::CPR;
+        if constexpr (KT == kI8) {
           u32x4 lo, hi;
-          widen_i8(rg[i], lo, hi);
-          *reinterpret_cast<u32x4*>(&sh[r * LS + cc * 16]) = lo;
-          *reinterpret_cast<u32x4*>(&sh[r * LS + cc * 16 + 8]) = hi;
+          widen_i8(kreg[i], lo, hi);
+          *reinterpret_cast<u32x4*>(&ks[buf][r * LS + cc * 16]) = lo;
+          *reinterpret_cast<u32x4*>(&ks[buf][r * LS + cc * 16 + 8]) = hi;
         } else {
-          *reinterpret_cast<u32x4*>(&sh[r * LS + cc * 8]) = rg[i];
+          *reinterpret_cast<u32x4*>(&ks[buf][r * LS + cc * 8]) = kreg[i];
         }
       }
     }
-  };
-  auto store_k = [&](const u32x4 (&kr)[SK::NL], float sr, int buf) {
-    store_rows(ks[buf], kr, SK{}, std::integral_constant<int, KEB>{});
-    if constexpr (KT == kI8) {
-      if (tid < kKeys) ksc[buf][tid] = sr;
+#pragma unroll
+    for (int i = 0; i < SV::NL; ++i) {
+      const int c = tid + 256 * i;
+      if (SV::NL * 256 == SV::TOTAL || c < SV::TOTAL) {
+        const int r = c / SV::CPR, cc = c % SV::CPR;
+        if constexpr (VT == kI8) {
+          u32x4 lo, hi;
+          widen_i8(vreg[i], lo, hi);
+          *reinterpret_cast<u32x4*>(&vs[buf][r * LSV + cc * 16]) = lo;
+          *reinterpret_cast<u32x4*>(&vs[buf][r * LSV + cc * 16 + 8]) = hi;
+        } else {
+          *reinterpret_cast<u32x4*>(&vs[buf][r * LSV + cc * 8]) = vreg[i];
+        }
+      }
     }
-  };
-  auto store_v = [&](const u32x4 (&vr)[SV::NL], float sr, int buf) {
-    store_rows(vs[buf], vr, SV{}, std::integral_constant<int, VEB>{});
+    if constexpr (KT == kI8) {
+      if (tid < kKeys) ksc[buf][tid] = sreg;
+    }
     if constexpr (VT == kI8) {
-      if (tid >= kKeys && tid < 2 * kKeys) vsc[buf][tid - kKeys] = sr;
+      if (tid >= kKeys && tid < 2 * kKeys) vsc[buf][tid - kKeys] = sreg;
     }
   };
 
-  // S^T for the 32 keys of the K tile in buffer `buf` against the wave's
-  // query blocks: lane holds keys mb*16 + 4*quad + j of query qi of block q.
-  // int8 keys: each raw score is q . code; the key's scale makes it q . k.
-  auto scores = [&](int buf, f32x4 (&s)[QB][2]) {
+  // Tiles j = 0 .. n_tiles - 1 (keys k_begin + 32 j) alternate between the
+  // two LDS buffers.  Iteration j computes tile j from buffer j % 2, then
+  // stages tile j + 1 (loaded during iteration j - 1) into the other buffer,
+  // whose previous tile every wave finished reading before the last
+  // barrier, and starts the loads of tile j + 2: one barrier per tile.
+  const int n_tiles = (k_end - k_begin + kKeys - 1) / kKeys;
+  load_tile(k_begin);
+  store_tile(0);
+  if (n_tiles > 1) load_tile(k_begin + kKeys);
+  __syncthreads();
+  for (int j = 0; j < n_tiles; ++j) {
+    const int k0 = k_begin + j * kKeys;
+    const int buf = j & 1;
+    const uint16_t* kb = ks[buf];
+    const uint16_t* vb_ = vs[buf];
+
+    // S^T for keys k0 + mb*16 + (0..15) against the wave's query blocks:
+    // lane holds keys k0 + mb*16 + 4*quad + j of query qi of block q.  The
+    // scores come out relative to the query's reference r = m (0 while m is
+    // -inf): where nothing is applied to the raw product, the accumulator
+    // starts at -r.
+    constexpr bool fold = !cap && KT != kI8;
+    float r[QB];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) r[q] = (m[q] == -INFINITY) ? 0.0f : m[q];
+    f32x4 s[QB][2];
 #pragma unroll
     for (int q = 0; q < QB; ++q)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) s[q][mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int mb = 0; mb < 2; ++mb) {
+        const float c0 = fold ? -r[q] : 0.0f;
+        s[q][mb] = f32x4{c0, c0, c0, c0};
+      }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int st = 0; st < KSTEPS; ++st) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&ks[buf][(mb * 16 + qi) * LS + st * 32 + 8 * quad]);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kb[(mb * 16 + qi) * LS + st * 32 + 8 * quad]);
 #pragma unroll
         for (int q = 0; q < QB; ++q) {
           s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[q][st], s[q][mb], 0, 0, 0);
@@ -331,62 +414,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-    if constexpr (KT == kI8) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float kscale = ksc[buf][mb * 16 + 4 * quad + j];
-#pragma unroll
-          for (int q = 0; q < QB; ++q) s[q][mb][j] *= kscale;
-        }
-    }
-  };
 
-  // Software pipeline over tiles j = 0 .. n_tiles - 1 (keys k_begin + 32 j):
-  // iteration j computes the softmax and PV product of tile j and, from the
-  // other K buffer, the scores of tile j + 1, which are independent of the
-  // softmax, so the matrix products overlap its vector work.  LDS holds K(j),
-  // V(j) in buffer j % 2 and K(j + 1), V(j + 1) in the other one; iteration j
-  // stages K(j + 2) into buffer j % 2 (K(j) was read in iteration j - 1) and
-  // V(j + 1) into buffer (j + 1) % 2 (V(j - 1)'s), so one barrier per tile
-  // suffices.  Past the last tile the clamped rows are loaded and their
-  // scores computed but never used.
-  const int n_tiles = (k_end - k_begin + kKeys - 1) / kKeys;
-  u32x4 kreg[SK::NL], vreg[SV::NL];
-  float sreg = 0.0f;
-  {
-    u32x4 k0r[SK::NL], v0r[SV::NL], k1r[SK::NL];
-    float s0 = 0.0f, s1 = 0.0f;
-    load_k(k_begin, k0r, s0);
-    load_v(k_begin, v0r, s0);
-    load_k(k_begin + kKeys, k1r, s1);
-    load_k(k_begin + 2 * kKeys, kreg, sreg);
-    load_v(k_begin + kKeys, vreg, sreg);
-    store_k(k0r, s0, 0);
-    store_v(v0r, s0, 0);
-    store_k(k1r, s1, 1);
-  }
-  __syncthreads();
-  f32x4 s[QB][2];
-  scores(0, s);
-  __syncthreads();  // every wave has read K(0) before iteration 0 replaces it
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int k0 = k_begin + j * kKeys;
-    store_k(kreg, sreg, j & 1);
-    store_v(vreg, sreg, (j + 1) & 1);
-    load_k(k0 + 3 * kKeys, kreg, sreg);
-    load_v(k0 + 2 * kKeys, vreg, sreg);
-
-    // Tile j: capped scores, and the mask unless every row of the
-    // work-group sees the whole tile (the common case).
-    float sv[QB][8];
+    // t = score - r: int8 keys scale the raw product (q . code) by the key's
+    // scale; the softcap clips the score.  Masked keys (outside a row's
+    // causal window) get -inf unless every row of the work-group sees the
+    // whole tile (the common case).
+    const bool full = rows_full && k0 >= lo_last && k0 + kKeys - 1 <= p_first;
+    float t[QB][8];
 #pragma unroll
     for (int q = 0; q < QB; ++q)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sv[q][e] = capped(s[q][e >> 2][e & 3], cap, cap_c, cap_inv);
-    const bool full = rows_full && k0 >= lo_last && k0 + kKeys - 1 <= p_first;
+      for (int e = 0; e < 8; ++e) {
+        float x = s[q][e >> 2][e & 3];
+        if constexpr (KT == kI8) {
+          const float kscale = ksc[buf][(e >> 2) * 16 + 4 * quad + (e & 3)];
+          x = cap ? capped(x * kscale, cap, cap_c, cap_inv) - r[q] : fmaf(x, kscale, -r[q]);
+        } else if constexpr (cap) {
+          x = capped(x, cap, cap_c, cap_inv) - r[q];
+        }
+        t[q][e] = x;
+      }
     if (!full) {
 #pragma unroll
       for (int q = 0; q < QB; ++q)
@@ -394,63 +441,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int e = 0; e < 8; ++e) {
           const int key = k0 + (e >> 2) * 16 + 4 * quad + (e & 3);
           const bool vis = row_ok[q] && key >= my_lo[q] && key <= my_p[q];
-          sv[q][e] = vis ? sv[q][e] : -INFINITY;
+          t[q][e] = vis ? t[q][e] : -INFINITY;
         }
     }
 
-    f32x4 sn[QB][2];
-    scores((j + 1) & 1, sn);
-
-    // Online softmax of tile j; the weights as the PV product's A operand.
+    // Online softmax with a lazy reference.  Fast path: the weights are
+    // 2^t, each lane adds its own; valid while every weight stays at most
+    // 2^kSlack, which the lane's sum bounds.  When some lane's sum exceeds
+    // it, or a query of the wave has no reference yet, the wave takes the
+    // exact path: the tile max over the query's lanes, and a new reference
+    // when it exceeds the old one by more than kSlack, with the rescale of
+    // the accumulator and the sums; the weights are recomputed in place.
     bf16x8 ph[QB], pl[QB];
-    float alpha[QB];
-    bool bump[QB];
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      float mt = sv[q][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[q][e]);
-      mt = pair_max_16_32(mt);
-      // m is a reference, not always the running max: it moves only when a
-      // tile's max exceeds it by more than kSlack (log2 units), so the
-      // weights stay below 2^kSlack and most tiles need no rescale.  The
-      // final normalisation divides by l, which carries the same reference.
-      bump[q] = mt > m[q] + kSlack;  // m = -inf: any visible key bumps
-      const float m_new = bump[q] ? mt : m[q];
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // no key yet: keep weights 0
-      alpha[q] = __builtin_amdgcn_exp2f(m[q] - m_use);           // m = -inf gives 0
       float p[8];
       float ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(sv[q][e] - m_use);
+        p[e] = __builtin_amdgcn_exp2f(t[q][e]);
         ps += p[e];
       }
-      ps = pair_sum_16_32(ps);
-      l[q] = l[q] * alpha[q] + ps;
-      m[q] = m_new;
+      if ((unref[q] | __builtin_amdgcn_ballot_w64(ps > kSlackW)) != 0) {
+        float lm = t[q][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) lm = max2(lm, t[q][e]);
+        const float ms = r[q] + pair_max_16_32(lm);  // tile max (-inf: no visible key)
+        const bool bump = ms > m[q] + kSlack;        // m = -inf: any visible key bumps
+        const float m_new = bump ? ms : m[q];
+        const float r_new = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float d = r_new - r[q];
+        const float alpha = __builtin_amdgcn_exp2f(m[q] - r_new);  // m = -inf gives 0
+        ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(t[q][e] - d);
+          ps += p[e];
+        }
+        l[q] *= alpha;
+        m[q] = m_new;
+        unref[q] = __builtin_amdgcn_ballot_w64(m_new == -INFINITY);
+        // Rescale the accumulator: its rows are queries 4*quad + jj, whose
+        // alpha lives in lane 4*quad + jj.  Skipped when no query's
+        // reference moved (every alpha is 1, or 0 for a query with no key
+        // yet, whose row is still 0).
+        if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float aj = __shfl(alpha, 4 * quad + jj);
+#pragma unroll
+            for (int n = 0; n < NB; ++n) o[q][n][jj] *= aj;
+          }
+        }
+      }
+      l[q] += ps;
       // int8 values: the weight of key j carries its value scale (the
       // codes are the V operand), the sum l does not.
       if constexpr (VT == kI8) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] *= vsc[j & 1][(e < 4) ? 4 * quad + e : 16 + 4 * quad + (e - 4)];
+        for (int e = 0; e < 8; ++e) p[e] *= vsc[buf][(e < 4) ? 4 * quad + e : 16 + 4 * quad + (e - 4)];
       }
       split8(p, ph[q], pl[q]);
-    }
-    // Rescale the accumulator: its rows are queries 4*quad + j, whose alpha
-    // lives in lane 4*quad + j.  Skipped when no query's reference moved
-    // (every alpha is 1, or 0 for a query with no key yet, whose row is
-    // still 0).
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      if (__builtin_amdgcn_ballot_w64(bump[q]) != 0) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float aj = __shfl(alpha[q], 4 * quad + jj);
-#pragma unroll
-          for (int n = 0; n < NB; ++n) o[q][n][jj] *= aj;
-        }
-      }
     }
 
     // O += P V.  A operand: lane holds P[qi][k = 8*quad + e], where k < 4 of
@@ -460,14 +511,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // (ds_read_b64_tr_b16).  Within each 16-lane group, the reading lane s
     // points at 4 dims (n*16 + 4*(s%4) ..) of key base + s/4, and lane i
     // receives dim n*16 + i of keys base .. base + 3.
-    const uint16_t* vb_ = vs[j & 1];
     const int tr_row = 4 * quad + (qi >> 2), tr_col = 4 * (qi & 3);
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const s16x4 v0 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[tr_row * LS + n * 16 + tr_col]));
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[tr_row * LSV + n * 16 + tr_col]));
       const s16x4 v1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[(16 + tr_row) * LS + n * 16 + tr_col]));
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[(16 + tr_row) * LSV + n * 16 + tr_col]));
       const s16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       const bf16x8 vb = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
@@ -476,22 +526,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         o[q][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[q], vb, o[q][n], 0, 0, 0);
       }
     }
-    __syncthreads();  // tile j's buffers are read; the stores above are visible
-#pragma unroll
-    for (int q = 0; q < QB; ++q)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) s[q][mb] = sn[q][mb];
+
+    if (j + 1 < n_tiles) {
+      store_tile(buf ^ 1);
+      if (j + 2 < n_tiles) load_tile(k0 + 2 * kKeys);
+    }
+    __syncthreads();  // tile j + 1 is staged; every wave is done with tile j
   }
 
   // Normalise (with the sink, if any) and write.  Accumulator rows are
   // queries 4*quad + j of each block; their m and l live in lane 4*quad + j.
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
+    const float lq = pair_sum_16_32(l[q]);  // the query's four lanes
     float sink2 = -INFINITY;
     if (a.sinks != nullptr && row_ok[q]) sink2 = a.sinks[kvh * G + my_g[q]] * kLog2eP;
     const float m_fin = fmaxf(m[q], sink2);
     const float keep = __builtin_amdgcn_exp2f(m[q] - m_fin);
-    const float den = l[q] * keep + __builtin_amdgcn_exp2f(sink2 - m_fin);
+    const float den = lq * keep + __builtin_amdgcn_exp2f(sink2 - m_fin);
     const float f = keep / den;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
