@@ -22,11 +22,14 @@
 //     The rows are (token, head) pairs t * G + g of one kv head's group, so
 //     the G heads that share a kv head share every K and V tile (grouped
 //     flash attention): each tile is read from HBM once per work-group.
+//   * Work-group order: all row groups of one (sequence, kv head) run on
+//     one XCD (they read the same K and V prefix through its L2), longest
+//     first within it (the causal tail is short).
 //   * Key tiles of 32 rows of K and V are staged in LDS by the whole
-//     work-group with 16-byte loads (padded rows, so the matrix reads below
-//     do not collide on banks).  The next tile's loads go to registers while
-//     the current tile's products run (16 registers at d128; with two query
-//     blocks per wave the kernel runs two waves per SIMD either way).
+//     work-group with 16-byte loads, double-buffered: one barrier per tile.
+//     Padded rows, so the matrix and transposing reads below do not collide
+//     on banks.  The next tile's loads go to registers while the current
+//     tile's products run.
 //   * Each wave owns 32 query rows (16 at d256 or in small grids) and
 //     computes the transposed
 //     scores S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (two 16-key blocks);
@@ -38,6 +41,11 @@
 //     load.
 //   * Online softmax per query in f32, in the log2 domain (q pre-multiplied
 //     by scale * log2 e); keys outside a query's causal window get weight 0.
+//     The reference a query's weights are taken against moves only when a
+//     tile exceeds it by more than 2^8, and the scores come out of the
+//     matrix product already relative to it, so the common tile costs an
+//     exp2 and an add per weight; the tile max, the rescale and the
+//     reduction across lanes run on a rare wave-uniform path.
 //   * Precision: q (f32) and the probabilities (f32) are each split into a
 //     bf16 high part and a bf16 remainder, and both parts are multiplied by
 //     the exact bf16 K or V: two MFMAs per product, about 16 significant bits
