@@ -148,13 +148,16 @@ def check_rows(st, ref_q, ck, cv, vs, ks):
     P.check_slot(w, gpu, ref, st.q_out.cpu().numpy(), ref_q)
 
 
-@pytest.mark.parametrize("spec", SMALL, ids=[c[0].name for c in SMALL])
-def test_prefill_small(spec):
-    w, lens, bs = spec
+def run_small(w, lens, bs, prep=None):
+    """One small chunk step on the GPU against the oracle: produced rows and
+    queries, untouched rows elsewhere, and every output.  prep, if given,
+    rewrites the seeded inputs first."""
     P.say(f"prefill case {w.name}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
           f"T={w.chunk} lens={lens.tolist()[:8]} W={w.window} cap={w.softcap} sink={w.sink} "
           f"paged={bs}")
     inputs = W.make_prefill_inputs(w, seq_lens=lens)
+    if prep is not None:
+        prep(inputs)
     paged = W.make_paged(inputs, bs) if bs else None
     if paged:
         before = [paged.pool_k, paged.pool_v, paged.pool_scale, paged.pool_k_scale]
@@ -187,6 +190,60 @@ def test_prefill_small(spec):
     err = float(np.max(np.abs(out - want)))
     P.say(f"  max abs err {err:.3g} (tol {tol:.3g}, {cls})")
     assert np.all(np.isfinite(out)) and err <= tol, err
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[c[0].name for c in SMALL])
+def test_prefill_small(spec):
+    run_small(*spec)
+
+
+def scale_cached_keys(factor):
+    """prep: multiply each cached bf16 key row [lo, L - T) by factor(j, n)
+    (j = 0 .. n - 1 from the oldest row), re-stored by truncation like the
+    generator's rows."""
+    def prep(inputs):
+        w = inputs.workload
+        assert w.k_dtype == W.BF16
+        for b in range(w.batch):
+            first = int(inputs.start[b])
+            lo, _ = w.visible(first + 1)
+            n = first - lo
+            if n <= 0:
+                continue
+            rows = inputs.cache_k[b, :, lo:first]
+            f = (rows.astype(np.uint32) << 16).view(np.float32)
+            f = f * factor(np.arange(n, dtype=np.float32), n)[None, :, None]
+            inputs.cache_k[b, :, lo:first] = (f.view(np.uint32) >> 16).astype(np.uint16)
+    return prep
+
+
+def spike(j, n):
+    out = np.ones(n, np.float32)
+    out[n // 2] = 25.0
+    return out
+
+
+# Scores whose running max keeps growing (keys scaled up along the cache:
+# about 11 log2 units more per 32-key tile), falling, or jumping once: the
+# chunk kernel's softmax reference then moves mid-sequence, and the
+# accumulator and sums are rescaled, on many tiles rather than only the
+# first.
+MOVING = [
+    (case("ramp-up-d128-g4", 128, 4, 2, 64, [700, 400], seed=31), lambda j, n: 1.0 + 0.1 * j),
+    (case("ramp-up-d128-g4-b32-two-blocks", 128, 4, 8, 72,
+          np.random.default_rng(32).integers(300, 601, 32), seed=32), lambda j, n: 1.0 + 0.1 * j),
+    (case("ramp-down-d64-g8", 64, 8, 1, 40, [500], seed=33), lambda j, n: 1.0 + 0.1 * (n - 1 - j)),
+    (case("spike-d128-g2-window-sink", 128, 2, 2, 50, [400, 300], window=200, sink=True, seed=34),
+     spike),
+    (case("ramp-up-vq8-d128-g4-softcap", 128, 4, 2, 48, [600], softcap=50.0, seed=35, kv=VQ8),
+     lambda j, n: 1.0 + 0.1 * j),
+]
+
+
+@pytest.mark.parametrize("spec", MOVING, ids=[c[0][0].name for c in MOVING])
+def test_prefill_moving_reference(spec):
+    (w, lens, bs), factor = spec
+    run_small(w, lens, bs, prep=scale_cached_keys(factor))
 
 
 @pytest.mark.parametrize("name", list(W.PREFILL))
