@@ -187,7 +187,8 @@ def prefill_main(args) -> int:
     name = args.prefill
     w = W.PREFILL[name]
     inputs = W.make_prefill_inputs(w)
-    st = DevicePrefill(inputs)
+    paged = W.make_paged(inputs, args.paged) if args.paged else None
+    st = DevicePrefill(inputs, paged=paged)
     flops = W.prefill_flops(w, inputs.seq_lens)
     t_w, n_w = time.perf_counter(), 0
     while n_w < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
@@ -229,14 +230,16 @@ def prefill_main(args) -> int:
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "kv_cache": {(1, 1): "bf16/bf16", (1, 2): "bf16/int8(vq8)",
                                 (2, 2): "q8"}[(w.k_dtype, w.v_dtype)],
-                   "window": w.window, "softcap": w.softcap, "parallelism": "single-gpu"},
+                   "window": w.window, "softcap": w.softcap,
+                   "layout": f"paged(block_size={args.paged})" if args.paged else "contiguous",
+                   "parallelism": "single-gpu"},
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "flops_per_step": flops,
         "attn_ms": round(attn_ms, 5),
         "roofline": {"kernel": "prefill_attn_kernel", "bound": "mfma",
                      "achieved": round(tflops_attn, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops_attn / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(name, prefill_source_hash()),
+                     "traffic": None if args.paged else measured_traffic(name, prefill_source_hash()),
                      "algorithmic_flops_per_launch": flops,
                      "kernel_source_sha256_16": prefill_source_hash(),
                      "note": "the kernel issues twice the algorithmic matrix flops (q and the "
