@@ -210,8 +210,15 @@ __device__ inline const StepArgs* step_of(const StepArgs& s) { return &s; }
 // amdgpu_waves_per_eu(2, 8): at least two waves per SIMD.  Without the hint
 // the allocator spends registers freely (the vq8 kernel spilled into AGPRs at
 // one wave per SIMD); with it the bf16 d128 kernel fits three waves per SIMD.
+// The paged d128 partial kernels (G <= 4, bf16 or f32 keys) are held to
+// three waves per SIMD too: with half as many loads in flight (below) they
+// fit without spilling, where the per-tile block lookups otherwise leave room
+// for two.
+template <int D, int G, int KT, bool PAGED, bool FUSED>
+constexpr int min_waves() { return (PAGED && !FUSED && D == 128 && G <= 4 && KT != kI8) ? 3 : 2; }
+
 template <int D, int G, int KT, int VT, bool PAGED, bool FUSED, bool ILV>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves<D, G, KT, PAGED, FUSED>(), 8))) void
 decode_partial_kernel(const KernelArgs<FUSED> args) {
   const AttnArgs& a = attn_of(args);
   const StepArgs* x = step_of(args);
@@ -225,8 +232,9 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   constexpr int VE = VLB / VB;
   // Eight 16-byte loads per lane in flight (the same bytes in 8-byte loads);
   // half as many for G = 8, whose query and accumulator registers would
-  // otherwise leave room for one wave per SIMD.
-  constexpr int LF = G >= 8 ? kLoadsInFlight / 2 : kLoadsInFlight;
+  // otherwise leave room for one wave per SIMD, and for paged caches, whose
+  // tiles each carry their own block's base (more waves per SIMD instead).
+  constexpr int LF = (G >= 8 || PAGED) ? kLoadsInFlight / 2 : kLoadsInFlight;
   constexpr int LFK = LF * 16 / KLB, LFV = LF * 16 / VLB;
   constexpr int UK = (LFK * KRPL <= kRowsPerChunk) ? LFK : kRowsPerChunk / KRPL;
   constexpr int UV = (LFV * VRPL <= kRowsPerChunk) ? LFV : kRowsPerChunk / VRPL;
