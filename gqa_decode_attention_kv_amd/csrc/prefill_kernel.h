@@ -26,7 +26,9 @@
 //     one XCD (they read the same K and V prefix through its L2), longest
 //     first within it (the causal tail is short).
 //   * Key tiles of 32 rows of K and V are staged in LDS by the whole
-//     work-group with 16-byte loads, double-buffered: one barrier per tile.
+//     work-group with 16-byte loads, double-buffered: one barrier per tile,
+//     or per two tiles (64 rows staged at once) with two query blocks per
+//     wave up to d128.
 //     Padded rows, so the matrix and transposing reads below do not collide
 //     on banks.  The next tile's loads go to registers while the current
 //     tile's products run.
@@ -137,10 +139,10 @@ constexpr int rows_per_group() { return 4 * 16 * QB; }
 // Staging of one operand (K or V) of a tile: EB bytes per element in the
 // cache (2: bf16, 1: int8 codes, widened to bf16 in LDS, which holds them
 // exactly).  NL 16-byte loads per thread cover the tile's 32 rows.
-template <int D, int EB>
+template <int D, int EB, int KT_ROWS>
 struct Stage {
   static constexpr int CPR = D * EB / 16;  // 16-byte chunks per row in the cache
-  static constexpr int TOTAL = kKeys * CPR;
+  static constexpr int TOTAL = KT_ROWS * CPR;
   static constexpr int NL = (TOTAL + 255) / 256;
 };
 
@@ -163,9 +165,13 @@ template <int D, int G, int QB, bool PAGED, bool CAP, int KT, int VT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(
     const PrefillArgs a) {
   constexpr int ROWS = rows_per_group<QB>();  // query rows per work-group
+  // Rows staged per barrier: two 32-key halves with two query blocks per
+  // wave up to d128 (half the barriers and staging bookkeeping per key),
+  // one otherwise (d256 tiles would not fit two work-groups' LDS).
+  constexpr int KST = (QB == 2 && D <= 128) ? 2 * kKeys : kKeys;
   constexpr int KEB = KT == kI8 ? 1 : 2, VEB = VT == kI8 ? 1 : 2;
-  using SK = Stage<D, KEB>;
-  using SV = Stage<D, VEB>;
+  using SK = Stage<D, KEB, KST>;
+  using SV = Stage<D, VEB, KST>;
   constexpr int KSTEPS = D / 32;  // k-steps of the score product
   constexpr int NB = D / 16;      // 16-column blocks of the output
   // LDS row strides in bf16 elements.  K (16-byte pad): a 16-lane group of
@@ -176,10 +182,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int LSV = D + 16;
   // Two buffers of K and V tiles (and, for int8 caches, the tiles' per-token
   // key and value scales): one is read while the next tile is staged.
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKeys * LS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kKeys * LSV];
-  __shared__ float ksc[2][KT == kI8 ? kKeys : 1];
-  __shared__ float vsc[2][VT == kI8 ? kKeys : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][KST * LS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][KST * LSV];
+  __shared__ float ksc[2][KT == kI8 ? KST : 1];
+  __shared__ float vsc[2][VT == kI8 ? KST : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const char* vslab = static_cast<const char*>(a.v) + slab * D * VEB;
   auto clamp_row = [&](int r) { return min(max(r, lo_first), k_end - 1); };
   auto load_tile = [&](int k0) {
-    if (!PAGED && k0 >= lo_first && k0 + kKeys <= k_end) {
+    if (!PAGED && k0 >= lo_first && k0 + KST <= k_end) {
       const char* kt = kslab + static_cast<int64_t>(k0) * (D * KEB);
       const char* vt = vslab + static_cast<int64_t>(k0) * (D * VEB);
 #pragma unroll
@@ -306,9 +312,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           vreg[i] = *reinterpret_cast<const u32x4*>(vt + static_cast<uint32_t>(c / SV::CPR * (D * VEB) + c % SV::CPR * 16));
       }
       if constexpr (KT == kI8 || VT == kI8) {
-        const bool is_k = tid < kKeys;
+        const bool is_k = tid < KST;
         const float* pool = is_k ? a.k_scale : a.v_scale;
-        if (tid < 2 * kKeys && pool != nullptr) sreg = pool[slab + k0 + (tid & (kKeys - 1))];
+        if (tid < 2 * KST && pool != nullptr) sreg = pool[slab + k0 + (tid & (KST - 1))];
       }
       return;
     }
@@ -331,9 +337,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     if constexpr (KT == kI8 || VT == kI8) {
-      const bool is_k = tid < kKeys;
+      const bool is_k = tid < KST;
       const float* pool = is_k ? a.k_scale : a.v_scale;
-      if (tid < 2 * kKeys && pool != nullptr) sreg = pool[row_off(clamp_row(k0 + (tid & (kKeys - 1)))) / D];
+      if (tid < 2 * KST && pool != nullptr) sreg = pool[row_off(clamp_row(k0 + (tid & (KST - 1)))) / D];
     }
   };
   // Write the staged registers to LDS buffer `buf` (int8 codes widened to
@@ -370,10 +376,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     if constexpr (KT == kI8) {
-      if (tid < kKeys) ksc[buf][tid] = sreg;
+      if (tid < KST) ksc[buf][tid] = sreg;
     }
     if constexpr (VT == kI8) {
-      if (tid >= kKeys && tid < 2 * kKeys) vsc[buf][tid - kKeys] = sreg;
+      if (tid >= KST && tid < 2 * KST) vsc[buf][tid - KST] = sreg;
     }
   };
 
@@ -382,16 +388,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // stages tile j + 1 (loaded during iteration j - 1) into the other buffer,
   // whose previous tile every wave finished reading before the last
   // barrier, and starts the loads of tile j + 2: one barrier per tile.
-  const int n_tiles = (k_end - k_begin + kKeys - 1) / kKeys;
+  const int n_tiles = (k_end - k_begin + KST - 1) / KST;
   load_tile(k_begin);
   store_tile(0);
-  if (n_tiles > 1) load_tile(k_begin + kKeys);
+  if (n_tiles > 1) load_tile(k_begin + KST);
   __syncthreads();
   for (int j = 0; j < n_tiles; ++j) {
-    const int k0 = k_begin + j * kKeys;
     const int buf = j & 1;
-    const uint16_t* kb = ks[buf];
-    const uint16_t* vb_ = vs[buf];
+#pragma unroll
+    for (int h = 0; h < KST / kKeys; ++h) {
+    const int k0 = k_begin + j * KST + h * kKeys;  // this half's first key
+    if (h > 0 && k0 >= k_end) break;               // wave-uniform: past the last key
+    const uint16_t* kb = ks[buf] + h * kKeys * LS;
+    const uint16_t* vb_ = vs[buf] + h * kKeys * LSV;
+    const float* kscb = ksc[buf] + (KT == kI8 ? h * kKeys : 0);
+    const float* vscb = vsc[buf] + (VT == kI8 ? h * kKeys : 0);
 
     // S^T for keys k0 + mb*16 + (0..15) against the wave's query blocks:
     // lane holds keys k0 + mb*16 + 4*quad + j of query qi of block q.  The
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int e = 0; e < 8; ++e) {
         float x = s[q][e >> 2][e & 3];
         if constexpr (KT == kI8) {
-          const float kscale = ksc[buf][(e >> 2) * 16 + 4 * quad + (e & 3)];
+          const float kscale = kscb[(e >> 2) * 16 + 4 * quad + (e & 3)];
           x = cap ? capped(x * kscale, cap, cap_c, cap_inv) - r[q] : fmaf(x, kscale, -r[q]);
         } else if constexpr (cap) {
           x = capped(x, cap, cap_c, cap_inv) - r[q];
@@ -507,7 +518,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // codes are the V operand), the sum l does not.
       if constexpr (VT == kI8) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] *= vsc[buf][(e < 4) ? 4 * quad + e : 16 + 4 * quad + (e - 4)];
+        for (int e = 0; e < 8; ++e) p[e] *= vscb[(e < 4) ? 4 * quad + e : 16 + 4 * quad + (e - 4)];
       }
       split8(p, ph[q], pl[q]);
     }
@@ -535,9 +546,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
 
+    }  // halves
+
     if (j + 1 < n_tiles) {
       store_tile(buf ^ 1);
-      if (j + 2 < n_tiles) load_tile(k0 + 2 * kKeys);
+      if (j + 2 < n_tiles) load_tile(k_begin + (j + 2) * KST);
     }
     __syncthreads();  // tile j + 1 is staged; every wave is done with tile j
   }
