@@ -84,6 +84,13 @@ SMALL = [
     case("q8-d256-g1-softcap", 256, 1, 2, 30, [90], softcap=20.0, seed=22, kv=Q8),
     case("vq8-d128-g4-b32-two-blocks", 128, 4, 8, 72,
          np.random.default_rng(23).integers(72, 241, 32), seed=23, kv=VQ8),
+    # Two query blocks per wave stage 64 key rows per barrier and compute
+    # them as two halves: int8 keys (each half's key scales) and a paged
+    # int8-value cache on that path.
+    case("q8-d128-g4-b32-two-blocks", 128, 4, 8, 72,
+         np.random.default_rng(24).integers(72, 301, 32), window=150, seed=24, kv=Q8),
+    case("vq8-d128-g2-b32-two-blocks-paged", 128, 2, 8, 140,
+         np.random.default_rng(25).integers(140, 331, 32), sink=True, seed=25, kv=VQ8, bs=32),
 ]
 
 
