@@ -155,6 +155,55 @@ def pin_freqs_llama3_continuous(o):
     assert np.all(div[1:] / div[:-1] >= 1.0 - 1e-12)
 
 
+def pin_freqs_llama3_smooth_band_golden(o):
+    """The divisors inside the smooth band for the two Llama shapes
+    (tests/golden/llama3_smooth_band.json: FREETOKEN Changes/Results for the
+    parameters, UAII P0.2 for Hugging Face's formulation), and which pair
+    indices are kept, blended and divided."""
+    for case in _golden("llama3_smooth_band.json")["cases"]:
+        d, theta, factor = case["head_dim"], case["theta"], case["factor"]
+        f = o.rope_freqs(d, O.PLAIN, theta)
+        g = o.rope_freqs(d, O.LLAMA3, theta, factor, case["low"], case["high"], case["original"])
+        div = f / g
+        k0, k1 = case["kept"]
+        s0, s1 = case["smooth"]
+        c0, c1 = case["scaled"]
+        assert np.all(div[k0:k1 + 1] == 1.0), case["model"]
+        assert np.allclose(div[c0:c1 + 1], factor, rtol=1e-15, atol=0), case["model"]
+        got = div[s0:s1 + 1]
+        assert got.size == len(case["smooth_divisors"])
+        for x, s in zip(got, case["smooth_divisors"]):
+            decimals = len(s.split(".")[1])
+            assert abs(x - float(s)) <= 0.5 * 10.0 ** -decimals * (1 + 1e-9), (case["model"], x, s)
+
+
+def pin_freqs_llama3_blend_affine_in_frequency(o):
+    """Inside the smooth band the frequency is a blend g = (1 - mu) f / factor
+    + mu f.  Recovering mu = (g - f/factor) / (f - f/factor) on a dense grid of
+    frequencies (huge head_dim), mu must be an affine function of f: it is a
+    ramp in orig / wavelength = orig f / (2 pi), not in the wavelength and
+    not a curve.  The line must reach 0 at the low-frequency edge (wavelength
+    orig/low) and 1 at the high-frequency edge (wavelength orig/high), for
+    several factors and band parameters."""
+    for d, theta, factor, low, high, orig in ((1 << 16, 5e5, 8.0, 1.0, 4.0, 8192.0),
+                                             (1 << 15, 5e5, 32.0, 1.0, 4.0, 8192.0),
+                                             (1 << 15, 1e6, 4.0, 2.0, 8.0, 4096.0)):
+        f = o.rope_freqs(d, O.PLAIN, theta)
+        g = o.rope_freqs(d, O.LLAMA3, theta, factor, low, high, orig)
+        lam = 2 * math.pi / f
+        mid = (lam > orig / high) & (lam < orig / low)
+        assert mid.sum() > 100
+        fm = f[mid]
+        mu = (g[mid] - fm / factor) / (fm - fm / factor)
+        A = np.stack([fm, np.ones_like(fm)], axis=1)
+        coef, *_ = np.linalg.lstsq(A, mu, rcond=None)
+        assert np.max(np.abs(A @ coef - mu)) < 1e-9, (factor, np.max(np.abs(A @ coef - mu)))
+        f_low_edge = 2 * math.pi * low / orig
+        f_high_edge = 2 * math.pi * high / orig
+        assert abs(coef[0] * f_low_edge + coef[1]) < 1e-9
+        assert abs(coef[0] * f_high_edge + coef[1] - 1.0) < 1e-9
+
+
 def pin_freqs_llama3_factor_one(o):
     """factor = 1 reduces llama3 scaling to plain frequencies."""
     f = o.rope_freqs(128, O.PLAIN, 5e5)
@@ -400,6 +449,26 @@ def pin_quantizer_crafted(o):
         codes, scale = o.quantize_v(v)
         assert scale == np.float32(case["scale"]), (case, scale)
         assert codes.tolist() == case["codes"], (case, codes.tolist())
+
+
+def pin_quantizer_near_ties(o):
+    """vq8 quantiser at non-power-of-two scales, with values next to a
+    half-way point (k + 1/2) * scale (tests/golden/vq8_near_ties.json, from
+    exact rational arithmetic in make_vq8_near_ties.py).  Each vector holds
+    values whose code changes if the quotient is taken as v * (1/scale)
+    instead of the f32 division v / scale, and values whose f32 quotient is
+    exactly a half-way point although the exact quotient is not, so that a
+    quotient kept in double precision would round the other way."""
+    doc = _golden("vq8_near_ties.json")
+    n_recip = n_double = 0
+    for case in doc["cases"]:
+        v = np.array(case["v"], dtype=np.float32)
+        codes, scale = o.quantize_v(v)
+        assert scale == np.float32(case["scale"]), (scale, case["scale"])
+        assert codes.tolist() == case["codes"], (codes.tolist(), case["codes"])
+        n_recip += case["n_recip_sensitive"]
+        n_double += case["n_double_sensitive"]
+    assert n_recip >= 10 and n_double >= 5
 
 
 def pin_quantizer_properties(o):

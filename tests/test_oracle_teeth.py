@@ -25,7 +25,14 @@ MUTANTS = [
     ("freq_exponent", "pow(theta, -2.0 * (double)i / (double)d)", "pow(theta, -(double)i / (double)d)"),
     ("llama3_smooth_dropped", "g[i] = (1.0 - mu) * f / factor + mu * f;", "g[i] = f / factor;"),
     ("llama3_mu_swapped", "g[i] = (1.0 - mu) * f / factor + mu * f;", "g[i] = mu * f / factor + (1.0 - mu) * f;"),
-    ("gqa_modulo_map", "int u = h / G;\n    int64_t slab = (int64_t)b * Hkv + u;\n    int64_t lo = visible_lo(L, W);\n    if (j0",
+    ("llama3_mu_linear_in_wavelength", "double mu = (orig / lambda - low) / (high - low);",
+     "double mu = (orig / low - lambda) / (orig / low - orig / high);"),
+    ("llama3_mu_squared", "double mu = (orig / lambda - low) / (high - low);",
+     "double mu = (orig / lambda - low) / (high - low);\n                mu = mu * mu;"),
+    ("quantizer_reciprocal_multiply", "float t = v[i] / scale;", "float t = v[i] * (1.0f / scale);"),
+    ("quantizer_double_quotient", "float t = v[i] / scale;\n        float r = roundf(t);",
+     "double t = (double)v[i] / (double)scale;\n        float r = (float)round(t);"),
+    ("gqa_modulo_map","int u = h / G;\n    int64_t slab = (int64_t)b * Hkv + u;\n    int64_t lo = visible_lo(L, W);\n    if (j0",
      "int u = h % Hkv;\n    int64_t slab = (int64_t)b * Hkv + u;\n    int64_t lo = visible_lo(L, W);\n    if (j0"),
     ("gqa_modulo_map_scores", "int u = h / G;\n    int64_t slab = (int64_t)b * Hkv + u;\n    int64_t lo = visible_lo(L, W);\n    double scale",
      "int u = h % Hkv;\n    int64_t slab = (int64_t)b * Hkv + u;\n    int64_t lo = visible_lo(L, W);\n    double scale"),
