@@ -3,11 +3,12 @@
 // kernel launches on the caller's stream.  See include/uaii_decode.h for
 // the contract of each call.
 //
-// Refusal style follows "Algenta - Model support matrix" (Conformance CLI:
-// a refusal names the exact fact, its value and the supported range) and
-// "Universal AI Inference - Hugging Face decoder completeness" (section 6:
-// every message says what failed and what to do; support contract: fail
-// closed with InvalidArgument / NotImplemented).
+// Refusals are typed and specific, after "Algenta - Model support matrix"
+// (Conformance CLI: the refusal identifies the offending fact with its value
+// and the accepted range) and "Universal AI Inference - Hugging Face decoder
+// completeness" (section 6 on error messages, which state the failure and
+// the remedy; support contract: unsupported inputs fail closed as
+// InvalidArgument or NotImplemented).
 #include "uaii_decode.h"
 
 #include <algorithm>

@@ -149,6 +149,15 @@ WORKLOADS = {
     "gemma2-global": Workload("gemma2-global", 8, 16, 8, 256, ("fixed", 32768), 32768, BF16, BF16,
                               Rope(NEOX, PLAIN, 1000000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),
                               window=0, softcap=50.0, split_size=4096, seed=(5, 1)),
+    # The same Gemma-2 pair read the other way: the "RMSNorm gain (1 + w)" of
+    # the configuration taken as the layer's input norm, off this path, so no
+    # QK-norm (same seeds, so the draws are those of the pair above).
+    "gemma2-local-noqknorm": Workload("gemma2-local-noqknorm", 8, 16, 8, 256, ("fixed", 32768), 32768,
+                                      BF16, BF16, Rope(NEOX, PLAIN, 10000.0), window=4096,
+                                      softcap=50.0, split_size=512, seed=(5, 0)),
+    "gemma2-global-noqknorm": Workload("gemma2-global-noqknorm", 8, 16, 8, 256, ("fixed", 32768),
+                                       32768, BF16, BF16, Rope(NEOX, PLAIN, 1000000.0), window=0,
+                                       softcap=50.0, split_size=4096, seed=(5, 1)),
     # The measured workload: B=32 sequences of 8192 keys, 32/8 heads, d=128, bf16 KV.
     # Split size 4096 (tuned): 2 splits per sequence, 512 work items, each taken
     # by one cooperative work-group of four waves (two work-groups per CU).

@@ -343,8 +343,9 @@ uaii_status uaii_kv_produce_chunk(const uaii_attn_shape *shape, const uaii_rope 
  * with m the largest of the s_j (and sink_h).  This is uaii_decode_attn +
  * uaii_decode_combine(_sink) of each query over its own prefix, in one
  * launch on the matrix cores.
- *   cache     bf16 keys and values (other dtypes are refused), contiguous
- *             or paged
+ *   cache     contiguous or paged, with (k_dtype, v_dtype) one of
+ *             (BF16, BF16), (BF16, I8) (vq8) or (I8, I8) (q8); f32 keys or
+ *             values are refused with UAII_ERR_NOT_IMPLEMENTED
  *   q         device [batch][T][n_heads][head_dim] f32 (q_out of the chunk
  *             producer)
  *   seq_lens  host [batch], each in [T, capacity]

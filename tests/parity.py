@@ -201,17 +201,21 @@ def compare_partials(st, ref, w, lens, pick=None, max_per_seq=None, rng=None):
 
 
 def run_and_compare(w: W.Workload, lens, max_partials_per_seq=None, seed=0, block_size=None,
-                    fused=False):
+                    fused=False, prep=None):
     """Run one step on the GPU (three calls, or the single launch with
     fused=True) and in the oracle; compare every output element, the
     produced cache rows (and that nothing else in the caches changed) and
-    the split partials.  Returns (max abs error, tolerance, class)."""
+    the split partials.  ``prep(inputs)``, if given, edits the seeded inputs
+    in place before either side sees them.  Returns (max abs error,
+    tolerance, class)."""
     lens = np.asarray(lens, dtype=np.int32)
     say(f"case {w.name}{' fused' if fused else ''}: B={w.batch} H={w.n_heads}/{w.n_kv_heads} d={w.head_dim} "
         f"K/V={w.k_dtype}/{w.v_dtype} lens={lens.tolist()[:8]} S={w.split_size} W={w.window} "
         f"cap={w.softcap} rope={w.rope.pairing}/{w.rope.scaling} norm={w.qk_norm.enabled} "
         f"sink={w.sink}")
     inputs = W.make_inputs(w, seq_lens=lens)
+    if prep is not None:
+        prep(inputs)
     paged = W.make_paged(inputs, block_size) if block_size else None
     if paged:
         say(f"  paged: block_size={paged.block_size} max_blocks={paged.max_blocks} "

@@ -61,7 +61,7 @@ def test_fused_sweep_cell(cell):
 
 
 FULL = ["tiny", "llama3.2-1b", "gpt-oss-20b-sliding", "gemma3-27b-local", "gemma2-local",
-        "qwen3-vq8", W.HEADLINE]
+        "gemma2-local-noqknorm", "gemma2-global-noqknorm", "qwen3-vq8", W.HEADLINE]
 
 
 @pytest.mark.parametrize("name", FULL)

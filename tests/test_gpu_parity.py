@@ -93,7 +93,7 @@ def test_small_case(spec):
 
 
 FULL = ["tiny", "llama3.2-1b", "llama3.1-8b-ragged", "qwen3-vq8", "gemma2-local", "gemma2-global",
-        W.HEADLINE]
+        "gemma2-local-noqknorm", "gemma2-global-noqknorm", W.HEADLINE]
 
 
 @pytest.mark.parametrize("name", FULL)
