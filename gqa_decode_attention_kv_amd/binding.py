@@ -22,8 +22,8 @@ ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 ROPE_PLAIN, ROPE_LLAMA3, ROPE_LINEAR, ROPE_YARN = 0, 1, 2, 3
 
 EXPORTS = ("uaii_last_error", "uaii_kv_produce", "uaii_decode_attn", "uaii_decode_combine",
-           "uaii_decode_combine_sink", "uaii_decode_step", "uaii_kv_produce_chunk",
-           "uaii_prefill_attn")
+           "uaii_decode_combine_sink", "uaii_decode_step", "uaii_decode_step_noalloc",
+           "uaii_kv_produce_chunk", "uaii_prefill_attn")
 
 
 class UaiiError(RuntimeError):
@@ -88,6 +88,11 @@ def load() -> C.CDLL:
                                          vp, vp, vp, ip, C.POINTER(KVCache), C.c_float, C.c_int32,
                                          C.c_float, C.c_int32, C.c_int32, vp, vp, vp, vp, vp, vp,
                                          vp]
+        lib.uaii_decode_step_noalloc.restype = C.c_int
+        lib.uaii_decode_step_noalloc.argtypes = [C.POINTER(Shape), C.POINTER(Rope),
+                                                 C.POINTER(QKNorm), vp, vp, vp, ip,
+                                                 C.POINTER(KVCache), C.c_float, C.c_int32,
+                                                 C.c_float, C.c_int32, vp, vp, vp, vp]
         lib.uaii_kv_produce_chunk.restype = C.c_int
         lib.uaii_kv_produce_chunk.argtypes = [C.POINTER(Shape), C.POINTER(Rope), C.POINTER(QKNorm),
                                               vp, vp, vp, ip, C.c_int32, C.POINTER(KVCache), vp,
@@ -157,6 +162,17 @@ def decode_step(shape: Shape, rope: Rope, qk_norm: QKNorm | None, q_in: int, k_i
                                    q_in, k_in, v_in, p, C.byref(cache), scale, window, softcap,
                                    split_size, max_splits, sinks, q_out, part_o, part_lse,
                                    counters, out, stream))
+
+
+def decode_step_noalloc(shape: Shape, rope: Rope, qk_norm: QKNorm | None, q_in: int, k_in: int,
+                        v_in: int, seq_lens, cache: KVCache, scale: float, window: int,
+                        softcap: float, split_size: int, sinks: int | None, q_out: int, out: int,
+                        stream: int = 0) -> None:
+    arr, p = _host_i32(seq_lens, shape.batch)
+    _check(load().uaii_decode_step_noalloc(C.byref(shape), C.byref(rope),
+                                           C.byref(qk_norm) if qk_norm is not None else None,
+                                           q_in, k_in, v_in, p, C.byref(cache), scale, window,
+                                           softcap, split_size, sinks, q_out, out, stream))
 
 
 def kv_produce_chunk(shape: Shape, rope: Rope, qk_norm: QKNorm | None, q_in: int, k_in: int,

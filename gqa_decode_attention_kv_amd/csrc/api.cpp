@@ -341,7 +341,7 @@ uaii_status produce_args(const char* fn, const uaii_attn_shape* shape, const uai
 uaii_status attn_args(const char* fn, const uaii_attn_shape* shape, const uaii_kv_cache* cache,
                       const float* q, bool check_q, const int32_t* seq_lens, float scale, int32_t window,
                       float softcap, int32_t split_size, int32_t max_splits, float* part_o, float* part_lse,
-                      uaii::AttnArgs* out) {
+                      uaii::AttnArgs* out, bool check_parts = true) {
   uaii_status st = check_lens(fn, shape, seq_lens, cache->capacity, split_size, max_splits, window);
   if (st != UAII_OK) return st;
   REQUIRE(std::isfinite(softcap) && softcap >= 0.0f, kInvalid,
@@ -353,8 +353,10 @@ uaii_status attn_args(const char* fn, const uaii_attn_shape* shape, const uaii_k
           "query_pre_attn_scalar is refused)",
           static_cast<double>(scale), want);
   if (check_q) CHECK_PTR("q", q, 16);
-  CHECK_PTR("part_o", part_o, 16);
-  CHECK_PTR("part_lse", part_lse, 4);
+  if (check_parts) {
+    CHECK_PTR("part_o", part_o, 16);
+    CHECK_PTR("part_lse", part_lse, 4);
+  }
 
   uaii::AttnArgs a{};
   a.H = shape->n_heads;
@@ -386,6 +388,18 @@ uaii_status attn_args(const char* fn, const uaii_attn_shape* shape, const uaii_k
   *out = a;
   return UAII_OK;
 }
+
+// The one-call step (validation, then one kernel or three) shared by
+// uaii_decode_step and uaii_decode_step_noalloc; fn names the entry point
+// in messages.  With scratch set, part_o, part_lse and counters are ignored
+// and taken from the GPU's static scratch once every argument has passed.
+uaii_status decode_step_impl(const char* fn, const uaii_attn_shape* shape, const uaii_rope* rope,
+                             const uaii_qk_norm* qk_norm, const float* q_in, const float* k_in,
+                             const float* v_in, const int32_t* seq_lens, const uaii_kv_cache* cache,
+                             float scale, int32_t window, float softcap, int32_t split_size,
+                             int32_t max_splits, const float* sinks, float* q_out, float* part_o,
+                             float* part_lse, int32_t* counters, float* out, void* stream,
+                             bool scratch);
 
 }  // namespace
 
@@ -543,8 +557,61 @@ uaii_status uaii_decode_step(const uaii_attn_shape* shape, const uaii_rope* rope
                              const uaii_kv_cache* cache, float scale, int32_t window, float softcap,
                              int32_t split_size, int32_t max_splits, const float* sinks, float* q_out,
                              float* part_o, float* part_lse, int32_t* counters, float* out, void* stream) {
-  const char* fn = "uaii_decode_step";
   g_error.clear();
+  return decode_step_impl("uaii_decode_step", shape, rope, qk_norm, q_in, k_in, v_in, seq_lens, cache, scale,
+                          window, softcap, split_size, max_splits, sinks, q_out, part_o, part_lse, counters, out,
+                          stream, false);
+}
+
+uaii_status uaii_decode_step_noalloc(const uaii_attn_shape* shape, const uaii_rope* rope,
+                                     const uaii_qk_norm* qk_norm, const float* q_in, const float* k_in,
+                                     const float* v_in, const int32_t* seq_lens, const uaii_kv_cache* cache,
+                                     float scale, int32_t window, float softcap, int32_t split_size,
+                                     const float* sinks, float* q_out, float* out, void* stream) {
+  const char* fn = "uaii_decode_step_noalloc";
+  g_error.clear();
+  uaii_status st = check_shape(fn, shape);
+  if (st != UAII_OK) return st;
+  st = check_cache(fn, cache);
+  if (st != UAII_OK) return st;
+  REQUIRE(seq_lens != nullptr, kInvalid, "seq_lens is NULL; pass a host array of batch=%d lengths", shape->batch);
+  REQUIRE(split_size >= 1, kInvalid, "split_size=%d is invalid (must be >= 1)", split_size);
+  int32_t max_len = 1;
+  for (int b = 0; b < shape->batch; ++b) {
+    REQUIRE(seq_lens[b] >= 1 && seq_lens[b] <= cache->capacity, kInvalid,
+            "seq_lens[%d]=%d is outside [1, capacity=%d]", b, seq_lens[b], cache->capacity);
+    max_len = std::max(max_len, seq_lens[b]);
+  }
+  const int64_t max_splits = (static_cast<int64_t>(max_len) + split_size - 1) / split_size;
+  const int64_t rows = static_cast<int64_t>(shape->batch) * shape->n_heads * max_splits;
+  const int64_t lse_bytes = (rows * 4 + 255) / 256 * 256;
+  const int64_t o_bytes = rows * shape->head_dim * 4;
+  const int64_t room = static_cast<int64_t>(uaii::kNoAllocScratchBytes - uaii::kNoAllocCounterBytes);
+  REQUIRE(static_cast<int64_t>(shape->batch) * shape->n_kv_heads <= uaii::kNoAllocCounterWords, kNotImpl,
+          "batch*n_kv_heads=%lld is not supported (supported: up to %d arrival counters in the static "
+          "scratch); use uaii_decode_step with a caller-owned counter buffer",
+          static_cast<long long>(shape->batch) * shape->n_kv_heads, uaii::kNoAllocCounterWords);
+  REQUIRE(lse_bytes + o_bytes <= room, kNotImpl,
+          "the split partials need %lld bytes (batch*n_heads*ceil(max seq_len/split_size)*(head_dim+1)*4, "
+          "split_size=%d) and the static scratch holds %lld; raise split_size, or use uaii_decode_step "
+          "with caller-owned partial buffers",
+          static_cast<long long>(lse_bytes + o_bytes), split_size, static_cast<long long>(room));
+  return decode_step_impl(fn, shape, rope, qk_norm, q_in, k_in, v_in, seq_lens, cache, scale, window, softcap,
+                          split_size, static_cast<int32_t>(max_splits), sinks, q_out, nullptr, nullptr, nullptr,
+                          out, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+uaii_status decode_step_impl(const char* fn, const uaii_attn_shape* shape, const uaii_rope* rope,
+                             const uaii_qk_norm* qk_norm, const float* q_in, const float* k_in,
+                             const float* v_in, const int32_t* seq_lens, const uaii_kv_cache* cache,
+                             float scale, int32_t window, float softcap, int32_t split_size,
+                             int32_t max_splits, const float* sinks, float* q_out, float* part_o,
+                             float* part_lse, int32_t* counters, float* out, void* stream,
+                             bool scratch) {
   uaii_status st = check_shape(fn, shape);
   if (st != UAII_OK) return st;
   st = check_cache(fn, cache);
@@ -553,16 +620,30 @@ uaii_status uaii_decode_step(const uaii_attn_shape* shape, const uaii_rope* rope
   st = produce_args(fn, shape, rope, qk_norm, q_in, k_in, v_in, cache, q_out, &x.p);
   if (st != UAII_OK) return st;
   st = attn_args(fn, shape, cache, q_out, false, seq_lens, scale, window, softcap, split_size, max_splits, part_o,
-                 part_lse, &x.a);
+                 part_lse, &x.a, !scratch);
   if (st != UAII_OK) return st;
   if (sinks != nullptr) CHECK_PTR("sinks", sinks, 4);
-  CHECK_PTR("counters", counters, 4);
+  if (!scratch) CHECK_PTR("counters", counters, 4);
   CHECK_PTR("out", out, 16);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (scratch) {
+    // Every argument is valid: only now is the device touched, to find this
+    // GPU's static scratch (counters, then part_lse, then part_o).
+    void* base = nullptr;
+    st = device_status(fn, uaii::noalloc_scratch(&base, s));
+    if (st != UAII_OK) return st;
+    const int64_t rows = static_cast<int64_t>(shape->batch) * shape->n_heads * max_splits;
+    unsigned char* p = static_cast<unsigned char*>(base);
+    counters = reinterpret_cast<int32_t*>(p);
+    part_lse = reinterpret_cast<float*>(p + uaii::kNoAllocCounterBytes);
+    part_o = reinterpret_cast<float*>(p + uaii::kNoAllocCounterBytes + (rows * 4 + 255) / 256 * 256);
+    x.a.part_o = part_o;
+    x.a.part_lse = part_lse;
+  }
   x.sinks = sinks;
   x.out = out;
   x.counters = counters;
   const int G = shape->n_heads / shape->n_kv_heads;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   const int items = x.a.t.work_prefix[shape->batch] * shape->n_kv_heads;
   if (items <= uaii::kStepOneLaunchMax) {
     if (cache->block_table != nullptr)
@@ -593,10 +674,6 @@ uaii_status uaii_decode_step(const uaii_attn_shape* shape, const uaii_rope* rope
   c.t = x.a.t;
   return device_status(fn, uaii::launch_decode_combine(shape->head_dim, shape->batch, c, s));
 }
-
-}  // extern "C"
-
-namespace {
 
 uaii_status combine(const char* fn, const uaii_attn_shape* shape, const int32_t* seq_lens, int32_t window,
                     int32_t split_size, int32_t max_splits, const float* part_o, const float* part_lse,

@@ -1,6 +1,7 @@
 // Internal interface between the C-ABI host code (api.cpp) and the HIP
-// kernels.  Everything here is passed to kernels by value: the library keeps
-// no device-side state and allocates nothing.
+// kernels.  Everything here is passed to kernels by value: the library
+// allocates nothing, and its only device-side state is the static scratch
+// array of uaii_decode_step_noalloc (decode_step_noalloc.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -130,6 +131,19 @@ struct StepArgs {
   float* out;
   int32_t* counters;   // [B][Hkv] arrival counters: zero on entry, zero on exit
 };
+
+// Static scratch of uaii_decode_step_noalloc, one array per GPU: the
+// arrival counters in [0, kNoAllocCounterBytes), then the split partials
+// (part_lse, then part_o, each starting on a 256-byte boundary), at most
+// kNoAllocScratchBytes in all.
+constexpr int kNoAllocCounterWords = 16384;
+constexpr size_t kNoAllocCounterBytes = static_cast<size_t>(kNoAllocCounterWords) * 4;
+constexpr size_t kNoAllocScratchBytes = (static_cast<size_t>(16) << 20) + kNoAllocCounterBytes;
+
+// The current GPU's scratch address (hipGetSymbolAddress, taken once per
+// device); the first call on a device also enqueues a kernel on `stream`
+// that zeroes the counters.
+hipError_t noalloc_scratch(void** base, hipStream_t stream);
 
 hipError_t launch_kv_produce(const ProduceArgs& a, hipStream_t stream);
 

@@ -311,6 +311,32 @@ uaii_status uaii_decode_step(const uaii_attn_shape *shape, const uaii_rope *rope
                              float *part_lse, int32_t *counters, float *out,
                              void *stream);
 
+/* uaii_decode_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The caller passes the inputs and outputs only; the split
+ * partials and arrival counters live in a static scratch array that the
+ * library holds on each GPU it runs on until the process ends
+ * (16 MiB + 64 KiB per GPU).  The call allocates nothing and frees nothing.
+ *   arguments   as uaii_decode_step, without max_splits (taken as
+ *               ceil(max seq_len / split_size)) and without part_o,
+ *               part_lse and counters
+ * Limits, refused with UAII_ERR_NOT_IMPLEMENTED before anything is
+ * launched: batch*n_heads*ceil(max seq_len/split_size)*(head_dim+1)*4 bytes
+ * of partials at most 16 MiB (256-byte alignment of the lse block
+ * included), and batch*n_kv_heads <= 16384.
+ * Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ * partials: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and must not be issued.  The
+ * counters are zeroed by a kernel enqueued on the stream of the first call
+ * on each GPU, and every completed call leaves them at zero. */
+uaii_status uaii_decode_step_noalloc(const uaii_attn_shape *shape, const uaii_rope *rope,
+                                     const uaii_qk_norm *qk_norm, const float *q_in,
+                                     const float *k_in, const float *v_in,
+                                     const int32_t *seq_lens, const uaii_kv_cache *cache,
+                                     float scale, int32_t window, float softcap,
+                                     int32_t split_size, const float *sinks, float *q_out,
+                                     float *out, void *stream);
+
 /* --------------------------------------------------------------------------
  * Chunks of new tokens (prefill)
  * ------------------------------------------------------------------------ */

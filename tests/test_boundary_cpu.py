@@ -369,3 +369,43 @@ def test_prefill_valid_calls_reach_the_launch():
         with pytest.raises(B.UaiiError) as ei:
             fn()
         assert ei.value.status == B.ERR_DEVICE
+
+
+def step_noalloc(sh=None, ca=None, lens=(10, 20), split=16, window=0, q_out=FAKE, out=FAKE):
+    sh = sh or shape()
+    rope = B.Rope(B.ROPE_NEOX, B.ROPE_PLAIN, 1e4, 1.0, 1.0, 4.0, 8192)
+    B.decode_step_noalloc(sh, rope, None, FAKE, FAKE, FAKE, lens, ca or cache(),
+                          1.0 / math.sqrt(sh.head_dim), window, 0.0, split, None, q_out, out, 0)
+
+
+@host_only
+@pytest.mark.parametrize("case", [
+    # 32 * 64 * 512 splits * 129 * 4 bytes > 16 MiB
+    ("partials beyond the scratch", lambda: step_noalloc(sh=shape(b=32, h=64, hkv=8, d=128),
+                                                         ca=cache(cap=8192), lens=[8192] * 32,
+                                                         split=16),
+     NI, ["static scratch holds", "split_size=16"]),
+    ("counters beyond the scratch", lambda: step_noalloc(sh=shape(b=32, h=1024, hkv=1024, d=64),
+                                                         lens=[1] * 32, split=64),
+     NI, ["batch*n_kv_heads=32768"]),
+    ("len 0", lambda: step_noalloc(lens=(0, 5)), INV, ["seq_lens[0]=0"]),
+    ("len > cap", lambda: step_noalloc(lens=(65, 5)), INV, ["seq_lens[0]=65"]),
+    ("split 0", lambda: step_noalloc(split=0), INV, ["split_size=0"]),
+    ("window", lambda: step_noalloc(window=-1), INV, ["window=-1"]),
+    ("out null", lambda: step_noalloc(out=None), INV, ["out is NULL"]),
+    ("head_dim", lambda: step_noalloc(sh=shape(d=96)), NI, ["head_dim=96"]),
+], ids=lambda c: c[0])
+def test_decode_step_noalloc_refusals(case):
+    _, fn, status, needles = case
+    msg = refused(fn, status, *needles)
+    assert msg.startswith("uaii_decode_step_noalloc: ")
+
+
+@host_only
+def test_decode_step_noalloc_valid_call_reaches_the_device():
+    """A valid call gets past validation; with no GPU, taking the scratch
+    address on the device fails with HIP's own text."""
+    with pytest.raises(B.UaiiError) as ei:
+        step_noalloc()
+    assert ei.value.status == B.ERR_DEVICE
+    assert ei.value.message.startswith("uaii_decode_step_noalloc: HIP error")
