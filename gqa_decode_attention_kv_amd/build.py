@@ -1,4 +1,6 @@
-"""Build ``libuaii_decode.so`` (HIP for gfx950) in-tree with hipcc.
+"""Build ``libuaii_decode.so`` (HIP for gfx950) in-tree with hipcc, and the
+measurement probe ``libuaii_probe.so`` (a plain streaming read, used only by
+the benchmark to find the practical HBM read rate).
 
 Each translation unit compiles in its own process, then one link step.
 Flags: -O3, gfx950 only, and packed-FP32 instructions disabled
@@ -16,6 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libuaii_decode.so")
+PROBE_LIBRARY = os.path.join(HERE, "libuaii_probe.so")
+PROBE_SOURCES = ["stream_probe.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "kv_produce.hip", "decode_partial.hip", "decode_partial_paged.hip",
@@ -43,23 +47,28 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every translation unit, then link both libraries; returns the
+    path of the decode library."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
     cmds = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
-        objs.append(obj)
+    objs = {}
+    for lib, sources in ((LIBRARY, SOURCES), (PROBE_LIBRARY, PROBE_SOURCES)):
+        objs[lib] = []
+        for src in sources:
+            obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            cmds.append([HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+            objs[lib].append(obj)
     with ThreadPoolExecutor(len(cmds)) as ex:
         for err in ex.map(_run, cmds):
             if err and verbose:
                 sys.stderr.write(err + "\n")
-    tmp = LIBRARY + ".tmp"
-    err = _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    if err and verbose:
-        sys.stderr.write(err + "\n")
-    os.replace(tmp, LIBRARY)
+    for lib, lib_objs in objs.items():
+        tmp = lib + ".tmp"
+        err = _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *lib_objs, "-o", tmp])
+        if err and verbose:
+            sys.stderr.write(err + "\n")
+        os.replace(tmp, lib)
     return LIBRARY
 
 

@@ -1,0 +1,60 @@
+// Measurement probe, not part of the decode path: a plain streaming read of
+// device memory, used to find the HBM read rate this part sustains in
+// practice, the ceiling the bandwidth-bound decode kernels are compared with.
+//
+// Each work-group of four waves reads one contiguous range (one sequential
+// stream per work-group) with 16-byte non-temporal loads, eight in flight
+// per lane.  The loaded words are folded into a value that is stored only
+// if it equals a constant no input here produces, so the loads stay live
+// and almost nothing is written.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kInFlight = 8;
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ src, size_t n,
+                                                               size_t per_group, uint32_t* sink) {
+  const size_t begin = static_cast<size_t>(blockIdx.x) * per_group;
+  const size_t end = begin + per_group < n ? begin + per_group : n;
+  uint32_t acc = 0;
+  size_t i = begin + threadIdx.x;
+  for (; i + (kInFlight - 1) * kThreads < end; i += kInFlight * kThreads) {
+    u32x4 v[kInFlight];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) v[k] = __builtin_nontemporal_load(src + i + k * kThreads);
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < end; i += kThreads) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+}  // namespace
+
+// Reads `bytes` bytes at `src` (device, 16-byte aligned, a multiple of 16),
+// `bytes_per_group` bytes per work-group (a multiple of 16).  `sink` is a
+// device buffer of at least ceil(bytes / bytes_per_group) words that is
+// practically never written.  Returns 0, or a HIP error code (nothing is
+// launched when the arguments are refused: 1 = invalid argument).
+extern "C" int uaii_probe_stream_read(const void* src, size_t bytes, size_t bytes_per_group,
+                                      uint32_t* sink, void* stream) {
+  if (src == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0 || bytes_per_group == 0 ||
+      bytes_per_group % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0)
+    return 1;
+  const size_t n = bytes / 16;
+  const size_t per = bytes_per_group / 16;
+  const size_t groups = (n + per - 1) / per;
+  if (groups > 0x7FFFFFFFu) return 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), n, per, sink);
+  return static_cast<int>(hipGetLastError());
+}
