@@ -322,3 +322,108 @@ def test_prefill_refusals_write_nothing():
                        0, 0.0, None, st.out.data_ptr(), st.stream())
     torch.cuda.synchronize()
     assert torch.equal(before, st.out)
+
+
+def scale_key_scales(factor):
+    """prep for int8 keys (q8): multiply the per-token key scale of cached
+    row lo + j by factor(j, n)."""
+    def prep(inputs):
+        w = inputs.workload
+        assert w.k_dtype == W.I8
+        for b in range(w.batch):
+            first = int(inputs.start[b])
+            lo, _ = w.visible(first + 1)
+            n = first - lo
+            if n > 0:
+                inputs.k_scale[b, :, lo:first] *= factor(np.arange(n, dtype=np.float32), n)[None, :]
+    return prep
+
+
+def then(*preps):
+    def prep(inputs):
+        for p in preps:
+            p(inputs)
+    return prep
+
+
+def huge_values(where, size=3e5):
+    """prep: cached bf16 value rows lo + j for j in where(n) multiplied by
+    `size` (beyond f16's range: the values must go through the product as
+    stored)."""
+    def prep(inputs):
+        w = inputs.workload
+        assert w.v_dtype == W.BF16
+        for b in range(w.batch):
+            first = int(inputs.start[b])
+            lo, _ = w.visible(first + 1)
+            n = first - lo
+            if n <= 0:
+                continue
+            rows = lo + np.asarray(where(n), dtype=np.int64)
+            f = (inputs.cache_v[b][:, rows].astype(np.uint32) << 16).view(np.float32) * np.float32(size)
+            inputs.cache_v[b][:, rows] = (f.view(np.uint32) >> 16).astype(np.uint16)
+    return prep
+
+
+# Scores far beyond the moving-reference cases: keys scaled up along the
+# cache so that the largest scores reach 430 to 670 log2 units (one lone
+# spike key at 1070).  q enters the score product as a bf16 pair (about
+# 2^-17 of q left out), an error in the score that grows with the score:
+# about 1e-3 in the output near 600 log2 units (415 in natural units), and
+# the 2e-3 bound is reached near 700 in a batch of 32 ragged items.  These
+# cases hold the path to the bound up to that limit.
+LARGE = [
+    (case("scores-500-d128-g4", 128, 4, 2, 64, [700, 400], seed=41),
+     scale_cached_keys(lambda j, n: 1.0 + 150.0 * j / n)),
+    (case("scores-500-d64-g8-two-blocks", 64, 8, 8, 40,
+          np.random.default_rng(42).integers(300, 601, 32), seed=42),
+     scale_cached_keys(lambda j, n: 1.0 + 100.0 * j / n)),
+    (case("scores-500-d256-g2-sink-window", 256, 2, 2, 50, [600, 300], window=400, sink=True,
+          seed=43), scale_cached_keys(lambda j, n: 1.0 + 120.0 * j / n)),
+    (case("scores-500-vq8-d128-g4", 128, 4, 2, 48, [640], seed=44, kv=VQ8),
+     scale_cached_keys(lambda j, n: 1.0 + 150.0 * j / n)),
+    (case("scores-500-q8-d128-g4", 128, 4, 2, 48, [640, 200], seed=45, kv=Q8),
+     scale_key_scales(lambda j, n: 1.0 + 150.0 * j / n)),
+    (case("scores-500-spike-paged", 128, 4, 2, 64, [500, 300], seed=46, bs=16),
+     scale_cached_keys(lambda j, n: np.where(j == n // 3, 400.0, 1.0).astype(np.float32))),
+    # Values beyond f16's range in low-weight rows (the first cached rows,
+    # under ramped keys): they must neither overflow nor leak into the
+    # output.
+    (case("huge-values-low-weight-d128", 128, 4, 2, 64, [700, 400], seed=47),
+     then(scale_cached_keys(lambda j, n: 1.0 + 20.0 * j / n),
+          huge_values(lambda n: np.arange(0, min(n, 40), 3)))),
+    (case("huge-values-low-weight-d64-two-blocks", 64, 4, 8, 72,
+          np.random.default_rng(48).integers(300, 501, 32), seed=48),
+     then(scale_cached_keys(lambda j, n: 1.0 + 20.0 * j / n),
+          huge_values(lambda n: [0, 5, 33]))),
+]
+
+
+@pytest.mark.parametrize("spec", LARGE, ids=[c[0][0].name for c in LARGE])
+def test_prefill_large_scores(spec):
+    (w, lens, bs), prep = spec
+    run_small(w, lens, bs, prep=prep)
+
+
+def test_prefill_huge_values_with_weight():
+    """Values of 1e5 and more in the rows that dominate the softmax: the
+    output is of their size, and is checked relative to the largest visible
+    value (f32 accumulation of bf16-split weights)."""
+    w, lens, bs = case("huge-values-dominant", 128, 4, 2, 64, [600, 300], seed=49)
+    prep = then(scale_cached_keys(lambda j, n: 1.0 + 3.0 * j / n),
+                huge_values(lambda n: np.arange(n - 48, n)))
+    inputs = W.make_prefill_inputs(w, seq_lens=lens)
+    prep(inputs)
+    st = run_gpu(inputs)
+    o, q, ck, cv, vs, ks = oracle_side(inputs)
+    want = o.prefill(q=q, cache_k=ck, cache_v=cv, v_scale=vs, k_scale=ks, k_dtype=w.k_dtype,
+                     v_dtype=w.v_dtype, seq_lens=lens, window=w.window, softcap=w.softcap,
+                     sinks=inputs.sinks)
+    out = st.out.cpu().numpy()
+    vmax = float(np.max(np.abs((cv.astype(np.uint32) << 16).view(np.float32)[np.isfinite(
+        (cv.astype(np.uint32) << 16).view(np.float32))])))
+    err = float(np.max(np.abs(out - want)))
+    P.say(f"  max |out| {np.max(np.abs(want)):.3g}, max |v| {vmax:.3g}, max abs err {err:.3g} "
+          f"({err / vmax:.3g} of max |v|)")
+    assert vmax > 65520.0 and np.max(np.abs(want)) > 1e4
+    assert np.all(np.isfinite(out)) and err <= 1e-5 * vmax, err
