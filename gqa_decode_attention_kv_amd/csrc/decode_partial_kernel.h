@@ -182,6 +182,52 @@ struct Elem {
   static constexpr int key_load() { return (DT == kI8 && G >= 8) ? 8 : 16; }
 };
 
+// ---- key pass on the matrix cores ----------------------------------------
+// bf16 and int8 keys of groups of at most four heads are scored 16 keys at a
+// time, one MFMA per 32 dims (bf16) or 64 dims (int8).  The A operand holds
+// the query group, row 4 h + t being term t of head h; the B operand is the
+// 16 key rows exactly as loaded (lane l: key l % 16, the 16 bytes at
+// 16 (l / 16) + 64 s of its row for step s, dims taken in that order on both
+// sides); lane l of the 16 x 16 result holds rows 4 (l / 16) + i of key
+// l % 16, the terms of one head, which the lane adds.  Keys are never
+// widened, and the cross-lane reduction of the vector pass disappears.
+//   * bf16 keys: q (f32) is cut into three bf16 terms whose sum is exactly q
+//     (truncation leaves the low 16, then 8 significand bits), so every
+//     product is exact and the sum runs in the f32 accumulator.
+//   * int8 keys: q / sigma (sigma a power of two per head, |q / sigma| < 64)
+//     is written as four base-128 int8 digits and multiplied by the codes
+//     in exact i32 arithmetic; the digits leave out at most 2^-22 sigma of
+//     each q.
+template <int G, int KT, int VT>
+constexpr bool key_mfma() { return G <= 4 && VT == kI8 && (KT == kBF16 || KT == kI8); }
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Term t (0, 1, 2) of x as bf16 bits: term 0 + term 1 + term 2 == x exactly.
+__device__ inline uint32_t bf16_term(float x, int t) {
+  const uint32_t u = __float_as_uint(x);
+  const float r1 = x - __uint_as_float(u & 0xFFFF0000u);  // the low 16 significand bits, exact
+  const uint32_t u1 = __float_as_uint(r1);
+  const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);  // at most 8 significant bits, exact
+  return (t == 0 ? u : (t == 1 ? u1 : __float_as_uint(r2))) >> 16;
+}
+
+// Digit t (0..3) of y, |y| < 64, in base 128 with nearest-integer digits:
+// y = d0 + d1 / 128 + d2 / 128^2 + d3 / 128^3 + e with |e| <= 2^-22 and every
+// |d| <= 64.  Each step is exact in f32.
+__device__ inline int i8_digit(float y, int t) {
+  float d[4];
+  d[0] = rintf(y);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    y = (y - d[i - 1]) * 128.0f;
+    d[i] = rintf(y);
+  }
+  return static_cast<int>(t == 0 ? d[0] : (t == 1 ? d[1] : (t == 2 ? d[2] : d[3])));
+}
+
 // Kernel arguments: the partials alone, or the fused step (partials plus
 // the producer's inputs, the sinks, the output and the arrival counters).
 template <bool FUSED>
@@ -222,11 +268,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_wa
 decode_partial_kernel(const KernelArgs<FUSED> args) {
   const AttnArgs& a = attn_of(args);
   const StepArgs* x = step_of(args);
+  // Matrix key pass (key_mfma): a K tile is 16 rows, each lane loading KNL
+  // 16-byte segments of one row; otherwise a tile is one wave load.
+  constexpr bool KMF = key_mfma<G, KT, VT>();
   constexpr int KB = Elem<KT>::bytes, VB = Elem<VT>::bytes;
-  constexpr int KLB = Elem<KT>::template key_load<G>(), VLB = Elem<VT>::value_load;
-  constexpr int KLPR = D * KB / KLB;  // lanes per K row
-  constexpr int KRPL = 64 / KLPR;     // K rows per wave load
-  constexpr int KE = KLB / KB;        // K elements per lane
+  constexpr int KLB = KMF ? 16 : Elem<KT>::template key_load<G>(), VLB = Elem<VT>::value_load;
+  constexpr int KLPR = KMF ? 4 : D * KB / KLB;  // lanes per K row
+  constexpr int KRPL = 64 / KLPR;               // K rows per tile
+  constexpr int KNL = KMF ? D * KB / 64 : 1;    // loads per lane per K tile
+  constexpr int KE = KLB / KB;                  // K elements per lane and load
+  constexpr int KRB = D * KB;                   // bytes per key row
+  constexpr int KSPR = KRB / 16;                // 16-byte segments per key row
+  constexpr int KRPI = KRB <= 1024 ? 1024 / KRB : 1;  // key rows per 1 KB wave load
   constexpr int VLPR = D * VB / VLB;
   constexpr int VRPL = 64 / VLPR;
   constexpr int VE = VLB / VB;
@@ -236,7 +289,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   // tiles each carry their own block's base (more waves per SIMD instead).
   constexpr int LF = (G >= 8 || PAGED) ? kLoadsInFlight / 2 : kLoadsInFlight;
   constexpr int LFK = LF * 16 / KLB, LFV = LF * 16 / VLB;
-  constexpr int UK = (LFK * KRPL <= kRowsPerChunk) ? LFK : kRowsPerChunk / KRPL;
+  constexpr int LFKT = (LFK / KNL > 0) ? LFK / KNL : 1;  // K tiles in flight
+  constexpr int UK = (LFKT * KRPL <= kRowsPerChunk) ? LFKT : kRowsPerChunk / KRPL;
   constexpr int UV = (LFV * VRPL <= kRowsPerChunk) ? LFV : kRowsPerChunk / VRPL;
   // Paged caches align tiles to blocks, so a chunk's rows sit up to 15 rows
   // after the start of its LDS window.
@@ -247,6 +301,9 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   static_assert(KLPR >= 4 && VLPR >= 4, "row must span at least a quad");
 
   __shared__ __attribute__((aligned(16))) float smem[kWaves * kLdsRows * G];
+  // Matrix key pass: per wave, one 16-row key tile staged between the
+  // coalesced loads and the operand reads.
+  __shared__ __attribute__((aligned(16))) uint32_t kstage[KMF ? kWaves * 4 * KRB : 4];  // 16 KRB bytes per wave
   // Fused step: per-wave staging of one head vector in double precision.
   __shared__ double sxd[FUSED ? kWaves * D : 1];
   static_assert(!FUSED || kLdsRows * G >= (G + 1) * D, "query and value staging must fit a wave's LDS");
@@ -339,11 +396,73 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   const float* sbase = (VT == kI8) ? a.v_scale + slab : nullptr;
   const float* ksbase = (KT == kI8) ? a.k_scale + slab : nullptr;
 
-  // Query group in registers: lane holds q[h][kc*KE .. kc*KE + KE) for its K segment.
-  const int kr = lane / KLPR, kc = lane % KLPR;
+  // Vector key pass: the query group in registers, lane holding
+  // q[h][kc*KE .. kc*KE + KE) for its K segment.  Matrix key pass: lane
+  // loads segment kc of key row kr of each tile, and qa is the A operand.
+  const int kr = KMF ? (lane & 15) : lane / KLPR, kc = KMF ? (lane >> 4) : lane % KLPR;
   const int vr = lane / VLPR, vc = lane % VLPR;
   float* sc = smem + wave * (kLdsRows * G);  // this wave's [row][G] scores / weights
-  float q[G][KE];
+  float q[KMF ? 1 : G][KMF ? 1 : KE];
+  using AOp = typename std::conditional<KT == kI8, i32x4, bf16x8>::type;
+  AOp qa[KNL];
+  float qsig = 1.0f;  // int8 keys: sigma of this lane's output head (kc)
+  // A operand from the G query rows at qsrc (row h at qsrc + h D, scaled by
+  // q_mul here): lane (m, kc), m = lane % 16, holds term / digit m % 4 of
+  // head m / 4 (zero past the group, and for bf16 row 4 h + 3), dims
+  // 32 s + 8 kc + j (bf16) or 64 s + 16 kc + j (int8) for step s.
+  auto build_qa = [&](const float* qsrc) {
+    const int m = lane & 15, t = m & 3;
+    const bool live = (m >> 2) < G && (KT == kI8 || t < 3);
+    const float* qh = qsrc + min(m >> 2, G - 1) * D;
+    constexpr int SD = KT == kI8 ? 16 : 8;  // dims per lane and step
+    float x[KNL][SD];
+#pragma unroll
+    for (int st = 0; st < KNL; ++st)
+#pragma unroll
+      for (int j = 0; j < SD; j += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(qh + 4 * SD * st + SD * kc + j);
+        x[st][j] = v.x * a.q_mul;
+        x[st][j + 1] = v.y * a.q_mul;
+        x[st][j + 2] = v.z * a.q_mul;
+        x[st][j + 3] = v.w * a.q_mul;
+      }
+    if constexpr (KT == kI8) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int st = 0; st < KNL; ++st)
+#pragma unroll
+        for (int j = 0; j < SD; ++j) mx = fmaxf(mx, fabsf(x[st][j]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));  // max |q| of head m / 4
+      const int ex = mx > 0.0f ? ilogbf(mx) - 5 : 0;  // |q| / 2^ex < 64
+#pragma unroll
+      for (int st = 0; st < KNL; ++st) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int dg = live ? i8_digit(ldexpf(x[st][4 * j + k], -ex), t) : 0;
+            word |= (static_cast<uint32_t>(dg) & 0xFFu) << (8 * k);
+          }
+          w[j] = word;
+        }
+        qa[st] = i32x4{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1]), static_cast<int32_t>(w[2]),
+                       static_cast<int32_t>(w[3])};
+      }
+      qsig = __shfl(ldexpf(1.0f, ex), 4 * min(kc, G - 1));
+    } else {
+#pragma unroll
+      for (int st = 0; st < KNL; ++st) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[j] = live ? (bf16_term(x[st][2 * j], t) | (bf16_term(x[st][2 * j + 1], t) << 16)) : 0u;
+        qa[st] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  };
   float s_new[G];  // fused step: raw scores of the new token's row
   float vnew[VE];  // fused step: its stored value, this lane's V segment
   if constexpr (FUSED) {
@@ -376,10 +495,14 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       }
     }
     pm::wave_sync();
+    if constexpr (KMF) {
+      build_qa(qs);
+    } else {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < KE; ++e) q[g][e] = qs[g * D + kc * KE + e] * a.q_mul;
+        for (int e = 0; e < KE; ++e) q[g][e] = qs[g * D + kc * KE + e] * a.q_mul;
+    }
     if (new_here) {
       const int64_t krow = static_cast<int64_t>(b) * a.Hkv + kvh;
       float kin[EPL], vin[EPL];
@@ -413,6 +536,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       for (int e = 0; e < VE; ++e) vnew[e] = vs[vc * VE + e];
     }
     pm::wave_sync();  // the staging area is the K pass's score buffer
+  } else if constexpr (KMF) {
+    build_qa(a.q + (static_cast<int64_t>(b) * a.H + kvh * G) * D);
   } else {
     const float* qb = a.q + (static_cast<int64_t>(b) * a.H + kvh * G) * D + kc * KE;
 #pragma unroll
@@ -429,18 +554,21 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   }
   (void)s_new;
   (void)vnew;
-  // q8 keys: each raw score carries 128 * sum(q_h) from the code offset.
+  (void)q;
+  (void)qsig;
+  // q8 keys in the vector pass: each raw score carries 128 * sum(q_h) from
+  // the code offset (the matrix pass multiplies the signed codes).
   float c128[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float t = 0.0f;
-    if constexpr (KT == kI8) {
+    if constexpr (KT == kI8 && !KMF) {
 #pragma unroll
       for (int e = 0; e < KE; ++e) t += q[g][e];
     }
     c128[g] = t;
   }
-  if constexpr (KT == kI8) {
+  if constexpr (KT == kI8 && !KMF) {
     group_sum_n<KLPR, G>(c128);
 #pragma unroll
     for (int g = 0; g < G; ++g) c128[g] *= 128.0f;
@@ -543,43 +671,118 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
     // tile has been widened.  The steady-state loop has no branches (every
     // tile and every reload is in range) so the compiler can count loads in
     // flight exactly; the last one or two batches run in a guarded tail.
-    vec_t<KLB> kd[UK];
-    auto k_scores = [&](const float (&kf)[KE], int r) {
-      float s[G];
+    if constexpr (KMF) {
+      // Matrix pass.  A tile of 16 rows is read as KNL wave loads of 1 KB
+      // each (KRPI whole rows, fully coalesced: measured 15% faster than
+      // loads that take 64 bytes of each of the 16 rows), staged in LDS
+      // slot = lane, and read back in the operand layout (lane: row kr,
+      // segment 4 st + kc for step st).  Within a row the segments are
+      // permuted (XOR with a function of the row) so that those reads hit
+      // distinct banks.  Each load is reissued for the tile UK ahead as soon
+      // as it is staged.
+      using COp = typename std::conditional<KT == kI8, i32x4, f32x4>::type;
+      auto kswz = [](int rr) { return (rr ^ (rr >> (KRB == 64 ? 2 : 3))) & (KSPR - 1); };
+      auto kaddr_mf = [&](int t, int st) -> const char* {
+        const int rr = KRPI * st + lane / KSPR;  // row of the tile this lane loads
+        const int seg = (lane % KSPR) ^ kswz(rr);
+        if constexpr (PAGED) {
+          const int R = TK0 + t * KRPL;
+          const int row = min(max(R + rr, a0), last);
+          return tile_base(a.k, R, KRB) + static_cast<uint32_t>((row - R) * KRB + 16 * seg);
+        } else {
+          return kblk + static_cast<uint32_t>(xrow(min(t * KRPL + rr, nrows - 1)) * KRB + 16 * seg);
+        }
+      };
+      u32x4* stg = reinterpret_cast<u32x4*>(kstage) + wave * KRB;
+      u32x4 kd[UK][KNL];
+      auto k_tile = [&](int u, int t_next, bool reload, int r) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float p = q[g][0] * kf[0];
+        for (int st = 0; st < KNL; ++st) {
+          stg[64 * st + lane] = kd[u][st];
+          if (reload) kd[u][st] = load_nt<16>(kaddr_mf(t_next, st));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        COp c = {0, 0, 0, 0};
 #pragma unroll
-        for (int e = 1; e < KE; ++e) p = fmaf(q[g][e], kf[e], p);
-        s[g] = p;
+        for (int st = 0; st < KNL; ++st) {
+          const int seg = 4 * st + kc;
+          const u32x4 kb = stg[64 * (kr / KRPI) + (kr % KRPI) * KSPR + (seg ^ kswz(kr))];
+          if constexpr (KT == kI8) {
+            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[st], __builtin_bit_cast(i32x4, kb), c, 0, 0, 0);
+          } else {
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], __builtin_bit_cast(bf16x8, kb), c, 0, 0, 0);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float sv;
+        if constexpr (KT == kI8) {
+          constexpr float k7 = 1.0f / 128.0f;
+          sv = fmaf(fmaf(fmaf(static_cast<float>(c[3]), k7, static_cast<float>(c[2])), k7, static_cast<float>(c[1])),
+                    k7, static_cast<float>(c[0])) *
+               qsig;
+        } else {
+          sv = (c[0] + c[1]) + c[2];
+        }
+        if (kc < G) sc[r * G + kc] = sv;
+      };
+#pragma unroll
+      for (int u = 0; u < UK; ++u)
+#pragma unroll
+        for (int st = 0; st < KNL; ++st) kd[u][st] = load_nt<16>(kaddr_mf(min(u, nk - 1), st));
+      const int kx0 = TK0 - A + kr;  // LDS row of tile 0 for this lane's output key
+      int t0 = 0;
+      for (; t0 + 2 * UK <= nk; t0 += UK) {
+#pragma unroll
+        for (int u = 0; u < UK; ++u) k_tile(u, t0 + UK + u, true, kx0 + (t0 + u) * KRPL);
       }
-      group_sum_n<KLPR, G>(s);
-      if (kc == 0) {
+      for (; t0 < nk; t0 += UK) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) sc[r * G + g] = s[g];
+        for (int u = 0; u < UK; ++u)
+          if (t0 + u < nk) k_tile(u, t0 + UK + u, t0 + UK + u < nk, kx0 + (t0 + u) * KRPL);
       }
-    };
+    } else {
+      vec_t<KLB> kd[UK];
+      auto k_scores = [&](const float (&kf)[KE], int r) {
+        float s[G];
 #pragma unroll
-    for (int u = 0; u < UK; ++u) kd[u] = load_nt<KLB>(kaddr(min(u, nk - 1)));
-    const int kx0 = TK0 - A + kr;  // LDS row of tile 0 for this lane
-    int t0 = 0;
-    for (; t0 + 2 * UK <= nk; t0 += UK) {
+        for (int g = 0; g < G; ++g) {
+          float p = q[g][0] * kf[0];
 #pragma unroll
-      for (int u = 0; u < UK; ++u) {
-        float kf[KE];
-        widen<KT, KE>(kd[u], kf);
-        kd[u] = load_nt<KLB>(kaddr(t0 + UK + u));
-        k_scores(kf, kx0 + (t0 + u) * KRPL);
-      }
-    }
-    for (; t0 < nk; t0 += UK) {
+          for (int e = 1; e < KE; ++e) p = fmaf(q[g][e], kf[e], p);
+          s[g] = p;
+        }
+        group_sum_n<KLPR, G>(s);
+        if (kc == 0) {
 #pragma unroll
-      for (int u = 0; u < UK; ++u) {
-        if (t0 + u < nk) {
+          for (int g = 0; g < G; ++g) sc[r * G + g] = s[g];
+        }
+      };
+#pragma unroll
+      for (int u = 0; u < UK; ++u) kd[u] = load_nt<KLB>(kaddr(min(u, nk - 1)));
+      const int kx0 = TK0 - A + kr;  // LDS row of tile 0 for this lane
+      int t0 = 0;
+      for (; t0 + 2 * UK <= nk; t0 += UK) {
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
           float kf[KE];
           widen<KT, KE>(kd[u], kf);
-          if (t0 + UK + u < nk) kd[u] = load_nt<KLB>(kaddr(t0 + UK + u));
+          kd[u] = load_nt<KLB>(kaddr(t0 + UK + u));
           k_scores(kf, kx0 + (t0 + u) * KRPL);
+        }
+      }
+      for (; t0 < nk; t0 += UK) {
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          if (t0 + u < nk) {
+            float kf[KE];
+            widen<KT, KE>(kd[u], kf);
+            if (t0 + UK + u < nk) kd[u] = load_nt<KLB>(kaddr(t0 + UK + u));
+            k_scores(kf, kx0 + (t0 + u) * KRPL);
+          }
         }
       }
     }
@@ -667,7 +870,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       }
     };
     const int vx0 = TV0 - A + vr;  // LDS row of tile 0 for this lane
-    t0 = 0;
+    int t0 = 0;
     for (; t0 + 2 * UV <= nv; t0 += UV) {
 #pragma unroll
       for (int u = 0; u < UV; ++u) {
