@@ -201,6 +201,10 @@ struct Elem {
 template <int G, int KT, int VT>
 constexpr bool key_mfma() { return G <= 4 && VT == kI8 && (KT == kBF16 || KT == kI8); }
 
+// The value pass on the matrix cores (int8 values, G of 2 or 4, d <= 128).
+template <int D, int G, int KT, int VT>
+constexpr bool value_mfma() { return key_mfma<G, KT, VT>() && (G == 2 || G == 4) && D <= 128; }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -256,15 +260,17 @@ __device__ inline const StepArgs* step_of(const StepArgs& s) { return &s; }
 // amdgpu_waves_per_eu(2, 8): at least two waves per SIMD.  Without the hint
 // the allocator spends registers freely (the vq8 kernel spilled into AGPRs at
 // one wave per SIMD); with it the bf16 d128 kernel fits three waves per SIMD.
-// The paged d128 partial kernels (G <= 4, bf16 or f32 keys) are held to
-// three waves per SIMD too: with half as many loads in flight (below) they
-// fit without spilling, where the per-tile block lookups otherwise leave room
-// for two.
-template <int D, int G, int KT, bool PAGED, bool FUSED>
-constexpr int min_waves() { return (PAGED && !FUSED && D == 128 && G <= 4 && KT != kI8) ? 3 : 2; }
+// The paged d128 partial kernels (G <= 4, bf16 or f32 keys, values not on
+// the matrix cores) are held to three waves per SIMD too: with half as many
+// loads in flight (below) they fit without spilling, where the per-tile
+// block lookups otherwise leave room for two.
+template <int D, int G, int KT, int VT, bool PAGED, bool FUSED>
+constexpr int min_waves() {
+  return (PAGED && !FUSED && D == 128 && G <= 4 && KT != kI8 && !value_mfma<D, G, KT, VT>()) ? 3 : 2;
+}
 
 template <int D, int G, int KT, int VT, bool PAGED, bool FUSED, bool ILV>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves<D, G, KT, PAGED, FUSED>(), 8))) void
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves<D, G, KT, VT, PAGED, FUSED>(), 8))) void
 decode_partial_kernel(const KernelArgs<FUSED> args) {
   const AttnArgs& a = attn_of(args);
   const StepArgs* x = step_of(args);
@@ -294,7 +300,17 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   constexpr int UV = (LFV * VRPL <= kRowsPerChunk) ? LFV : kRowsPerChunk / VRPL;
   // Paged caches align tiles to blocks, so a chunk's rows sit up to 15 rows
   // after the start of its LDS window.
-  constexpr int kLdsRows = kRowsPerChunk + (PAGED ? 16 : 0);
+  // Matrix value pass (int8 values, G of 2 or 4, d <= 128): blocks of 64
+  // keys, staged like the key tiles and read back transposed.
+  constexpr bool VMF = value_mfma<D, G, KT, VT>();
+  constexpr int VBK = 64;                        // keys per value block
+  constexpr int VRPI = 1024 / (D * VB);          // value rows per 1 KB wave load
+  constexpr int VNL = VMF ? VBK / VRPI : 1;      // loads per lane per value block
+  constexpr int NT = D / 16;                     // 16-dim output tiles
+  // Paged chunks align their value blocks to 16 rows, up to 63 rows before
+  // the chunk.
+  constexpr int kLdsRows = kRowsPerChunk + (PAGED ? (VMF ? 64 : 16) : 0);
+  constexpr int kStageBytes = (VMF && VBK * D * VB > 16 * KRB) ? VBK * D * VB : 16 * KRB;
   constexpr int kScaleRegs = (VT == kI8) ? (kLdsRows + 63) / 64 : 1;
   constexpr int kKScaleRegs = (KT == kI8) ? (kLdsRows + 63) / 64 : 1;
   static_assert(kRowsPerChunk % (UK * KRPL) == 0 && kRowsPerChunk % (UV * VRPL) == 0, "tiling");
@@ -303,7 +319,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   __shared__ __attribute__((aligned(16))) float smem[kWaves * kLdsRows * G];
   // Matrix key pass: per wave, one 16-row key tile staged between the
   // coalesced loads and the operand reads.
-  __shared__ __attribute__((aligned(16))) uint32_t kstage[KMF ? kWaves * 4 * KRB : 4];  // 16 KRB bytes per wave
+  __shared__ __attribute__((aligned(16))) uint32_t kstage[KMF ? kWaves * kStageBytes / 4 : 4];
   // Fused step: per-wave staging of one head vector in double precision.
   __shared__ double sxd[FUSED ? kWaves * D : 1];
   static_assert(!FUSED || kLdsRows * G >= (G + 1) * D, "query and value staging must fit a wave's LDS");
@@ -465,6 +481,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   };
   float s_new[G];  // fused step: raw scores of the new token's row
   float vnew[VE];  // fused step: its stored value, this lane's V segment
+  float vnewm[NT];  // fused step, matrix value pass: dims 16 t + lane % 16
   if constexpr (FUSED) {
     const ProduceArgs& p = x->p;
     constexpr int EPL = pm::Shape<D>::EPL, NP = pm::Shape<D>::NP;
@@ -534,6 +551,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       pm::wave_sync();
 #pragma unroll
       for (int e = 0; e < VE; ++e) vnew[e] = vs[vc * VE + e];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) vnewm[t] = vs[16 * t + (lane & 15)];
     }
     pm::wave_sync();  // the staging area is the K pass's score buffer
   } else if constexpr (KMF) {
@@ -554,6 +573,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   }
   (void)s_new;
   (void)vnew;
+  (void)vnewm;
   (void)q;
   (void)qsig;
   // q8 keys in the vector pass: each raw score carries 128 * sum(q_h) from
@@ -576,11 +596,19 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   const bool capped = a.softcap > 0.0f;
   const float cap_c = a.softcap, cap_inv = capped ? 1.0f / a.softcap : 0.0f;
 
-  float acc[G][VE];
+  // Vector value pass: acc[g][e] of this lane's value segment.  Matrix
+  // value pass: vacc[T] = head kc, dim 16 T + lane % 16, complete (no
+  // reduction across lanes), and vsig the chunk's digit scale.
+  float acc[VMF ? 1 : G][VMF ? 1 : VE];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int g = 0; g < (VMF ? 1 : G); ++g)
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
+    for (int e = 0; e < (VMF ? 1 : VE); ++e) acc[g][e] = 0.0f;
+  float vacc[VMF ? NT : 1];
+#pragma unroll
+  for (int t = 0; t < (VMF ? NT : 1); ++t) vacc[t] = 0.0f;
+  (void)acc;
+  (void)vacc;
   float m_run[G], l_run[G];
   float psum[G];  // int8 values: sum of the scaled weights this lane wrote (removes the +128)
 #pragma unroll
@@ -602,9 +630,10 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
     const int last = a0 + nrows - 1;
     const int A = PAGED ? (a0 & ~15) : a0;
     const int TK0 = PAGED ? (a0 & ~(KRPL - 1)) : a0;
-    const int TV0 = PAGED ? (a0 & ~(VRPL - 1)) : a0;
+    const int TV0 = VMF ? A : (PAGED ? (a0 & ~(VRPL - 1)) : a0);
     const int nk = (a0 + nrows - TK0 + KRPL - 1) / KRPL;  // K tiles of KRPL rows
-    const int nv = (a0 + nrows - TV0 + VRPL - 1) / VRPL;  // V tiles of VRPL rows
+    constexpr int VTR = VMF ? VBK : VRPL;                   // rows per V tile
+    const int nv = (a0 + nrows - TV0 + VTR - 1) / VTR;      // V tiles (matrix pass: blocks)
     const char* kblk = kbase + static_cast<int64_t>(chunk_row(a0)) * (D * KB);
     const char* vblk = vbase + static_cast<int64_t>(chunk_row(a0)) * (D * VB);
     // Paged: lane j holds the physical id of logical block j0 + j (a chunk
@@ -693,7 +722,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
           return kblk + static_cast<uint32_t>(xrow(min(t * KRPL + rr, nrows - 1)) * KRB + 16 * seg);
         }
       };
-      u32x4* stg = reinterpret_cast<u32x4*>(kstage) + wave * KRB;
+      u32x4* stg = reinterpret_cast<u32x4*>(kstage) + wave * (kStageBytes / 16);
       u32x4 kd[UK][KNL];
       auto k_tile = [&](int u, int t_next, bool reload, int r) {
 #pragma unroll
@@ -787,9 +816,33 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       }
     }
     // First value tiles are in flight while the weights are computed.
-    vec_t<VLB> vd[UV];
+    // Matrix value pass: load st of block t brings rows VRPI st + lane / CB
+    // of the block, 16-byte column block lane % CB (1 KB per wave load).
+    constexpr int CB = D * VB / 16;
+    auto vaddr_mf = [&](int t, int st) -> const char* {
+      const int rr = VRPI * st + lane / CB;
+      const int col = 16 * (lane % CB);
+      if constexpr (PAGED) {
+        // A load's VRPI rows lie in one 16-row group, hence in one block; a
+        // load wholly past the chunk reads its last row.
+        const int R = min(TV0 + t * VBK + VRPI * st, last);
+        const int row = min(max(R + lane / CB, a0), last);
+        return tile_base(a.v, R, D * VB) + static_cast<uint32_t>((row - R) * (D * VB) + col);
+      } else {
+        return vblk + static_cast<uint32_t>(xrow(min(t * VBK + rr, nrows - 1)) * (D * VB) + col);
+      }
+    };
+    vec_t<VLB> vd[VMF ? 1 : UV];
+    u32x4 vdm[VMF ? VNL : 1];
+    if constexpr (VMF) {
 #pragma unroll
-    for (int u = 0; u < UV; ++u) vd[u] = load_nt<VLB>(vaddr(min(u, nv - 1)));
+      for (int st = 0; st < VNL; ++st) vdm[st] = load_nt<16>(vaddr_mf(0, st));
+    } else {
+#pragma unroll
+      for (int u = 0; u < UV; ++u) vd[u] = load_nt<VLB>(vaddr(min(u, nv - 1)));
+    }
+    (void)vd;
+    (void)vdm;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -827,15 +880,35 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       const float m_new = fmaxf(m_run[g], capped_log2(m_chunk, capped, cap_c, cap_inv));
       const float alpha = (m_run[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
       l_run[g] *= alpha;
+      if constexpr (VMF) {
+        if (kc == g) {
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
+          for (int t = 0; t < NT; ++t) vacc[t] *= alpha;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
+      }
       psum[g] *= alpha;
       m_run[g] = m_new;
     }
 
+    // Matrix value pass: the weights p * vscale of the chunk are written as
+    // four base-128 int8 digits of p * vscale / vsig, vsig = 2^vex a power of
+    // two with max(vscale) / vsig in [32, 64) (p <= 1), packed one word per
+    // head (digit t in byte t).
+    int vex = 0;
+    if constexpr (VMF) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kScaleRegs; ++i) mx = fmaxf(mx, sreg[i]);
+      mx = wave_max(mx);
+      vex = mx > 0.0f ? ilogbf(mx) - 5 : 0;
+    }
+
     // ---- weights p = 2^(s - m) for every row the value tiles cover (0 past
     // the end); vq8 folds the token's scale into p ---------------------------
-    const int xend = TV0 - A + nv * VRPL;  // LDS rows the value tiles read
+    const int xend = TV0 - A + nv * VTR;  // LDS rows the value tiles read
 #pragma unroll
     for (int i = 0; i < (kLdsRows + 63) / 64; ++i) {
       const int r = lane + 64 * i;
@@ -849,8 +922,16 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
               ok ? __builtin_amdgcn_exp2f(capped_log2(sc[r * G + g], capped, cap_c, cap_inv) - m_run[g]) : 0.0f;
           l_run[g] += p;
           const float pv = p * vs;
-          sc[r * G + g] = pv;
-          if constexpr (VT == kI8) psum[g] += pv;
+          if constexpr (VMF) {
+            const float y = ldexpf(pv, -vex);
+            uint32_t word = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) word |= (static_cast<uint32_t>(i8_digit(y, t)) & 0xFFu) << (8 * t);
+            reinterpret_cast<uint32_t*>(sc)[r * G + g] = word;
+          } else {
+            sc[r * G + g] = pv;
+            if constexpr (VT == kI8) psum[g] += pv;
+          }
         }
       }
     }
@@ -858,36 +939,98 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- pass 2: weighted sum of values (rolling prefetch of UV tiles) ------
-    auto v_accum = [&](const float (&vf)[VE], int r) {
-      float p[G];
+    if constexpr (VMF) {
+      // ---- pass 2 on the matrix cores: per 64-key block, O += P V with the
+      // weights' digits as the A operand (row 4 h + t: digit t of head h)
+      // and the codes as the B operand.  The block is staged in LDS (rows
+      // of D bytes, 16-byte column blocks permuted within a row so that the
+      // transposing reads below hit distinct banks); gfx950's transposing
+      // 8-bit LDS read gives lane (q, n) dim n of 8 keys at a time, and the
+      // same read over the digit rows (4 G bytes per key) gives the A
+      // operand.  Each load is reissued for the next block once staged.
+      // The i32 products are exact; the chunk's digit rows are combined
+      // into vacc at the end of the chunk.
+      typedef int32_t v2i32 __attribute__((ext_vector_type(2)));
+      typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+      auto vswz = [](int rr) { return ((rr >> (D == 64 ? 2 : 1)) ^ ((rr >> 4) << (D == 64 ? 1 : 2))) & (CB - 1); };
+      char* vst = reinterpret_cast<char*>(kstage) + wave * kStageBytes;
+      const char* dig = reinterpret_cast<const char*>(sc);
+      const int s16 = lane & 15, qg = lane >> 4;
+      i32x4 cacc[NT];
 #pragma unroll
-      for (int g = 0; g < G; ++g) p[g] = sc[r * G + g];
+      for (int t = 0; t < NT; ++t) cacc[t] = i32x4{0, 0, 0, 0};
+      for (int t = 0; t < nv; ++t) {
+        const bool more = t + 1 < nv;  // wave-uniform
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+        for (int st = 0; st < VNL; ++st) {
+          const int rr = VRPI * st + lane / CB;
+          *reinterpret_cast<u32x4*>(vst + rr * (D * VB) + 16 * ((lane % CB) ^ vswz(rr))) = vdm[st];
+          if (more) vdm[st] = load_nt<16>(vaddr_mf(t + 1, st));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // A: digits of keys 16 qg + (0..15) of the block, row s16.
+        const int xb = TV0 - A + t * VBK + 16 * qg + (s16 >> 1);
+        const int dh = (G == 4) ? 8 * (s16 & 1) : 0;
+        const v2i32 d0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(dig + xb * (4 * G) + dh));
+        const v2i32 d1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(dig + (xb + 8) * (4 * G) + dh));
+        const i32x4 av = i32x4{d0.x, d0.y, d1.x, d1.y};
+        const int vb = 16 * qg + (s16 >> 1);  // staged row of this lane's first read
 #pragma unroll
-        for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(p[g], vf[e], acc[g][e]);
+        for (int tt = 0; tt < NT; ++tt) {
+          const v2i32 b0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_v2i32*)(vst + vb * (D * VB) + 16 * (tt ^ vswz(vb)) + 8 * (s16 & 1)));
+          const v2i32 b1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_v2i32*)(vst + (vb + 8) * (D * VB) + 16 * (tt ^ vswz(vb + 8)) + 8 * (s16 & 1)));
+          cacc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{b0.x, b0.y, b1.x, b1.y}, cacc[tt], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
-    };
-    const int vx0 = TV0 - A + vr;  // LDS row of tile 0 for this lane
-    int t0 = 0;
-    for (; t0 + 2 * UV <= nv; t0 += UV) {
+      const float vsig = ldexpf(1.0f, vex);
+      constexpr float k7 = 1.0f / 128.0f;
 #pragma unroll
-      for (int u = 0; u < UV; ++u) {
-        float vf[VE];
-        widen<VT, VE>(vd[u], vf);
-        vd[u] = load_nt<VLB>(vaddr(t0 + UV + u));
-        v_accum(vf, vx0 + (t0 + u) * VRPL);
+      for (int tt = 0; tt < NT; ++tt) {
+        const i32x4 c = cacc[tt];
+        const float x = fmaf(fmaf(fmaf(static_cast<float>(c[3]), k7, static_cast<float>(c[2])), k7,
+                                  static_cast<float>(c[1])),
+                             k7, static_cast<float>(c[0]));
+        vacc[tt] = fmaf(x, vsig, vacc[tt]);
       }
-    }
-    for (; t0 < nv; t0 += UV) {
+    } else {
+      // ---- pass 2: weighted sum of values (rolling prefetch of UV tiles) ------
+      auto v_accum = [&](const float (&vf)[VE], int r) {
+        float p[G];
 #pragma unroll
-      for (int u = 0; u < UV; ++u) {
-        if (t0 + u < nv) {
+        for (int g = 0; g < G; ++g) p[g] = sc[r * G + g];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(p[g], vf[e], acc[g][e]);
+        }
+      };
+      const int vx0 = TV0 - A + vr;  // LDS row of tile 0 for this lane
+      int t0 = 0;
+      for (; t0 + 2 * UV <= nv; t0 += UV) {
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
           float vf[VE];
           widen<VT, VE>(vd[u], vf);
-          if (t0 + UV + u < nv) vd[u] = load_nt<VLB>(vaddr(t0 + UV + u));
+          vd[u] = load_nt<VLB>(vaddr(t0 + UV + u));
           v_accum(vf, vx0 + (t0 + u) * VRPL);
+        }
+      }
+      for (; t0 < nv; t0 += UV) {
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+          if (t0 + u < nv) {
+            float vf[VE];
+            widen<VT, VE>(vd[u], vf);
+            if (t0 + UV + u < nv) vd[u] = load_nt<VLB>(vaddr(t0 + UV + u));
+            v_accum(vf, vx0 + (t0 + u) * VRPL);
+          }
         }
       }
     }
@@ -905,15 +1048,22 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         const float m_new = fmaxf(m_run[g], sl);
         const float alpha = (m_run[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
         l_run[g] *= alpha;
-#pragma unroll
-        for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
         psum[g] *= alpha;
         m_run[g] = m_new;
         const float pn = __builtin_amdgcn_exp2f(sl - m_new);
         if (lane == 0) l_run[g] += pn;  // l is summed over the whole wave below
-        if (vr == 0) {                  // acc is summed over the row groups below
+        if constexpr (VMF) {
+          if (kc == g) {
 #pragma unroll
-          for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(pn, vnew[e], acc[g][e]);
+            for (int t = 0; t < NT; ++t) vacc[t] = fmaf(pn, vnewm[t], vacc[t] * alpha);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
+          if (vr == 0) {  // acc is summed over the row groups below
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(pn, vnew[e], acc[g][e]);
+          }
         }
       }
     }
@@ -923,15 +1073,23 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     l_run[g] = wave_sum(l_run[g]);
-    if constexpr (VT == kI8) psum[g] = wave_sum(psum[g]);  // one lane wrote each row's weight
+    if constexpr (!VMF) {  // the matrix value pass leaves vacc complete
+      if constexpr (VT == kI8) psum[g] = wave_sum(psum[g]);  // one lane wrote each row's weight
 #pragma unroll
-    for (int e = 0; e < VE; ++e) {
-      float x = acc[g][e];
+      for (int e = 0; e < VE; ++e) {
+        float x = acc[g][e];
 #pragma unroll
-      for (int m = VLPR; m < 64; m <<= 1) x += __shfl_xor(x, m);
-      acc[g][e] = (VT == kI8) ? fmaf(-128.0f, psum[g], x) : x;
+        for (int m = VLPR; m < 64; m <<= 1) x += __shfl_xor(x, m);
+        acc[g][e] = (VT == kI8) ? fmaf(-128.0f, psum[g], x) : x;
+      }
     }
   }
+  // Matrix value pass: this lane's head kc (rows of heads >= G are unused)
+  // and its output dims 16 t + vn.
+  const int vn = lane & 15;
+  const bool vlive = !VMF || kc < G;
+  (void)vn;
+  (void)vlive;
   // ---- cooperative item: part 0 merges the four parts' states -------------
   if (coop) {
     // This wave's area of LDS (free after the last chunk) holds its state:
@@ -946,7 +1104,12 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         sc[G + g] = l_run[g];
       }
     }
-    if (vr == 0) {
+    if constexpr (VMF) {
+      if (vlive) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sc[2 * G + kc * D + 16 * t + vn] = vacc[t];
+      }
+    } else if (vr == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -960,8 +1123,15 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
 #pragma unroll
       for (int q = 0; q < kWaves; ++q) M = fmaxf(M, smem[q * (kLdsRows * G) + g]);
       float l = 0.0f;
+      if constexpr (VMF) {
+        if (kc == g) {
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
+          for (int t = 0; t < NT; ++t) vacc[t] = 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
+      }
 #pragma unroll
       for (int q = 0; q < kWaves; ++q) {
         const float* st = smem + q * (kLdsRows * G);
@@ -969,8 +1139,15 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         // an empty part has m = -inf and contributes nothing
         const float wq = (mq == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mq - M);
         l = fmaf(wq, st[G + g], l);
+        if constexpr (VMF) {
+          if (kc == g) {
 #pragma unroll
-        for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(wq, st[2 * G + g * D + vc * VE + e], acc[g][e]);
+            for (int t = 0; t < NT; ++t) vacc[t] = fmaf(wq, st[2 * G + g * D + 16 * t + vn], vacc[t]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(wq, st[2 * G + g * D + vc * VE + e], acc[g][e]);
+        }
       }
       m_run[g] = M;
       l_run[g] = l;
@@ -978,7 +1155,16 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   }
 
   const int64_t row0 = (static_cast<int64_t>(b) * a.H + kvh * G) * a.max_splits + sigma;
-  if (vr == 0) {
+  if constexpr (VMF) {
+    float inv = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) inv = (kc == g) ? 1.0f / l_run[g] : inv;
+    if (vlive) {
+      float* dst = a.part_o + (row0 + static_cast<int64_t>(kc) * a.max_splits) * D + vn;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) dst[16 * t] = vacc[t] * inv;
+    }
+  } else if (vr == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float inv = 1.0f / l_run[g];
