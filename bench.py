@@ -231,6 +231,7 @@ def settle_kernel(launch, seconds: float, kernel: str) -> dict:
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
 
 
 def prefill_cpu_baseline(inputs, q, min_seconds: float = 10.0) -> dict:
@@ -279,7 +280,8 @@ def prefill_cpu_baseline(inputs, q, min_seconds: float = 10.0) -> dict:
 def prefill_main(args) -> int:
     """One JSON line for a chunk (prefill) workload: the chunk producer plus
     the chunk's causal attention per step; roofline of the attention kernel
-    against the bf16 matrix-core peak."""
+    against the matrix-core peak of its operand type (bf16, or f32 for f32
+    caches)."""
     import numpy as np
     import torch
 
@@ -319,16 +321,19 @@ def prefill_main(args) -> int:
     tflops_step = flops / (ms_step * 1e-3) / 1e12
     tflops_attn = flops / (attn_ms * 1e-3) / 1e12
     tokens = w.batch * w.chunk
+    f32_cache = (w.k_dtype, w.v_dtype) == (0, 0)
+    peak = MFMA_F32_PEAK_TFLOPS if f32_cache else MFMA_BF16_PEAK_TFLOPS
     result = {
         "metric": "prefill chunk attention TFLOP/s (algorithmic) and tokens/s",
         "value": round(tflops_step, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
         "warmup": n_w, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if f32_cache else "bf16",
+        "data": "synthetic",
         "config": {"workload": name, "batch": w.batch, "chunk": w.chunk,
                    "ctx": int(inputs.seq_lens.max()), "n_heads": w.n_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "kv_cache": {(1, 1): "bf16/bf16", (1, 2): "bf16/int8(vq8)",
-                                (2, 2): "q8"}[(w.k_dtype, w.v_dtype)],
+                                (2, 2): "q8", (0, 0): "f32/f32"}[(w.k_dtype, w.v_dtype)],
                    "window": w.window, "softcap": w.softcap,
                    "layout": f"paged(block_size={args.paged})" if args.paged else "contiguous",
                    "parallelism": "single-gpu"},
@@ -339,12 +344,13 @@ def prefill_main(args) -> int:
         "settle": settle,
         "hbm_stream_probe": probe,
         "roofline": {"kernel": "prefill_attn_kernel", "bound": "mfma",
-                     "achieved": round(tflops_attn, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops_attn / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "achieved": round(tflops_attn, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops_attn / peak, 4),
                      "traffic": None if args.paged else measured_traffic(name, prefill_source_hash()),
                      "algorithmic_flops_per_launch": flops,
                      "kernel_source_sha256_16": prefill_source_hash(),
-                     "note": "the kernel issues twice the algorithmic matrix flops (q and the "
+                     "note": "f32 caches: f32 matrix products, the algorithmic flops" if f32_cache else
+                             "the kernel issues twice the algorithmic matrix flops (q and the "
                              "softmax weights enter as a bf16 high part and remainder)"},
     }
     if not args.no_cpu_baseline:

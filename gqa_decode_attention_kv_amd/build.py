@@ -24,7 +24,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "kv_produce.hip", "decode_partial.hip", "decode_partial_paged.hip",
            "decode_combine.hip", "decode_step.hip", "decode_step_paged.hip", "prefill_attn.hip",
-           "prefill_attn_vq8.hip", "prefill_attn_q8.hip", "decode_step_noalloc.hip"]
+           "prefill_attn_vq8.hip", "prefill_attn_q8.hip", "prefill_attn_f32.hip",
+           "decode_step_noalloc.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -494,11 +494,16 @@ uaii_status uaii_prefill_attn(const uaii_attn_shape* shape, const uaii_kv_cache*
   if (st != UAII_OK) return st;
   REQUIRE((cache->k_dtype == UAII_BF16 && cache->v_dtype == UAII_BF16) ||
               (cache->k_dtype == UAII_BF16 && cache->v_dtype == UAII_I8) ||
-              (cache->k_dtype == UAII_I8 && cache->v_dtype == UAII_I8),
+              (cache->k_dtype == UAII_I8 && cache->v_dtype == UAII_I8) ||
+              (cache->k_dtype == UAII_F32 && cache->v_dtype == UAII_F32),
           kNotImpl,
           "prefill over k_dtype=%d, v_dtype=%d is not supported (supported: bf16 keys with bf16 or int8 "
-          "values, or int8 keys and values: (1,1), (1,2), (2,2))",
+          "values, int8 keys and values, or f32 keys and values: (1,1), (1,2), (2,2), (0,0))",
           cache->k_dtype, cache->v_dtype);
+  REQUIRE(cache->k_dtype != UAII_F32 || shape->head_dim <= 128, kNotImpl,
+          "prefill over f32 caches with head_dim=%d is not supported (supported: 64 and 128; the f32 "
+          "tiles of head_dim 256 would not fit two work-groups' LDS)",
+          shape->head_dim);
   REQUIRE(n_tokens >= 1, kInvalid, "n_tokens=%d is invalid (must be >= 1)", n_tokens);
   REQUIRE(n_tokens <= (1 << 20), kNotImpl, "n_tokens=%d is not supported (supported: 1..%d per call)",
           n_tokens, 1 << 20);

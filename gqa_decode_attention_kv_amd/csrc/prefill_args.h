@@ -26,11 +26,13 @@ struct PrefillArgs {
 };
 
 // One work-group per (64 or 128 query rows, kv head, sequence).  Caches:
-// bf16 K and V, vq8 (bf16 K, int8 V) or q8 (int8 K and V).
+// bf16 K and V, vq8 (bf16 K, int8 V), q8 (int8 K and V), or f32 K and V
+// (head dim 64 or 128).
 hipError_t launch_prefill_attn(int D, int G, int B, int k_dtype, int v_dtype, const PrefillArgs& a,
                                hipStream_t stream);
 hipError_t launch_prefill_bf16(int D, int G, int B, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_vq8(int D, int G, int B, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_q8(int D, int G, int B, const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(int D, int G, int B, const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace uaii

@@ -13,6 +13,7 @@ hipError_t launch_prefill_attn(int D, int G, int B, int k_dtype, int v_dtype, co
   if (k_dtype == kBF16 && v_dtype == kBF16) return launch_prefill_bf16(D, G, B, a, stream);
   if (k_dtype == kBF16 && v_dtype == kI8) return launch_prefill_vq8(D, G, B, a, stream);
   if (k_dtype == kI8 && v_dtype == kI8) return launch_prefill_q8(D, G, B, a, stream);
+  if (k_dtype == kF32 && v_dtype == kF32) return launch_prefill_f32(D, G, B, a, stream);
   return hipErrorInvalidValue;
 }
 

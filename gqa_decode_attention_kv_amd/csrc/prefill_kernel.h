@@ -168,8 +168,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Rows staged per barrier: two 32-key halves with two query blocks per
   // wave up to d128 (half the barriers and staging bookkeeping per key),
   // one otherwise (d256 tiles would not fit two work-groups' LDS).
-  constexpr int KST = (QB == 2 && D <= 128) ? 2 * kKeys : kKeys;
-  constexpr int KEB = KT == kI8 ? 1 : 2, VEB = VT == kI8 ? 1 : 2;
+  // f32 caches (keys and values both f32) stage f32 tiles, one 32-key half
+  // per barrier, and multiply on the f32 matrix cores (16x16x4): q, the
+  // weights, K and V enter the products as they are.
+  constexpr bool F32 = KT == kF32;
+  static_assert(F32 == (VT == kF32), "f32 keys go with f32 values");
+  constexpr int KST = (QB == 2 && D <= 128 && !F32) ? 2 * kKeys : kKeys;
+  constexpr int KEB = F32 ? 4 : (KT == kI8 ? 1 : 2), VEB = F32 ? 4 : (VT == kI8 ? 1 : 2);
   using SK = Stage<D, KEB, KST>;
   using SV = Stage<D, VEB, KST>;
   constexpr int KSTEPS = D / 32;  // k-steps of the score product
@@ -178,12 +183,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // 16-byte reads, one per row, covers the banks once.  V (32-byte pad):
   // the transposing reads take 8 bytes from each of 8 rows per 32 lanes,
   // and rows 8 banks apart cover the banks once.
-  constexpr int LS = D + 8;
-  constexpr int LSV = D + 16;
+  // f32 tiles (strides in floats, 16-byte pad): the score reads (four
+  // floats of each of 16 rows) and the value reads (16 floats of each of 4
+  // rows, 4 rows apart) both cover the banks once.
+  constexpr int LS = F32 ? D + 4 : D + 8;
+  constexpr int LSV = F32 ? D + 4 : D + 16;
+  using LE = typename std::conditional<F32, float, uint16_t>::type;  // LDS element
+  constexpr int CE = 16 / static_cast<int>(sizeof(LE));  // LDS elements per 16-byte chunk
   // Two buffers of K and V tiles (and, for int8 caches, the tiles' per-token
   // key and value scales): one is read while the next tile is staged.
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][KST * LS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][KST * LSV];
+  __shared__ __attribute__((aligned(16))) LE ks[2][KST * LS];
+  __shared__ __attribute__((aligned(16))) LE vs[2][KST * LSV];
   __shared__ float ksc[2][KT == kI8 ? KST : 1];
   __shared__ float vsc[2][VT == kI8 ? KST : 1];
 
@@ -235,10 +245,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool rows_full = row0 + ROWS <= rows;
 
   // Queries: B operand of S^T = K Q^T, lane holds q[qi][ks*32 + 8*quad + j]
-  // of each block.
-  bf16x8 qh[QB][KSTEPS], ql[QB][KSTEPS];
+  // of each block (f32: qf holds q[qi][4 s + quad] for step s).
+  bf16x8 qh[QB][F32 ? 1 : KSTEPS], ql[QB][F32 ? 1 : KSTEPS];
+  float qf[QB][F32 ? D / 4 : 1];
+  (void)qh;
+  (void)ql;
+  (void)qf;
+  if constexpr (F32) {
 #pragma unroll
-  for (int q = 0; q < QB; ++q) {
+    for (int q = 0; q < QB; ++q) {
+      const float* qp = a.q + ((static_cast<int64_t>(b) * T + my_t[q]) * a.H + kvh * G + my_g[q]) * D + quad;
+#pragma unroll
+      for (int st = 0; st < D / 4; ++st) qf[q][st] = qp[4 * st] * a.q_mul;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < (F32 ? 0 : QB); ++q) {
     const float* qp =
         a.q + ((static_cast<int64_t>(b) * T + my_t[q]) * a.H + kvh * G + my_g[q]) * D + 8 * quad;
 #pragma unroll
@@ -356,7 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           *reinterpret_cast<u32x4*>(&ks[buf][r * LS + cc * 16]) = lo;
           *reinterpret_cast<u32x4*>(&ks[buf][r * LS + cc * 16 + 8]) = hi;
         } else {
-          *reinterpret_cast<u32x4*>(&ks[buf][r * LS + cc * 8]) = kreg[i];
+          *reinterpret_cast<u32x4*>(&ks[buf][r * LS + cc * CE]) = kreg[i];
         }
       }
     }
@@ -371,7 +393,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           *reinterpret_cast<u32x4*>(&vs[buf][r * LSV + cc * 16]) = lo;
           *reinterpret_cast<u32x4*>(&vs[buf][r * LSV + cc * 16 + 8]) = hi;
         } else {
-          *reinterpret_cast<u32x4*>(&vs[buf][r * LSV + cc * 8]) = vreg[i];
+          *reinterpret_cast<u32x4*>(&vs[buf][r * LSV + cc * CE]) = vreg[i];
         }
       }
     }
@@ -399,8 +421,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int h = 0; h < KST / kKeys; ++h) {
     const int k0 = k_begin + j * KST + h * kKeys;  // this half's first key
     if (h > 0 && k0 >= k_end) break;               // wave-uniform: past the last key
-    const uint16_t* kb = ks[buf] + h * kKeys * LS;
-    const uint16_t* vb_ = vs[buf] + h * kKeys * LSV;
+    const LE* kb = ks[buf] + h * kKeys * LS;
+    const LE* vb_ = vs[buf] + h * kKeys * LSV;
     const float* kscb = ksc[buf] + (KT == kI8 ? h * kKeys : 0);
     const float* vscb = vsc[buf] + (VT == kI8 ? h * kKeys : 0);
 
@@ -421,15 +443,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float c0 = fold ? -r[q] : 0.0f;
         s[q][mb] = f32x4{c0, c0, c0, c0};
       }
+    if constexpr (F32) {
+      // A = K (lane: key mb*16 + qi, dim 4 st + quad), B = Q^T.
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int st = 0; st < KSTEPS; ++st) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kb[(mb * 16 + qi) * LS + st * 32 + 8 * quad]);
+        for (int st = 0; st < D / 4; ++st) {
+          const float ka = kb[(mb * 16 + qi) * LS + 4 * st + quad];
 #pragma unroll
-        for (int q = 0; q < QB; ++q) {
-          s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[q][st], s[q][mb], 0, 0, 0);
-          s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[q][st], s[q][mb], 0, 0, 0);
+          for (int q = 0; q < QB; ++q) s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, qf[q][st], s[q][mb], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kb[(mb * 16 + qi) * LS + st * 32 + 8 * quad]);
+#pragma unroll
+          for (int q = 0; q < QB; ++q) {
+            s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[q][st], s[q][mb], 0, 0, 0);
+            s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[q][st], s[q][mb], 0, 0, 0);
+          }
         }
       }
     }
@@ -472,6 +507,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // when it exceeds the old one by more than kSlack, with the rescale of
     // the accumulator and the sums; the weights are recomputed in place.
     bf16x8 ph[QB], pl[QB];
+    float pf[QB][F32 ? 8 : 1];  // f32: the weights themselves, the A operand
+    (void)pf;
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       float p[8];
@@ -520,7 +557,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] *= vscb[(e < 4) ? 4 * quad + e : 16 + 4 * quad + (e - 4)];
       }
-      split8(p, ph[q], pl[q]);
+      if constexpr (F32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[q][e] = p[e];
+      } else {
+        split8(p, ph[q], pl[q]);
+      }
     }
 
     // O += P V.  A operand: lane holds P[qi][k = 8*quad + e], where k < 4 of
@@ -530,19 +572,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // (ds_read_b64_tr_b16).  Within each 16-lane group, the reading lane s
     // points at 4 dims (n*16 + 4*(s%4) ..) of key base + s/4, and lane i
     // receives dim n*16 + i of keys base .. base + 3.
-    const int tr_row = 4 * quad + (qi >> 2), tr_col = 4 * (qi & 3);
+    if constexpr (F32) {
+      // f32: step e multiplies key (e / 4) * 16 + 4*quad + e % 4 (k = quad),
+      // the key of the lane's weight pf[q][e]; B = V at that key, dim
+      // n*16 + qi.
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const s16x4 v0 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[tr_row * LSV + n * 16 + tr_col]));
-      const s16x4 v1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[(16 + tr_row) * LSV + n * 16 + tr_col]));
-      const s16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, vv);
+      for (int n = 0; n < NB; ++n) {
 #pragma unroll
-      for (int q = 0; q < QB; ++q) {
-        o[q][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[q], vb, o[q][n], 0, 0, 0);
-        o[q][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[q], vb, o[q][n], 0, 0, 0);
+        for (int e = 0; e < 8; ++e) {
+          const float vv = vb_[((e >> 2) * 16 + 4 * quad + (e & 3)) * LSV + n * 16 + qi];
+#pragma unroll
+          for (int q = 0; q < QB; ++q) o[q][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(pf[q][e], vv, o[q][n], 0, 0, 0);
+        }
+      }
+    } else {
+      const int tr_row = 4 * quad + (qi >> 2), tr_col = 4 * (qi & 3);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const s16x4 v0 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[tr_row * LSV + n * 16 + tr_col]));
+        const s16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[(16 + tr_row) * LSV + n * 16 + tr_col]));
+        const s16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          o[q][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[q], vb, o[q][n], 0, 0, 0);
+          o[q][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[q], vb, o[q][n], 0, 0, 0);
+        }
       }
     }
 

@@ -228,6 +228,13 @@ PREFILL = {
                                               ("fixed", 8192), 8192, BF16, BF16,
                                               Rope(NEOX, PLAIN, 10000.0), QKNorm(True, 1e-6, 1, 0.0, 0.1),
                                               window=4096, softcap=50.0, seed=(24,), chunk=1024),
+    # The gpt-oss-20b shape over its exact f32 cache (YaRN, a sink per head):
+    # a 512-token chunk appended to 3584 cached tokens, full-attention layer.
+    "prefill-gpt-oss-20b-f32-b2-c512-ctx4k": Workload("prefill-gpt-oss-20b-f32-b2-c512-ctx4k", 2, 64, 8, 64,
+                                                      ("fixed", 4096), 4096, F32, F32,
+                                                      Rope(NEOX, YARN, 150000.0, 32.0, 1.0, 32.0, 4096,
+                                                           False),
+                                                      sink=True, seed=(26,), chunk=512),
 }
 
 PREFILL_HEADLINE = "prefill-llama3.1-8b-b8-p2048"

@@ -370,16 +370,19 @@ uaii_status uaii_kv_produce_chunk(const uaii_attn_shape *shape, const uaii_rope 
  * uaii_decode_combine(_sink) of each query over its own prefix, in one
  * launch on the matrix cores.
  *   cache     contiguous or paged, with (k_dtype, v_dtype) one of
- *             (BF16, BF16), (BF16, I8) (vq8) or (I8, I8) (q8); f32 keys or
- *             values are refused with UAII_ERR_NOT_IMPLEMENTED
+ *             (BF16, BF16), (BF16, I8) (vq8), (I8, I8) (q8) or (F32, F32)
+ *             (head_dim 64 or 128); other pairs, and f32 at head_dim 256,
+ *             are refused with UAII_ERR_NOT_IMPLEMENTED
  *   q         device [batch][T][n_heads][head_dim] f32 (q_out of the chunk
  *             producer)
  *   seq_lens  host [batch], each in [T, capacity]
  *   n_tokens  1..2^20
  *   sinks     device [n_heads] f32, or NULL (no sink)
  *   out       device [batch][T][n_heads][head_dim] f32
- * Accumulation is f32; q and the softmax weights enter the matrix products
- * as a bf16 pair (high part and remainder), K and V as stored. */
+ * Accumulation is f32.  bf16 and int8 caches: q and the softmax weights
+ * enter the matrix products as a bf16 pair (high part and remainder), K and
+ * V as stored.  f32 caches: every operand enters as f32 (f32 matrix
+ * products). */
 uaii_status uaii_prefill_attn(const uaii_attn_shape *shape, const uaii_kv_cache *cache,
                               const float *q, const int32_t *seq_lens, int32_t n_tokens,
                               float scale, int32_t window, float softcap,

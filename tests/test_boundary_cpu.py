@@ -337,9 +337,10 @@ def test_kv_produce_chunk_refusals(case):
 
 @host_only
 @pytest.mark.parametrize("case", [
-    ("f32 cache", lambda: prefill(ca=cache(kd=B.F32, vd=B.F32)), NI,
-     ["prefill over k_dtype=0, v_dtype=0 is not supported", "(1,1), (1,2), (2,2)"]),
-    ("bf16 keys, f32 values", lambda: prefill(ca=cache(kd=B.BF16, vd=B.F32)), NI, ["v_dtype=0"]),
+    ("f32 cache at head_dim 256", lambda: prefill(sh=shape(d=256), ca=cache(kd=B.F32, vd=B.F32)), NI,
+     ["f32 caches with head_dim=256 is not supported", "64 and 128"]),
+    ("bf16 keys, f32 values", lambda: prefill(ca=cache(kd=B.BF16, vd=B.F32)), NI,
+     ["prefill over k_dtype=1, v_dtype=0 is not supported", "(1,1), (1,2), (2,2), (0,0)"]),
     ("f32 keys, int8 values", lambda: prefill(ca=cache(kd=B.F32, vd=B.I8, s=FAKE)), NI,
      ["k_dtype=0, v_dtype=2"]),
     ("vq8 without scales", lambda: prefill(ca=cache(vd=B.I8)), INV, ["v_scale is NULL"]),

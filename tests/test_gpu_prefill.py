@@ -46,7 +46,7 @@ def case(name, d, G, Hkv, T, lens, window=0, softcap=0.0, rope=None, norm=None, 
     return w, np.array(lens, np.int32), bs
 
 
-VQ8, Q8 = (W.BF16, W.I8), (W.I8, W.I8)
+VQ8, Q8, F32 = (W.BF16, W.I8), (W.I8, W.I8), (W.F32, W.F32)
 
 
 LLAMA3 = W.Rope(W.INTERLEAVED, W.LLAMA3, 5e5, 8.0)
@@ -91,6 +91,15 @@ SMALL = [
          np.random.default_rng(24).integers(72, 301, 32), window=150, seed=24, kv=Q8),
     case("vq8-d128-g2-b32-two-blocks-paged", 128, 2, 8, 140,
          np.random.default_rng(25).integers(140, 331, 32), sink=True, seed=25, kv=VQ8, bs=32),
+    # f32 caches (f32 matrix products), head dims 64 and 128: the gpt-oss
+    # shape (d64, G 8, sinks, a window), several tiles, paging, softcap, a
+    # ragged batch on the two-blocks path.
+    case("f32-d64-g8-sink-window", 64, 8, 1, 96, [300, 97], window=128, sink=True, seed=26, kv=F32),
+    case("f32-d128-g4-several-tiles", 128, 4, 2, 130, [700, 131], rope=LLAMA3, seed=27, kv=F32),
+    case("f32-d64-g2-paged-softcap", 64, 2, 2, 50, [250, 60], softcap=30.0, seed=28, kv=F32, bs=16),
+    case("f32-d128-g1-window-in-chunk", 128, 1, 3, 70, [200], window=33, norm=1, seed=29, kv=F32),
+    case("f32-d64-g8-b32-two-blocks", 64, 8, 8, 40,
+         np.random.default_rng(30).integers(40, 201, 32), sink=True, seed=30, kv=F32),
 ]
 
 
@@ -305,17 +314,18 @@ def test_prefill_matches_decode_token_by_token():
 
 
 def test_prefill_refusals_write_nothing():
-    """An f32 cache (not supported by the chunk kernel) and a length shorter
-    than the chunk are refused before any launch; nothing is written."""
+    """A cache pair the chunk kernel does not take (bf16 keys with f32
+    values) and a length shorter than the chunk are refused before any
+    launch; nothing is written."""
     from gqa_decode_attention_kv_amd import binding as B
     w, lens, _ = SMALL[0]
     inputs = W.make_prefill_inputs(w, seq_lens=lens)
     st = run_gpu(inputs)
     before = st.out.clone()
-    f32_cache = B.KVCache(B.F32, B.F32, st.cache.capacity, st.cache.k, st.cache.v, None, None, 0,
-                          0, 0, None)
-    with pytest.raises(B.UaiiError, match="prefill over k_dtype=0"):
-        B.prefill_attn(st.shape, f32_cache, st.q_out.data_ptr(), st.seq_lens, st.T, st.scale, 0,
+    mixed = B.KVCache(B.BF16, B.F32, st.cache.capacity, st.cache.k, st.cache.v, None, None, 0,
+                      0, 0, None)
+    with pytest.raises(B.UaiiError, match="prefill over k_dtype=1, v_dtype=0"):
+        B.prefill_attn(st.shape, mixed, st.q_out.data_ptr(), st.seq_lens, st.T, st.scale, 0,
                        0.0, None, st.out.data_ptr(), st.stream())
     with pytest.raises(B.UaiiError, match="seq_lens"):
         B.prefill_attn(st.shape, st.cache, st.q_out.data_ptr(), st.seq_lens - st.T, st.T, st.scale,
