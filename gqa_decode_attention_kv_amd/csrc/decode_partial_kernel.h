@@ -13,8 +13,10 @@
 // Models and formats" (The KV cache, in three precisions: vq8 values, q8
 // keys and values).
 //
-// Design (gfx950, bandwidth bound, no MFMA: one query row per kv head is a
-// GEMV; arithmetic intensity is 2-5 flop per KV byte, far below the ridge):
+// Design (gfx950, bandwidth bound: one query row per kv head is a GEMV with
+// 2-5 flop per KV byte, far below the ridge; the bf16 and f32 kernels run
+// it on the vector ALUs, the int8-value kernels on the matrix cores, which
+// takes the code widening and the per-element FMAs off the vector ALUs):
 //   * one wave64 per (sequence, kv head, split) work item, taken from a
 //     flattened per-sequence work table, so ragged batches and windows only
 //     launch waves that hold visible keys; four independent waves share a
@@ -36,11 +38,12 @@
 //   * scores live in the log2 domain (q pre-multiplied by scale*log2 e) so the
 //     exponential is one v_exp_f32; with a softcap the tanh clip is applied
 //     in the weights pass (it is monotonic, so the max commutes with it);
-//   * vq8: int8 codes are widened in registers and the per-token scale is
-//     folded into the softmax weight, so dequantisation costs no extra pass;
-//   * q8 keys: codes are widened the same way (as code + 128) in the K pass;
-//     the 128 * sum(q) offset and the key's per-token scale are applied to
-//     the raw score once per row, where the chunk max is taken;
+//   * int8 values (vq8, q8) with G of 2 or 4 and d <= 128: both passes on
+//     the matrix cores (key_mfma, value_mfma below); the key's per-token
+//     scale is applied to the raw score once per row, where the chunk max is
+//     taken, and the value's is folded into the softmax weight;
+//   * other int8 caches: codes are widened in registers (as code + 128), the
+//     128 * sum offsets removed once per row (keys) or at the end (values);
 //   * at the end the wave sums its row groups across lanes and writes one
 //     normalised partial and its log-sum-exp per query head.
 // Loads run as a rolling pipeline (the next tiles are requested as soon as
