@@ -920,18 +920,22 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       m_run[g] = m_new;
     }
 
-    // Matrix value pass: the weights p * vscale of the chunk are written as
-    // four base-128 int8 digits of p * vscale / vsig, vsig = 2^vex a power of
-    // two with max(vscale) / vsig in [32, 64) (p <= 1), packed one word per
-    // head (digit t in byte t).
-    int vex = 0;
-    if constexpr (VMF) {
-      float mx = 0.0f;
+    // Matrix value pass: the weights pv = p * vscale of the chunk are written
+    // as four base-128 int8 digits of pv / 2^vex[g], 2^vex[g] a power of two
+    // with the head's largest pv of the chunk / 2^vex[g] in [32, 64), packed
+    // one word per row and head (digit t in byte t).  The weights that carry
+    // the output thus keep their full precision whatever the spread of the
+    // value scales.  The weights pass leaves pv in LDS and its largest value
+    // per head in vmx; the digits replace pv after it.
+    int vex[G];
+    float vmx[G];
 #pragma unroll
-      for (int i = 0; i < kScaleRegs; ++i) mx = fmaxf(mx, sreg[i]);
-      mx = wave_max(mx);
-      vex = mx > 0.0f ? ilogbf(mx) - 5 : 0;
+    for (int g = 0; g < G; ++g) {
+      vex[g] = 0;
+      vmx[g] = 0.0f;
     }
+    (void)vex;
+    (void)vmx;
 
     // ---- weights p = 2^(s - m) for every row the value tiles cover (0 past
     // the end); vq8 folds the token's scale into p ---------------------------
@@ -949,15 +953,34 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
               ok ? __builtin_amdgcn_exp2f(capped_log2(sc[r * G + g], capped, cap_c, cap_inv) - m_run[g]) : 0.0f;
           l_run[g] += p;
           const float pv = p * vs;
+          sc[r * G + g] = pv;
           if constexpr (VMF) {
-            const float y = ldexpf(pv, -vex);
+            vmx[g] = fmaxf(vmx[g], pv);
+          } else if constexpr (VT == kI8) {
+            psum[g] += pv;
+          }
+        }
+      }
+    }
+    if constexpr (VMF) {
+      // Each lane rewrites its own rows, so no wave barrier is needed here.
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mx = wave_max(vmx[g]);
+        vex[g] = mx > 0.0f ? ilogbf(mx) - 5 : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < (kLdsRows + 63) / 64; ++i) {
+        const int r = lane + 64 * i;
+        if (64 * i >= xend) break;  // wave-uniform
+        if (r < xend) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float y = ldexpf(sc[r * G + g], -vex[g]);
             uint32_t word = 0;
 #pragma unroll
             for (int t = 0; t < 4; ++t) word |= (static_cast<uint32_t>(i8_digit(y, t)) & 0xFFu) << (8 * t);
             reinterpret_cast<uint32_t*>(sc)[r * G + g] = word;
-          } else {
-            sc[r * G + g] = pv;
-            if constexpr (VT == kI8) psum[g] += pv;
           }
         }
       }
@@ -1016,7 +1039,10 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
-      const float vsig = ldexpf(1.0f, vex);
+      int vexl = 0;  // the digit scale of this lane's head (kc)
+#pragma unroll
+      for (int g = 0; g < G; ++g) vexl = (kc == g) ? vex[g] : vexl;
+      const float vsig = ldexpf(1.0f, vexl);
       constexpr float k7 = 1.0f / 128.0f;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {

@@ -192,6 +192,42 @@ def dominant_new_row(strength, then=None):
     return prep
 
 
+def wild_value_scales(lo_exp, hi_exp, seed):
+    """prep (int8 values): multiply the per-token value scale of every cached
+    row by 10^u, u uniform in [lo_exp, hi_exp), so one chunk holds scales
+    over several orders of magnitude (the matrix value pass writes each
+    weight in digits of one scale per chunk)."""
+    def prep(inputs):
+        w = inputs.workload
+        assert w.v_dtype == W.I8
+        rng = np.random.default_rng(seed)
+        for b in range(w.batch):
+            L = int(inputs.seq_lens[b])
+            lo, _ = w.visible(L)
+            n = L - 1 - lo
+            if n > 0:
+                f = 10.0 ** rng.uniform(lo_exp, hi_exp, size=(w.n_kv_heads, n))
+                inputs.v_scale[b, :, lo:L - 1] *= f.astype(np.float32)
+    return prep
+
+
+def spiky_queries(factor, comp=5):
+    """prep: component `comp` of every query (before norm and rotation) is
+    multiplied by `factor`, so the largest element of each rotated query is
+    hundreds of times the others (the matrix key pass writes q in digits of
+    one scale per head)."""
+    def prep(inputs):
+        inputs.q_in[:, :, comp] *= np.float32(factor)
+    return prep
+
+
+def chain(*preps):
+    def prep(inputs):
+        for p in preps:
+            p(inputs)
+    return prep
+
+
 # -- score gap measurement --------------------------------------------------
 
 def score_gap_log2(inputs, pairs):
@@ -269,6 +305,23 @@ EDGES = [
      dominant_key(20.0), "lone", 100.0, 32, 3),
     (case("paged-coop-ramp-down-vq8-sink-window", 128, 4, 2, W.BF16, W.I8, [3000, 700], 512,
           window=2000, sink=True, seed=13), ramp_down(30.0), "coop", 100.0, 64, None),
+    # int8 values on the matrix cores: value scales over six orders of
+    # magnitude inside each chunk, on ramped keys (q8 G 4, vq8 G 2 d64 lone)
+    (case("coop-ramp-up-wild-value-scales-q8", 128, 4, 2, W.I8, W.I8, [4500, 2000], 1024,
+          seed=14), chain(ramp_up(30.0), wild_value_scales(-6.0, 0.0, 14)), "coop", 100.0, None,
+     None),
+    (case("lone-ramp-down-wild-value-scales-vq8-d64-g2", 64, 2, 32, W.BF16, W.I8, [2400] * 16,
+          600, seed=15), chain(ramp_down(30.0), wild_value_scales(-6.0, 0.0, 15)), "lone", 100.0,
+     None, 3),
+    # queries with one element hundreds of times the others: q8 keys (q in
+    # int8 digits), bf16 keys with G = 1 (key pass only on the matrix
+    # cores), and a paged vq8 G = 2 d64 cache
+    (case("coop-spiky-queries-q8", 128, 4, 2, W.I8, W.I8, [3000, 1500], 512, seed=16),
+     spiky_queries(1000.0), "coop", 100.0, None, None),
+    (case("coop-spiky-queries-vq8-g1", 128, 1, 4, W.BF16, W.I8, [3000, 1500], 512, seed=17),
+     spiky_queries(1000.0), "coop", 100.0, None, None),
+    (case("paged-coop-spiky-queries-vq8-g2-d64", 64, 2, 2, W.BF16, W.I8, [3000, 900], 1024,
+          seed=18), spiky_queries(300.0), "coop", 100.0, 16, None),
 ]
 
 
