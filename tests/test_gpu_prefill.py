@@ -7,13 +7,14 @@ computes their causal attention on the matrix cores.
   64/128/256, GQA ratios 1-8, empty and non-empty caches, ragged batches,
   windows (1, inside the chunk, wider than the context), softcap, sinks,
   one-token chunks, several key tiles, the paged layout, and both kernel
-  shapes (16 and 32 query rows per wave).
+  shapes (16 and 32 query rows per wave), over bf16, vq8, q8 and f32
+  caches.
 * The prefill workloads run at full size with sampled (sequence, token,
   head) outputs and every produced row.
 * The chunk's attention agrees with the decode path run token by token.
-Tolerances on the output are the decode path's: 2e-3 absolute for bf16 K/V
-(f32 accumulation), 1e-2 of the output's max-abs for int8 values (vq8, q8);
-produced int8 codes and scales are bit-exact.
+Tolerances on the output are the decode path's: 1e-5 absolute for f32 K/V,
+2e-3 for bf16 K/V (f32 accumulation), 1e-2 of the output's max-abs for int8
+values (vq8, q8); produced int8 codes and scales are bit-exact.
 """
 import numpy as np
 import pytest
