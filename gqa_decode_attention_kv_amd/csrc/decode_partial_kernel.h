@@ -30,7 +30,7 @@
 //     softmax states in LDS;
 //   * the G query heads that share the kv head are held in registers, so
 //     every K and V byte is read from HBM exactly once per group;
-//   * int8 values use 8-byte loads (see Elem);
+//   * int8 values on the vector pass use 8-byte loads (see Elem);
 //   * a wave walks its split in chunks of up to 512 rows with two passes per
 //     chunk: K (coalesced 16-byte loads, a row spread over d*sizeof(K)/16
 //     lanes, scores reduced across those lanes with DPP) with raw scores
@@ -39,10 +39,11 @@
 //   * scores live in the log2 domain (q pre-multiplied by scale*log2 e) so the
 //     exponential is one v_exp_f32; with a softcap the tanh clip is applied
 //     in the weights pass (it is monotonic, so the max commutes with it);
-//   * int8 values (vq8, q8) with G of 2 or 4 and d <= 128: both passes on
-//     the matrix cores (key_mfma, value_mfma below); the key's per-token
-//     scale is applied to the raw score once per row, where the chunk max is
-//     taken, and the value's is folded into the softmax weight;
+//   * int8 values (vq8, q8) with G <= 4: the key pass on the matrix cores
+//     (key_mfma below), and the value pass too with G of 2 or 4 and
+//     d <= 128 (value_mfma); the key's per-token scale is applied to the raw
+//     score once per row, where the chunk max is taken, and the value's is
+//     folded into the softmax weight;
 //   * other int8 caches: codes are widened in registers (as code + 128), the
 //     128 * sum offsets removed once per row (keys) or at the end (values);
 //   * at the end the wave sums its row groups across lanes and writes one
@@ -187,14 +188,18 @@ struct Elem {
 };
 
 // ---- key pass on the matrix cores ----------------------------------------
-// bf16 and int8 keys of groups of at most four heads are scored 16 keys at a
-// time, one MFMA per 32 dims (bf16) or 64 dims (int8).  The A operand holds
-// the query group, row 4 h + t being term t of head h; the B operand is the
-// 16 key rows exactly as loaded (lane l: key l % 16, the 16 bytes at
-// 16 (l / 16) + 64 s of its row for step s, dims taken in that order on both
-// sides); lane l of the 16 x 16 result holds rows 4 (l / 16) + i of key
-// l % 16, the terms of one head, which the lane adds.  Keys are never
-// widened, and the cross-lane reduction of the vector pass disappears.
+// Over caches with int8 values (where the vector pass is bound by the
+// vector ALUs; with bf16 values it is bound by HBM and the staging below
+// measured slower), bf16 and int8 keys of groups of at most four heads are
+// scored 16 keys at a time, one MFMA per 32 dims (bf16) or 64 dims (int8).
+// The A operand holds the query group, row 4 h + t being term t of head h;
+// the B operand is the 16 key rows, loaded as whole rows (1 KB per wave
+// load), staged in LDS and read back so that lane l holds key l % 16, the
+// 16 bytes of segment 4 s + l / 16 of its row for step s (dims taken in
+// that order on both sides); lane l of the 16 x 16 result holds rows
+// 4 (l / 16) + i of key l % 16, the terms of one head, which the lane adds.
+// Keys are never widened, and the cross-lane reduction of the vector pass
+// disappears.
 //   * bf16 keys: q (f32) is cut into three bf16 terms whose sum is exactly q
 //     (truncation leaves the low 16, then 8 significand bits), so every
 //     product is exact and the sum runs in the f32 accumulator.
@@ -268,13 +273,13 @@ __device__ inline const StepArgs* step_of(const StepArgs& s) { return &s; }
 // the matrix cores) are held to three waves per SIMD too: with half as many
 // loads in flight (below) they fit without spilling, where the per-tile
 // block lookups otherwise leave room for two.
-template <int D, int G, int KT, int VT, bool PAGED, bool FUSED, bool ILV>
+template <int D, int G, int KT, int VT, bool PAGED, bool FUSED>
 constexpr int min_waves() {
   return (PAGED && !FUSED && D == 128 && G <= 4 && KT != kI8 && !value_mfma<D, G, KT, VT>()) ? 3 : 2;
 }
 
 template <int D, int G, int KT, int VT, bool PAGED, bool FUSED, bool ILV>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves<D, G, KT, VT, PAGED, FUSED, ILV>(), 8))) void
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves<D, G, KT, VT, PAGED, FUSED>(), 8))) void
 decode_partial_kernel(const KernelArgs<FUSED> args) {
   const AttnArgs& a = attn_of(args);
   const StepArgs* x = step_of(args);
