@@ -207,12 +207,14 @@ struct Elem {
 //     is written as four base-128 int8 digits and multiplied by the codes
 //     in exact i32 arithmetic; the digits leave out at most 2^-22 sigma of
 //     each q.
-template <int G, int KT, int VT>
-constexpr bool key_mfma() { return G <= 4 && VT == kI8 && (KT == kBF16 || KT == kI8); }
+template <int D, int G, int KT, int VT>
+constexpr bool key_mfma() {
+  return (KT == kBF16 || KT == kI8) && ((G <= 4 && VT == kI8) || (G == 8 && VT != kF32 && D <= 128));
+}
 
 // The value pass on the matrix cores (int8 values, G of 2 or 4, d <= 128).
 template <int D, int G, int KT, int VT>
-constexpr bool value_mfma() { return key_mfma<G, KT, VT>() && (G == 2 || G == 4) && D <= 128; }
+constexpr bool value_mfma() { return key_mfma<D, G, KT, VT>() && (G == 2 || G == 4) && D <= 128; }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -285,7 +287,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   const StepArgs* x = step_of(args);
   // Matrix key pass (key_mfma): a K tile is 16 rows, each lane loading KNL
   // 16-byte segments of one row; otherwise a tile is one wave load.
-  constexpr bool KMF = key_mfma<G, KT, VT>();
+  constexpr bool KMF = key_mfma<D, G, KT, VT>();
   constexpr int KB = Elem<KT>::bytes, VB = Elem<VT>::bytes;
   constexpr int KLB = KMF ? 16 : Elem<KT>::template key_load<G>(), VLB = Elem<VT>::value_load;
   constexpr int KLPR = KMF ? 4 : D * KB / KLB;  // lanes per K row
@@ -307,8 +309,12 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   constexpr int LF = (G >= 8 || PAGED) ? kLoadsInFlight / 2 : kLoadsInFlight;
   constexpr int LFK = LF * 16 / KLB, LFV = LF * 16 / VLB;
   constexpr int LFKT = (LFK / KNL > 0) ? LFK / KNL : 1;  // K tiles in flight
-  constexpr int UK = (LFKT * KRPL <= kRowsPerChunk) ? LFKT : kRowsPerChunk / KRPL;
-  constexpr int UV = (LFV * VRPL <= kRowsPerChunk) ? LFV : kRowsPerChunk / VRPL;
+  // Rows per chunk: 512, or 256 for the matrix key pass at G = 8, whose
+  // [row][G] scores and key staging would otherwise leave LDS for one
+  // work-group per CU.
+  constexpr int CH = (KMF && G == 8) ? kRowsPerChunk / 2 : kRowsPerChunk;
+  constexpr int UK = (LFKT * KRPL <= CH) ? LFKT : CH / KRPL;
+  constexpr int UV = (LFV * VRPL <= CH) ? LFV : CH / VRPL;
   // Paged caches align tiles to blocks, so a chunk's rows sit up to 15 rows
   // after the start of its LDS window.
   // Matrix value pass (int8 values, G of 2 or 4, d <= 128): blocks of 64
@@ -320,11 +326,11 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   constexpr int NT = D / 16;                     // 16-dim output tiles
   // Paged chunks align their value blocks to 16 rows, up to 63 rows before
   // the chunk.
-  constexpr int kLdsRows = kRowsPerChunk + (PAGED ? (VMF ? 64 : 16) : 0);
+  constexpr int kLdsRows = CH + (PAGED ? (VMF ? 64 : 16) : 0);
   constexpr int kStageBytes = (VMF && VBK * D * VB > 16 * KRB) ? VBK * D * VB : 16 * KRB;
   constexpr int kScaleRegs = (VT == kI8) ? (kLdsRows + 63) / 64 : 1;
   constexpr int kKScaleRegs = (KT == kI8) ? (kLdsRows + 63) / 64 : 1;
-  static_assert(kRowsPerChunk % (UK * KRPL) == 0 && kRowsPerChunk % (UV * VRPL) == 0, "tiling");
+  static_assert(CH % (UK * KRPL) == 0 && CH % (UV * VRPL) == 0, "tiling");
   static_assert(KLPR >= 4 && VLPR >= 4, "row must span at least a quad");
 
   __shared__ __attribute__((aligned(16))) float smem[kWaves * kLdsRows * G];
@@ -406,7 +412,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       r1 = min(r0 + piece, r1);
     }
   }
-  // Chunk starts are multiples of kRowsPerChunk local rows, hence of BR.
+  // Chunk starts are multiples of CH local rows, hence of BR.
   auto chunk_row = [&](int c) -> int {
     if constexpr (ILV) {
       return R0 + kWaves * c + BR * part;
@@ -439,62 +445,72 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   float* sc = smem + wave * (kLdsRows * G);  // this wave's [row][G] scores / weights
   float q[KMF ? 1 : G][KMF ? 1 : KE];
   using AOp = typename std::conditional<KT == kI8, i32x4, bf16x8>::type;
-  AOp qa[KNL];
-  float qsig = 1.0f;  // int8 keys: sigma of this lane's output head (kc)
-  // A operand from the G query rows at qsrc (row h at qsrc + h D, scaled by
-  // q_mul here): lane (m, kc), m = lane % 16, holds term / digit m % 4 of
-  // head m / 4 (zero past the group, and for bf16 row 4 h + 3), dims
-  // 32 s + 8 kc + j (bf16) or 64 s + 16 kc + j (int8) for step s.
+  // Matrix passes: heads are handled in groups of four (HG groups; G = 8
+  // has two), one A operand and one MFMA chain per group.
+  constexpr int HG = KMF ? (G + 3) / 4 : 1;
+  AOp qa[HG][KNL];
+  float qsig[HG];  // int8 keys: sigma of this lane's output head 4 hg + kc
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) qsig[hg] = 1.0f;
+  // A operand of head group hg from the G query rows at qsrc (row h at
+  // qsrc + h D, scaled by q_mul here): lane (m, kc), m = lane % 16, holds
+  // term / digit m % 4 of head 4 hg + m / 4 (zero past the group, and for
+  // bf16 row 4 h + 3), dims 32 s + 8 kc + j (bf16) or 64 s + 16 kc + j
+  // (int8) for step s.
   auto build_qa = [&](const float* qsrc) {
-    const int m = lane & 15, t = m & 3;
-    const bool live = (m >> 2) < G && (KT == kI8 || t < 3);
-    const float* qh = qsrc + min(m >> 2, G - 1) * D;
-    constexpr int SD = KT == kI8 ? 16 : 8;  // dims per lane and step
-    float x[KNL][SD];
 #pragma unroll
-    for (int st = 0; st < KNL; ++st)
-#pragma unroll
-      for (int j = 0; j < SD; j += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(qh + 4 * SD * st + SD * kc + j);
-        x[st][j] = v.x * a.q_mul;
-        x[st][j + 1] = v.y * a.q_mul;
-        x[st][j + 2] = v.z * a.q_mul;
-        x[st][j + 3] = v.w * a.q_mul;
-      }
-    if constexpr (KT == kI8) {
-      float mx = 0.0f;
+    for (int hg = 0; hg < HG; ++hg) {
+      const int m = lane & 15, t = m & 3;
+      const int h = 4 * hg + (m >> 2);
+      const bool live = h < G && (KT == kI8 || t < 3);
+      const float* qh = qsrc + min(h, G - 1) * D;
+      constexpr int SD = KT == kI8 ? 16 : 8;  // dims per lane and step
+      float x[KNL][SD];
 #pragma unroll
       for (int st = 0; st < KNL; ++st)
 #pragma unroll
-        for (int j = 0; j < SD; ++j) mx = fmaxf(mx, fabsf(x[st][j]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));  // max |q| of head m / 4
-      const int ex = mx > 0.0f ? ilogbf(mx) - 5 : 0;  // |q| / 2^ex < 64
-#pragma unroll
-      for (int st = 0; st < KNL; ++st) {
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int dg = live ? i8_digit(ldexpf(x[st][4 * j + k], -ex), t) : 0;
-            word |= (static_cast<uint32_t>(dg) & 0xFFu) << (8 * k);
-          }
-          w[j] = word;
+        for (int j = 0; j < SD; j += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(qh + 4 * SD * st + SD * kc + j);
+          x[st][j] = v.x * a.q_mul;
+          x[st][j + 1] = v.y * a.q_mul;
+          x[st][j + 2] = v.z * a.q_mul;
+          x[st][j + 3] = v.w * a.q_mul;
         }
-        qa[st] = i32x4{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1]), static_cast<int32_t>(w[2]),
-                       static_cast<int32_t>(w[3])};
-      }
-      qsig = __shfl(ldexpf(1.0f, ex), 4 * min(kc, G - 1));
-    } else {
+      if constexpr (KT == kI8) {
+        float mx = 0.0f;
 #pragma unroll
-      for (int st = 0; st < KNL; ++st) {
-        u32x4 w;
+        for (int st = 0; st < KNL; ++st)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          w[j] = live ? (bf16_term(x[st][2 * j], t) | (bf16_term(x[st][2 * j + 1], t) << 16)) : 0u;
-        qa[st] = __builtin_bit_cast(bf16x8, w);
+          for (int j = 0; j < SD; ++j) mx = fmaxf(mx, fabsf(x[st][j]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));  // max |q| of head m / 4
+        const int ex = mx > 0.0f ? ilogbf(mx) - 5 : 0;  // |q| / 2^ex < 64
+#pragma unroll
+        for (int st = 0; st < KNL; ++st) {
+          uint32_t w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int dg = live ? i8_digit(ldexpf(x[st][4 * j + k], -ex), t) : 0;
+              word |= (static_cast<uint32_t>(dg) & 0xFFu) << (8 * k);
+            }
+            w[j] = word;
+          }
+          qa[hg][st] = i32x4{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1]),
+                             static_cast<int32_t>(w[2]), static_cast<int32_t>(w[3])};
+        }
+        qsig[hg] = __shfl(ldexpf(1.0f, ex), 4 * min(kc, G - 1 - 4 * hg));
+      } else {
+#pragma unroll
+        for (int st = 0; st < KNL; ++st) {
+          u32x4 w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            w[j] = live ? (bf16_term(x[st][2 * j], t) | (bf16_term(x[st][2 * j + 1], t) << 16)) : 0u;
+          qa[hg][st] = __builtin_bit_cast(bf16x8, w);
+        }
       }
     }
   };
@@ -637,8 +653,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
     psum[g] = 0.0f;
   }
 
-  for (int a0 = r0; a0 < r1; a0 += kRowsPerChunk) {
-    const int nrows = min(kRowsPerChunk, r1 - a0);  // rows [a0, a0 + nrows), wave-uniform
+  for (int a0 = r0; a0 < r1; a0 += CH) {
+    const int nrows = min(CH, r1 - a0);  // rows [a0, a0 + nrows), wave-uniform
 
     // Loads address a row clamped into [a0, last]: every load is
     // unconditional and in the visible range; rows outside are masked after
@@ -765,30 +781,41 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        COp c = {0, 0, 0, 0};
+        COp c[HG];
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) c[hg] = COp{0, 0, 0, 0};
 #pragma unroll
         for (int st = 0; st < KNL; ++st) {
           const int seg = 4 * st + kc;
           const u32x4 kb = stg[64 * (kr / KRPI) + (kr % KRPI) * KSPR + (seg ^ kswz(kr))];
-          if constexpr (KT == kI8) {
-            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[st], __builtin_bit_cast(i32x4, kb), c, 0, 0, 0);
-          } else {
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], __builtin_bit_cast(bf16x8, kb), c, 0, 0, 0);
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg) {
+            if constexpr (KT == kI8) {
+              c[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[hg][st], __builtin_bit_cast(i32x4, kb), c[hg], 0, 0,
+                                                            0);
+            } else {
+              c[hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hg][st], __builtin_bit_cast(bf16x8, kb), c[hg], 0,
+                                                              0, 0);
+            }
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float sv;
-        if constexpr (KT == kI8) {
-          constexpr float k7 = 1.0f / 128.0f;
-          sv = fmaf(fmaf(fmaf(static_cast<float>(c[3]), k7, static_cast<float>(c[2])), k7, static_cast<float>(c[1])),
-                    k7, static_cast<float>(c[0])) *
-               qsig;
-        } else {
-          sv = (c[0] + c[1]) + c[2];
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          float sv;
+          if constexpr (KT == kI8) {
+            constexpr float k7 = 1.0f / 128.0f;
+            sv = fmaf(fmaf(fmaf(static_cast<float>(c[hg][3]), k7, static_cast<float>(c[hg][2])), k7,
+                           static_cast<float>(c[hg][1])),
+                      k7, static_cast<float>(c[hg][0])) *
+                 qsig[hg];
+          } else {
+            sv = (c[hg][0] + c[hg][1]) + c[hg][2];
+          }
+          if (4 * hg + kc < G) sc[r * G + 4 * hg + kc] = sv;
         }
-        if (kc < G) sc[r * G + kc] = sv;
       };
 #pragma unroll
       for (int u = 0; u < UK; ++u)

@@ -75,6 +75,14 @@ SMALL = [
          seed=13),
     case("yarn-q8-d128", 128, 4, 2, W.I8, W.I8, [1200], 512,
          rope=W.Rope(W.NEOX, W.YARN, 1e6, 4.0, 2.0, 64.0, 32768, True), seed=14),
+    # int8 caches at G = 8 (the key pass on the matrix cores in two groups
+    # of four heads, 256-row chunks): cooperative items, a window, softcap
+    # with a sink, d64, and one wave per item
+    case("vq8-d128-g8", 128, 8, 2, W.BF16, W.I8, [1500, 700, 3], 512, seed=15),
+    case("q8-d128-g8-softcap-sink", 128, 8, 1, W.I8, W.I8, [2000, 65], 256, softcap=30.0,
+         sink=True, seed=16),
+    case("vq8-d64-g8-window", 64, 8, 2, W.BF16, W.I8, [1700, 90], 256, window=600, seed=17),
+    case("q8-d128-g8-lone", 128, 8, 8, W.I8, W.I8, [2048] * 8, 64, seed=18),
 ]
 
 
@@ -85,7 +93,8 @@ def test_variant_small(spec):
 
 
 PAGED = [
-    (SMALL[0], 16), (SMALL[1], 32), (SMALL[5], 16), (SMALL[11], 64),
+    (SMALL[0], 16), (SMALL[1], 32), (SMALL[5], 16), (SMALL[11], 64), (SMALL[14], 16),
+    (SMALL[15], 32),
 ]
 
 
