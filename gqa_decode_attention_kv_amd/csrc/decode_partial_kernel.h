@@ -212,9 +212,9 @@ constexpr bool key_mfma() {
   return (KT == kBF16 || KT == kI8) && ((G <= 4 && VT == kI8) || (G == 8 && VT != kF32 && D <= 128));
 }
 
-// The value pass on the matrix cores (int8 values, G of 2 or 4, d <= 128).
+// The value pass on the matrix cores (int8 values, G of 2, 4 or 8, d <= 128).
 template <int D, int G, int KT, int VT>
-constexpr bool value_mfma() { return key_mfma<D, G, KT, VT>() && (G == 2 || G == 4) && D <= 128; }
+constexpr bool value_mfma() { return key_mfma<D, G, KT, VT>() && VT == kI8 && G >= 2 && D <= 128; }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -317,7 +317,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   constexpr int UV = (LFV * VRPL <= CH) ? LFV : CH / VRPL;
   // Paged caches align tiles to blocks, so a chunk's rows sit up to 15 rows
   // after the start of its LDS window.
-  // Matrix value pass (int8 values, G of 2 or 4, d <= 128): blocks of 64
+  // Matrix value pass (int8 values, G of 2, 4 or 8, d <= 128): blocks of 64
   // keys, staged like the key tiles and read back transposed.
   constexpr bool VMF = value_mfma<D, G, KT, VT>();
   constexpr int VBK = 64;                        // keys per value block
@@ -516,7 +516,6 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   };
   float s_new[G];  // fused step: raw scores of the new token's row
   float vnew[VE];  // fused step: its stored value, this lane's V segment
-  float vnewm[NT];  // fused step, matrix value pass: dims 16 t + lane % 16
   if constexpr (FUSED) {
     const ProduceArgs& p = x->p;
     constexpr int EPL = pm::Shape<D>::EPL, NP = pm::Shape<D>::NP;
@@ -586,8 +585,13 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       pm::wave_sync();
 #pragma unroll
       for (int e = 0; e < VE; ++e) vnew[e] = vs[vc * VE + e];
+      if constexpr (VMF) {
+        // The matrix value pass reads the stored value row at the merge
+        // (the prologue's staging row, free from here on, holds it).
+        float* vkeep = reinterpret_cast<float*>(sx);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) vnewm[t] = vs[16 * t + (lane & 15)];
+        for (int e = 0; e < EPL; ++e) vkeep[lane + 64 * e] = vst[e];
+      }
     }
     pm::wave_sync();  // the staging area is the K pass's score buffer
   } else if constexpr (KMF) {
@@ -608,7 +612,6 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   }
   (void)s_new;
   (void)vnew;
-  (void)vnewm;
   (void)q;
   (void)qsig;
   // q8 keys in the vector pass: each raw score carries 128 * sum(q_h) from
@@ -632,16 +635,18 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   const float cap_c = a.softcap, cap_inv = capped ? 1.0f / a.softcap : 0.0f;
 
   // Vector value pass: acc[g][e] of this lane's value segment.  Matrix
-  // value pass: vacc[T] = head kc, dim 16 T + lane % 16, complete (no
-  // reduction across lanes), and vsig the chunk's digit scale.
+  // value pass: vacc[hg][T] = head 4 hg + kc, dim 16 T + lane % 16,
+  // complete (no reduction across lanes).
   float acc[VMF ? 1 : G][VMF ? 1 : VE];
 #pragma unroll
   for (int g = 0; g < (VMF ? 1 : G); ++g)
 #pragma unroll
     for (int e = 0; e < (VMF ? 1 : VE); ++e) acc[g][e] = 0.0f;
-  float vacc[VMF ? NT : 1];
+  float vacc[VMF ? HG : 1][VMF ? NT : 1];
 #pragma unroll
-  for (int t = 0; t < (VMF ? NT : 1); ++t) vacc[t] = 0.0f;
+  for (int hg = 0; hg < (VMF ? HG : 1); ++hg)
+#pragma unroll
+    for (int t = 0; t < (VMF ? NT : 1); ++t) vacc[hg][t] = 0.0f;
   (void)acc;
   (void)vacc;
   float m_run[G], l_run[G];
@@ -940,10 +945,12 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       const float alpha = (m_run[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
       l_run[g] *= alpha;
       if constexpr (VMF) {
-        if (kc == g) {
 #pragma unroll
-          for (int t = 0; t < NT; ++t) vacc[t] *= alpha;
-        }
+        for (int hg = 0; hg < HG; ++hg)
+          if (4 * hg + kc == g) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) vacc[hg][t] *= alpha;
+          }
       } else {
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
@@ -1038,9 +1045,11 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       char* vst = reinterpret_cast<char*>(kstage) + wave * kStageBytes;
       const char* dig = reinterpret_cast<const char*>(sc);
       const int s16 = lane & 15, qg = lane >> 4;
-      i32x4 cacc[NT];
+      i32x4 cacc[HG][NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) cacc[t] = i32x4{0, 0, 0, 0};
+      for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) cacc[hg][t] = i32x4{0, 0, 0, 0};
       for (int t = 0; t < nv; ++t) {
         const bool more = t + 1 < nv;  // wave-uniform
 #pragma unroll
@@ -1052,12 +1061,17 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // A: digits of keys 16 qg + (0..15) of the block, row s16.
+        // A of head group hg: digits of keys 16 qg + (0..15) of the block,
+        // row s16 (bytes 16 hg .. 16 hg + 15 of a key's 4 G digit bytes).
         const int xb = TV0 - A + t * VBK + 16 * qg + (s16 >> 1);
-        const int dh = (G == 4) ? 8 * (s16 & 1) : 0;
-        const v2i32 d0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(dig + xb * (4 * G) + dh));
-        const v2i32 d1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(dig + (xb + 8) * (4 * G) + dh));
-        const i32x4 av = i32x4{d0.x, d0.y, d1.x, d1.y};
+        i32x4 av[HG];
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          const int dh = (G >= 4) ? 16 * hg + 8 * (s16 & 1) : 0;
+          const v2i32 d0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(dig + xb * (4 * G) + dh));
+          const v2i32 d1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(dig + (xb + 8) * (4 * G) + dh));
+          av[hg] = i32x4{d0.x, d0.y, d1.x, d1.y};
+        }
         const int vb = 16 * qg + (s16 >> 1);  // staged row of this lane's first read
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -1065,24 +1079,30 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
               (lds_v2i32*)(vst + vb * (D * VB) + 16 * (tt ^ vswz(vb)) + 8 * (s16 & 1)));
           const v2i32 b1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               (lds_v2i32*)(vst + (vb + 8) * (D * VB) + 16 * (tt ^ vswz(vb + 8)) + 8 * (s16 & 1)));
-          cacc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{b0.x, b0.y, b1.x, b1.y}, cacc[tt], 0, 0, 0);
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg)
+            cacc[hg][tt] =
+                __builtin_amdgcn_mfma_i32_16x16x64_i8(av[hg], i32x4{b0.x, b0.y, b1.x, b1.y}, cacc[hg][tt], 0, 0, 0);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
-      int vexl = 0;  // the digit scale of this lane's head (kc)
-#pragma unroll
-      for (int g = 0; g < G; ++g) vexl = (kc == g) ? vex[g] : vexl;
-      const float vsig = ldexpf(1.0f, vexl);
       constexpr float k7 = 1.0f / 128.0f;
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        const i32x4 c = cacc[tt];
-        const float x = fmaf(fmaf(fmaf(static_cast<float>(c[3]), k7, static_cast<float>(c[2])), k7,
-                                  static_cast<float>(c[1])),
-                             k7, static_cast<float>(c[0]));
-        vacc[tt] = fmaf(x, vsig, vacc[tt]);
+      for (int hg = 0; hg < HG; ++hg) {
+        int vexl = 0;  // the digit scale of this lane's head 4 hg + kc
+#pragma unroll
+        for (int g = 0; g < G; ++g) vexl = (4 * hg + kc == g) ? vex[g] : vexl;
+        const float vsig = ldexpf(1.0f, vexl);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          const i32x4 c = cacc[hg][tt];
+          const float x = fmaf(fmaf(fmaf(static_cast<float>(c[3]), k7, static_cast<float>(c[2])), k7,
+                                    static_cast<float>(c[1])),
+                               k7, static_cast<float>(c[0]));
+          vacc[hg][tt] = fmaf(x, vsig, vacc[hg][tt]);
+        }
       }
     } else {
       // ---- pass 2: weighted sum of values (rolling prefetch of UV tiles) ------
@@ -1138,10 +1158,14 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         const float pn = __builtin_amdgcn_exp2f(sl - m_new);
         if (lane == 0) l_run[g] += pn;  // l is summed over the whole wave below
         if constexpr (VMF) {
-          if (kc == g) {
+          const float* vkeep = reinterpret_cast<const float*>(sxd + wave * D);
 #pragma unroll
-            for (int t = 0; t < NT; ++t) vacc[t] = fmaf(pn, vnewm[t], vacc[t] * alpha);
-          }
+          for (int hg = 0; hg < HG; ++hg)
+            if (4 * hg + kc == g) {
+#pragma unroll
+              for (int t = 0; t < NT; ++t)
+                vacc[hg][t] = fmaf(pn, vkeep[16 * t + (lane & 15)], vacc[hg][t] * alpha);
+            }
         } else {
 #pragma unroll
           for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
@@ -1169,12 +1193,10 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       }
     }
   }
-  // Matrix value pass: this lane's head kc (rows of heads >= G are unused)
-  // and its output dims 16 t + vn.
+  // Matrix value pass: this lane's heads 4 hg + kc (rows of heads >= G are
+  // unused) and its output dims 16 t + vn.
   const int vn = lane & 15;
-  const bool vlive = !VMF || kc < G;
   (void)vn;
-  (void)vlive;
   // ---- cooperative item: part 0 merges the four parts' states -------------
   if (coop) {
     // This wave's area of LDS (free after the last chunk) holds its state:
@@ -1190,10 +1212,12 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       }
     }
     if constexpr (VMF) {
-      if (vlive) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) sc[2 * G + kc * D + 16 * t + vn] = vacc[t];
-      }
+      for (int hg = 0; hg < HG; ++hg)
+        if (4 * hg + kc < G) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) sc[2 * G + (4 * hg + kc) * D + 16 * t + vn] = vacc[hg][t];
+        }
     } else if (vr == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -1209,10 +1233,12 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       for (int q = 0; q < kWaves; ++q) M = fmaxf(M, smem[q * (kLdsRows * G) + g]);
       float l = 0.0f;
       if constexpr (VMF) {
-        if (kc == g) {
 #pragma unroll
-          for (int t = 0; t < NT; ++t) vacc[t] = 0.0f;
-        }
+        for (int hg = 0; hg < HG; ++hg)
+          if (4 * hg + kc == g) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) vacc[hg][t] = 0.0f;
+          }
       } else {
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
@@ -1225,10 +1251,12 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         const float wq = (mq == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mq - M);
         l = fmaf(wq, st[G + g], l);
         if constexpr (VMF) {
-          if (kc == g) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) vacc[t] = fmaf(wq, st[2 * G + g * D + 16 * t + vn], vacc[t]);
-          }
+          for (int hg = 0; hg < HG; ++hg)
+            if (4 * hg + kc == g) {
+#pragma unroll
+              for (int t = 0; t < NT; ++t) vacc[hg][t] = fmaf(wq, st[2 * G + g * D + 16 * t + vn], vacc[hg][t]);
+            }
         } else {
 #pragma unroll
           for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(wq, st[2 * G + g * D + vc * VE + e], acc[g][e]);
@@ -1241,13 +1269,17 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
 
   const int64_t row0 = (static_cast<int64_t>(b) * a.H + kvh * G) * a.max_splits + sigma;
   if constexpr (VMF) {
-    float inv = 0.0f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) inv = (kc == g) ? 1.0f / l_run[g] : inv;
-    if (vlive) {
-      float* dst = a.part_o + (row0 + static_cast<int64_t>(kc) * a.max_splits) * D + vn;
+    for (int hg = 0; hg < HG; ++hg) {
+      const int h = 4 * hg + kc;
+      float inv = 0.0f;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) dst[16 * t] = vacc[t] * inv;
+      for (int g = 0; g < G; ++g) inv = (h == g) ? 1.0f / l_run[g] : inv;
+      if (h < G) {
+        float* dst = a.part_o + (row0 + static_cast<int64_t>(h) * a.max_splits) * D + vn;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) dst[16 * t] = vacc[hg][t] * inv;
+      }
     }
   } else if (vr == 0) {
 #pragma unroll
