@@ -79,6 +79,9 @@ constexpr int kKeys = 32;    // keys per tile
 constexpr float kSlack = 8.0f;
 constexpr float kSlackW = 256.0f;  // 2^kSlack
 constexpr float kLog2eP = 1.4426950408889634f;
+// Word 3 of a raw buffer descriptor on gfx9 parts: 32-bit data format,
+// offsets checked against the record count (reads past it return zero).
+constexpr int kBufferWord3 = 0x00020000;
 
 // max / sum of x over lanes l and l ^ 16, then over l and l ^ 32, with
 // gfx950's row swaps (v_permlane16_swap, v_permlane32_swap): swapping a
@@ -285,12 +288,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // key, start at 0 so that they never hold the wave on the exact path), and
   // this lane's share of the weight sum relative to m (the lanes of a query
   // hold different keys; their shares are added at the end).
+  // The reference r itself (m, or 0 while m is -inf) is kept negated in all
+  // four slots, the initial accumulator of the score product.
   float m[QB], l[QB];
+  f32x4 nref[QB];
   uint64_t unref[QB];  // lanes whose query has no reference yet (wave-uniform)
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
     m[q] = row_ok[q] ? -INFINITY : 0.0f;
     l[q] = 0.0f;
+    nref[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     unref[q] = __builtin_amdgcn_ballot_w64(row_ok[q]);
   }
 
@@ -317,21 +324,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const char* kslab = static_cast<const char*>(a.k) + slab * D * KEB;
   const char* vslab = static_cast<const char*>(a.v) + slab * D * VEB;
   auto clamp_row = [&](int r) { return min(max(r, lo_first), k_end - 1); };
+  // Byte offset of a thread's first 16-byte chunk within a K (V) tile; its
+  // load i is 4096 i bytes further (256 threads of 16 bytes, and a row
+  // spans a power of two of chunks up to 256).
+  static_assert(256 % SK::CPR == 0 && 256 % SV::CPR == 0, "tile chunks");
+  const int koff0 = tid / SK::CPR * (D * KEB) + tid % SK::CPR * 16;
+  const int voff0 = tid / SV::CPR * (D * VEB) + tid % SV::CPR * 16;
+  (void)koff0;
+  (void)voff0;
   auto load_tile = [&](int k0) {
     if (!PAGED && k0 >= lo_first && k0 + KST <= k_end) {
+      // Buffer loads over the tile's bytes (a descriptor built from the
+      // uniform tile base in scalar registers): load i of a thread reads
+      // chunk tid + 256 i, 4096 i bytes after its first, so the per-load
+      // offsets are scalar and no vector address is formed per tile.
       const char* kt = kslab + static_cast<int64_t>(k0) * (D * KEB);
       const char* vt = vslab + static_cast<int64_t>(k0) * (D * VEB);
+      const __amdgpu_buffer_rsrc_t krs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kt), 0, KST * D * KEB, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vrs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vt), 0, KST * D * VEB, kBufferWord3);
 #pragma unroll
       for (int i = 0; i < SK::NL; ++i) {
         const int c = tid + 256 * i;
         if (SK::NL * 256 == SK::TOTAL || c < SK::TOTAL)
-          kreg[i] = *reinterpret_cast<const u32x4*>(kt + static_cast<uint32_t>(c / SK::CPR * (D * KEB) + c % SK::CPR * 16));
+          kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, koff0, 4096 * i, 0));
       }
 #pragma unroll
       for (int i = 0; i < SV::NL; ++i) {
         const int c = tid + 256 * i;
         if (SV::NL * 256 == SV::TOTAL || c < SV::TOTAL)
-          vreg[i] = *reinterpret_cast<const u32x4*>(vt + static_cast<uint32_t>(c / SV::CPR * (D * VEB) + c % SV::CPR * 16));
+          vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff0, 4096 * i, 0));
       }
       if constexpr (KT == kI8 || VT == kI8) {
         const bool is_k = tid < KST;
@@ -434,15 +457,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr bool fold = !cap && KT != kI8;
     float r[QB];
 #pragma unroll
-    for (int q = 0; q < QB; ++q) r[q] = (m[q] == -INFINITY) ? 0.0f : m[q];
+    for (int q = 0; q < QB; ++q) r[q] = -nref[q][0];
     f32x4 s[QB][2];
 #pragma unroll
     for (int q = 0; q < QB; ++q)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const float c0 = fold ? -r[q] : 0.0f;
-        s[q][mb] = f32x4{c0, c0, c0, c0};
-      }
+      for (int mb = 0; mb < 2; ++mb) s[q][mb] = fold ? nref[q] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (F32) {
       // A = K (lane: key mb*16 + qi, dim 4 st + quad), B = Q^T.
 #pragma unroll
@@ -536,6 +556,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         l[q] *= alpha;
         m[q] = m_new;
+        nref[q] = f32x4{-r_new, -r_new, -r_new, -r_new};
         unref[q] = __builtin_amdgcn_ballot_w64(m_new == -INFINITY);
         // Rescale the accumulator: its rows are queries 4*quad + jj, whose
         // alpha lives in lane 4*quad + jj.  Skipped when no query's
