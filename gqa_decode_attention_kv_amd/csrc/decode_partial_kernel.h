@@ -39,11 +39,12 @@
 //   * scores live in the log2 domain (q pre-multiplied by scale*log2 e) so the
 //     exponential is one v_exp_f32; with a softcap the tanh clip is applied
 //     in the weights pass (it is monotonic, so the max commutes with it);
-//   * int8 values (vq8, q8) with G <= 4: the key pass on the matrix cores
-//     (key_mfma below), and the value pass too with G of 2 or 4 and
-//     d <= 128 (value_mfma); the key's per-token scale is applied to the raw
-//     score once per row, where the chunk max is taken, and the value's is
-//     folded into the softmax weight;
+//   * int8 values (vq8, q8), and groups of eight heads up to d128: the key
+//     pass on the matrix cores (key_mfma below), and with int8 values of
+//     groups of 2, 4 or 8 heads up to d128 the value pass too (value_mfma);
+//     the key's per-token scale is applied to the raw score once per row,
+//     where the chunk max is taken, and the value's is folded into the
+//     softmax weight;
 //   * other int8 caches: codes are widened in registers (as code + 128), the
 //     128 * sum offsets removed once per row (keys) or at the end (values);
 //   * at the end the wave sums its row groups across lanes and writes one
@@ -190,8 +191,11 @@ struct Elem {
 // ---- key pass on the matrix cores ----------------------------------------
 // Over caches with int8 values (where the vector pass is bound by the
 // vector ALUs; with bf16 values it is bound by HBM and the staging below
-// measured slower), bf16 and int8 keys of groups of at most four heads are
-// scored 16 keys at a time, one MFMA per 32 dims (bf16) or 64 dims (int8).
+// measured slower), and for groups of eight heads (whose vector pass spends
+// eight products and a cross-lane reduction per key element), keys are
+// scored 16 at a time on the matrix cores.  bf16 and int8 keys take groups
+// of four heads per MFMA chain, one MFMA per 32 dims (bf16) or 64 dims
+// (int8).
 // The A operand holds the query group, row 4 h + t being term t of head h;
 // the B operand is the 16 key rows, loaded as whole rows (1 KB per wave
 // load), staged in LDS and read back so that lane l holds key l % 16, the
@@ -207,9 +211,16 @@ struct Elem {
 //     is written as four base-128 int8 digits and multiplied by the codes
 //     in exact i32 arithmetic; the digits leave out at most 2^-22 sigma of
 //     each q.
+//   * f32 keys (G = 8): v_mfma_f32_16x16x4_f32 with row h of the A operand
+//     head h itself (rows past G zero), one MFMA per 4 dims: lane l takes
+//     dims (d / 4) (l / 16) + s at step s on both sides, so its key operand
+//     for four steps is one 16-byte LDS read; the result lane holds heads
+//     4 (l / 16) + i of key l % 16.  Products and sums are the f32 ones of
+//     the vector pass, in another order.
 template <int D, int G, int KT, int VT>
 constexpr bool key_mfma() {
-  return (KT == kBF16 || KT == kI8) && ((G <= 4 && VT == kI8) || (G == 8 && VT != kF32 && D <= 128));
+  return ((KT == kBF16 || KT == kI8) && ((G <= 4 && VT == kI8) || (G == 8 && VT != kF32 && D <= 128))) ||
+         (KT == kF32 && VT == kF32 && G == 8 && D <= 128);
 }
 
 // The value pass on the matrix cores (int8 values, G of 2, 4 or 8, d <= 128).
@@ -447,8 +458,11 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   using AOp = typename std::conditional<KT == kI8, i32x4, bf16x8>::type;
   // Matrix passes: heads are handled in groups of four (HG groups; G = 8
   // has two), one A operand and one MFMA chain per group.
-  constexpr int HG = KMF ? (G + 3) / 4 : 1;
-  AOp qa[HG][KNL];
+  constexpr bool KF32 = KMF && KT == kF32;  // f32 keys: one chain for all G heads
+  constexpr int HG = KMF ? (KF32 ? 1 : (G + 3) / 4) : 1;
+  AOp qa[KF32 ? 1 : HG][KF32 ? 1 : KNL];
+  float qk[KF32 ? D / 4 : 1];  // f32 keys: q[lane % 16][(D / 4) (lane / 16) + s]
+  (void)qk;
   float qsig[HG];  // int8 keys: sigma of this lane's output head 4 hg + kc
 #pragma unroll
   for (int hg = 0; hg < HG; ++hg) qsig[hg] = 1.0f;
@@ -458,8 +472,21 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   // bf16 row 4 h + 3), dims 32 s + 8 kc + j (bf16) or 64 s + 16 kc + j
   // (int8) for step s.
   auto build_qa = [&](const float* qsrc) {
+    if constexpr (KF32) {
+      const int m = lane & 15;
+      const float* qh = qsrc + min(m, G - 1) * D + (D / 4) * kc;
 #pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
+      for (int j = 0; j < D / 4; j += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(qh + j);
+        qk[j] = m < G ? v.x * a.q_mul : 0.0f;
+        qk[j + 1] = m < G ? v.y * a.q_mul : 0.0f;
+        qk[j + 2] = m < G ? v.z * a.q_mul : 0.0f;
+        qk[j + 3] = m < G ? v.w * a.q_mul : 0.0f;
+      }
+      return;
+    }
+#pragma unroll
+    for (int hg = 0; hg < (KF32 ? 0 : HG); ++hg) {
       const int m = lane & 15, t = m & 3;
       const int h = 4 * hg + (m >> 2);
       const bool live = h < G && (KT == kI8 || t < 3);
@@ -789,8 +816,20 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         COp c[HG];
 #pragma unroll
         for (int hg = 0; hg < HG; ++hg) c[hg] = COp{0, 0, 0, 0};
+        if constexpr (KF32) {
+          // Segment KNL kc + st of row kr: dims 4 (KNL kc + st) + e, step
+          // 4 st + e.
 #pragma unroll
-        for (int st = 0; st < KNL; ++st) {
+          for (int st = 0; st < KNL; ++st) {
+            const int seg = KNL * kc + st;
+            const u32x4 kb = stg[64 * (kr / KRPI) + (kr % KRPI) * KSPR + (seg ^ kswz(kr))];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              c[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(qk[4 * st + e], __uint_as_float(kb[e]), c[0], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int st = 0; st < (KF32 ? 0 : KNL); ++st) {
           const int seg = 4 * st + kc;
           const u32x4 kb = stg[64 * (kr / KRPI) + (kr % KRPI) * KSPR + (seg ^ kswz(kr))];
 #pragma unroll
@@ -807,8 +846,13 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if constexpr (KF32) {
 #pragma unroll
-        for (int hg = 0; hg < HG; ++hg) {
+          for (int i = 0; i < 4; ++i)
+            if (4 * kc + i < G) sc[r * G + 4 * kc + i] = c[0][i];
+        }
+#pragma unroll
+        for (int hg = 0; hg < (KF32 ? 0 : HG); ++hg) {
           float sv;
           if constexpr (KT == kI8) {
             constexpr float k7 = 1.0f / 128.0f;

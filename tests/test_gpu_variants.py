@@ -83,6 +83,15 @@ SMALL = [
          sink=True, seed=16),
     case("vq8-d64-g8-window", 64, 8, 2, W.BF16, W.I8, [1700, 90], 256, window=600, seed=17),
     case("q8-d128-g8-lone", 128, 8, 8, W.I8, W.I8, [2048] * 8, 64, seed=18),
+    # f32 caches at G = 8 (the key pass on the f32 matrix cores): cooperative
+    # items with softcap at d128, and one wave per item with the sink and
+    # gpt-oss's YaRN at d64 and with a window at d128
+    case("f32-d128-g8-softcap", 128, 8, 2, W.F32, W.F32, [1500, 700, 3], 512, softcap=30.0,
+         seed=19),
+    case("f32-d64-g8-lone-sink", 64, 8, 8, W.F32, W.F32, [2048] * 8, 64, rope=GPT_OSS_YARN,
+         sink=True, seed=20),
+    case("f32-d128-g8-lone-window", 128, 8, 8, W.F32, W.F32, [2048] * 8, 64, window=900,
+         seed=21),
 ]
 
 
@@ -94,7 +103,7 @@ def test_variant_small(spec):
 
 PAGED = [
     (SMALL[0], 16), (SMALL[1], 32), (SMALL[5], 16), (SMALL[11], 64), (SMALL[14], 16),
-    (SMALL[15], 32),
+    (SMALL[15], 32), (SMALL[18], 16), (SMALL[19], 32), (SMALL[20], 16),
 ]
 
 
