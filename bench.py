@@ -164,6 +164,62 @@ def cpu_baseline(inputs, min_seconds: float = 8.0) -> dict:
 PROBE_LIBRARY = os.path.join(ROOT, "gqa_decode_attention_kv_amd", "libuaii_probe.so")
 
 
+def gather_probe(piece_bytes: int, nbytes: int = 1 << 30, per_group: int = 2 << 20,
+                 min_seconds: float = 0.3) -> dict:
+    """The read ceiling of a paged cache's access pattern: nbytes of device
+    memory read as pieces of piece_bytes (one cache block of one kv head,
+    e.g. 4096 = 16 rows of d128 bf16) in a seeded random order, per_group
+    bytes of pieces per work-group of four waves, 16-byte non-temporal
+    loads; timed like stream_probe."""
+    import ctypes as C
+
+    import torch
+
+    if not os.path.exists(PROBE_LIBRARY):
+        raise RuntimeError(f"{PROBE_LIBRARY} is missing; run __graft_entry__.build()")
+    lib = C.CDLL(PROBE_LIBRARY)
+    lib.uaii_probe_gather_read.restype = C.c_int
+    lib.uaii_probe_gather_read.argtypes = [C.c_void_p, C.c_size_t, C.c_size_t, C.c_void_p, C.c_int,
+                                           C.c_int, C.c_void_p, C.c_void_p]
+    n_pieces = nbytes // piece_bytes
+    per = max(1, per_group // piece_bytes)
+    gen = torch.Generator().manual_seed(20240611)
+    order = torch.randperm(n_pieces, generator=gen).to(torch.int32).to("cuda")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(-(-n_pieces // per), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = lib.uaii_probe_gather_read(src.data_ptr(), n_pieces, piece_bytes, order.data_ptr(), n_pieces, per,
+                                        sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"uaii_probe_gather_read failed ({rc})")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(20):
+            launch()
+        n_settle += 20
+        torch.cuda.synchronize()
+    reps = 100
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        launch()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    gbs = n_pieces * piece_bytes / (us * 1e-6) / 1e9
+    del src, sink, order
+    torch.cuda.empty_cache()
+    return {"kernel": "gather_read_kernel", "bytes": n_pieces * piece_bytes, "piece_bytes": piece_bytes,
+            "pieces_per_group": per, "order": "seeded random permutation",
+            "us_per_launch": round(us, 2), "achieved": round(gbs, 1), "unit": "GB/s",
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "launches": n_settle + reps}
+
+
 def stream_probe(nbytes: int = 1 << 30, per_group: int = 2 << 20, min_seconds: float = 0.3) -> dict:
     """The practical HBM read ceiling: a plain streaming read of nbytes of
     device memory (16-byte non-temporal loads, one sequential stream per
@@ -388,6 +444,9 @@ def main() -> int:
                     help="skip the streaming-read probe that runs before the warm-up")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only run the streaming-read probe (1 GiB) and print its JSON line")
+    ap.add_argument("--gather-probe", type=int, default=0, metavar="PIECE_BYTES",
+                    help="only run the scattered-piece read probe (1 GiB in pieces of PIECE_BYTES, "
+                         "a paged cache's pattern) and print its JSON line")
     ap.add_argument("--workload", default=None, help="workload name (default: the B=32 ctx-8K one)")
     ap.add_argument("--split-size", type=int, default=None)
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK_SIZE",
@@ -425,6 +484,14 @@ def main() -> int:
         torch.cuda.synchronize()
         print(f"bench: copy probe moved {n * 4} bytes each way", file=sys.stderr, flush=True)
         del src, dst
+    if args.gather_probe:
+        probe = gather_probe(args.gather_probe)
+        print(json.dumps({"metric": "read of device memory in scattered pieces, GB/s",
+                          "value": probe["achieved"], "unit": "GB/s", "n_gpus": 1,
+                          "higher_is_better": True, "data": "synthetic",
+                          "config": {"workload": f"gather-read-1GiB-{args.gather_probe}B-pieces"},
+                          "probe": probe}), flush=True)
+        return 0
     if args.stream_probe:
         probe = stream_probe()
         print(json.dumps({"metric": "plain streaming read of device memory, GB/s",
