@@ -170,6 +170,18 @@ WORKLOADS = {
     "llama3.1-8b-q8": Workload("llama3.1-8b-q8", 32, 32, 8, 128, ("fixed", 8192), 8192, I8, I8,
                                Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
                                split_size=1024, seed=(7,)),
+    # Llama-3.1-70B attention: 64/8 heads of 128 (groups of eight query heads),
+    # the headline's batch, context and rotary scaling, over the bf16, q8 and
+    # vq8 caches.
+    "llama3.1-70b-b32-ctx8k": Workload("llama3.1-70b-b32-ctx8k", 32, 64, 8, 128, ("fixed", 8192), 8192,
+                                       BF16, BF16, Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
+                                       split_size=4096, seed=(10,)),
+    "llama3.1-70b-q8": Workload("llama3.1-70b-q8", 32, 64, 8, 128, ("fixed", 8192), 8192, I8, I8,
+                                Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
+                                split_size=1024, seed=(11,)),
+    "llama3.1-70b-vq8": Workload("llama3.1-70b-vq8", 32, 64, 8, 128, ("fixed", 8192), 8192, BF16, I8,
+                                 Rope(INTERLEAVED, LLAMA3, 500000.0, 8.0, 1.0, 4.0, 8192),
+                                 split_size=4096, seed=(12,)),
     # gpt-oss-20b attention: 64/8 heads of 64, YaRN (theta 150000, factor 32,
     # beta 1..32 over 4096, edges not rounded), a per-head sink, and the exact
     # f32 cache (its sampler moves too far under vq8); full-attention layers
