@@ -16,6 +16,8 @@ Prints ONE JSON line:
                  else null
   hbm_stream_probe  a plain streaming read of 1 GiB run before the warm-up: the
                  read rate this part sustains in practice
+                 (--stream-probe alone; --gather-probe BYTES reads the same
+                 bytes in scattered pieces, a paged cache's pattern)
   cpu_baseline   the CPU oracle (scalar double precision) on a bounded sample of
                  the same workload, on this host's cores
 """
