@@ -475,17 +475,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     } else {
+      // Both 16-key blocks per step, high terms then low terms: the 2 QB
+      // accumulators take turns, so consecutive products into one
+      // accumulator are 2 QB issues apart.
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int st = 0; st < KSTEPS; ++st) {
+        bf16x8 ka[2];
 #pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kb[(mb * 16 + qi) * LS + st * 32 + 8 * quad]);
+        for (int mb = 0; mb < 2; ++mb)
+          ka[mb] = *reinterpret_cast<const bf16x8*>(&kb[(mb * 16 + qi) * LS + st * 32 + 8 * quad]);
 #pragma unroll
-          for (int q = 0; q < QB; ++q) {
-            s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[q][st], s[q][mb], 0, 0, 0);
-            s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[q][st], s[q][mb], 0, 0, 0);
-          }
-        }
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int q = 0; q < QB; ++q)
+            s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[mb], qh[q][st], s[q][mb], 0, 0, 0);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int q = 0; q < QB; ++q)
+            s[q][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[mb], ql[q][st], s[q][mb], 0, 0, 0);
       }
     }
 
@@ -608,19 +616,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     } else {
       const int tr_row = 4 * quad + (qi >> 2), tr_col = 4 * (qi & 3);
+      // Two 16-column blocks at a time, high terms then low terms: 2 QB
+      // accumulators take turns.
 #pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const s16x4 v0 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[tr_row * LSV + n * 16 + tr_col]));
-        const s16x4 v1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[(16 + tr_row) * LSV + n * 16 + tr_col]));
-        const s16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, vv);
+      for (int n0 = 0; n0 < NB; n0 += 2) {
+        bf16x8 vb[2];
 #pragma unroll
-        for (int q = 0; q < QB; ++q) {
-          o[q][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[q], vb, o[q][n], 0, 0, 0);
-          o[q][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[q], vb, o[q][n], 0, 0, 0);
+        for (int i = 0; i < 2; ++i) {
+          const int n = n0 + i;
+          const s16x4 v0 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[tr_row * LSV + n * 16 + tr_col]));
+          const s16x4 v1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_[(16 + tr_row) * LSV + n * 16 + tr_col]));
+          vb[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
         }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < QB; ++q)
+            o[q][n0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[q], vb[i], o[q][n0 + i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < QB; ++q)
+            o[q][n0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[q], vb[i], o[q][n0 + i], 0, 0, 0);
       }
     }
 
