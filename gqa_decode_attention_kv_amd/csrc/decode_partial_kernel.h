@@ -41,7 +41,8 @@
 //     in the weights pass (it is monotonic, so the max commutes with it);
 //   * int8 values (vq8, q8), and groups of eight heads up to d128: the key
 //     pass on the matrix cores (key_mfma below), and with int8 values of
-//     groups of 2, 4 or 8 heads up to d128 the value pass too (value_mfma);
+//     groups of 2, 4 or 8 heads, or bf16 values of groups of eight, up to
+//     d128, the value pass too (value_mfma);
 //     the key's per-token scale is applied to the raw score once per row,
 //     where the chunk max is taken, and the value's is folded into the
 //     softmax weight;
@@ -223,9 +224,12 @@ constexpr bool key_mfma() {
          (KT == kF32 && VT == kF32 && G == 8 && D <= 128);
 }
 
-// The value pass on the matrix cores (int8 values, G of 2, 4 or 8, d <= 128).
+// The value pass on the matrix cores: int8 values with G of 2, 4 or 8, and
+// bf16 values with G = 8, d <= 128.
 template <int D, int G, int KT, int VT>
-constexpr bool value_mfma() { return key_mfma<D, G, KT, VT>() && VT == kI8 && G >= 2 && D <= 128; }
+constexpr bool value_mfma() {
+  return key_mfma<D, G, KT, VT>() && D <= 128 && ((VT == kI8 && G >= 2) || (VT == kBF16 && G == 8));
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -331,7 +335,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   // Matrix value pass (int8 values, G of 2, 4 or 8, d <= 128): blocks of 64
   // keys, staged like the key tiles and read back transposed.
   constexpr bool VMF = value_mfma<D, G, KT, VT>();
-  constexpr int VBK = 64;                        // keys per value block
+  constexpr bool VMB = VMF && VT == kBF16;       // bf16 values: weights as two bf16 terms
+  constexpr int VBK = VMB ? 32 : 64;             // keys per value block
   constexpr int VRPI = 1024 / (D * VB);          // value rows per 1 KB wave load
   constexpr int VNL = VMF ? VBK / VRPI : 1;      // loads per lane per value block
   constexpr int NT = D / 16;                     // 16-dim output tiles
@@ -662,16 +667,22 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   const float cap_c = a.softcap, cap_inv = capped ? 1.0f / a.softcap : 0.0f;
 
   // Vector value pass: acc[g][e] of this lane's value segment.  Matrix
-  // value pass: vacc[hg][T] = head 4 hg + kc, dim 16 T + lane % 16,
+  // value pass: vacc[s][T] = head vhead(s), dim 16 T + lane % 16,
   // complete (no reduction across lanes).
   float acc[VMF ? 1 : G][VMF ? 1 : VE];
 #pragma unroll
   for (int g = 0; g < (VMF ? 1 : G); ++g)
 #pragma unroll
     for (int e = 0; e < (VMF ? 1 : VE); ++e) acc[g][e] = 0.0f;
-  float vacc[VMF ? HG : 1][VMF ? NT : 1];
+  // Heads per lane: int8 values 4 hg + kc (one per head group), bf16
+  // values 2 kc and 2 kc + 1 (rows 4 kc .. 4 kc + 3 of the result are their
+  // two weight terms).
+  constexpr int VH = VMB ? 2 : HG;
+  auto vhead = [&](int s) { return VMB ? 2 * kc + s : 4 * s + kc; };
+  (void)vhead;
+  float vacc[VMF ? VH : 1][VMF ? NT : 1];
 #pragma unroll
-  for (int hg = 0; hg < (VMF ? HG : 1); ++hg)
+  for (int hg = 0; hg < (VMF ? VH : 1); ++hg)
 #pragma unroll
     for (int t = 0; t < (VMF ? NT : 1); ++t) vacc[hg][t] = 0.0f;
   (void)acc;
@@ -990,8 +1001,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       l_run[g] *= alpha;
       if constexpr (VMF) {
 #pragma unroll
-        for (int hg = 0; hg < HG; ++hg)
-          if (4 * hg + kc == g) {
+        for (int hg = 0; hg < VH; ++hg)
+          if (vhead(hg) == g) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) vacc[hg][t] *= alpha;
           }
@@ -1036,8 +1047,17 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
               ok ? __builtin_amdgcn_exp2f(capped_log2(sc[r * G + g], capped, cap_c, cap_inv) - m_run[g]) : 0.0f;
           l_run[g] += p;
           const float pv = p * vs;
-          sc[r * G + g] = pv;
-          if constexpr (VMF) {
+          if constexpr (VMB) {
+            // bf16 values: the weight as its bf16 high part (low half of
+            // the word) and the bf16 of the remainder (high half).
+            const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(pv));
+            const float rem = pv - __uint_as_float(hi << 16);
+            const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(rem));
+            reinterpret_cast<uint32_t*>(sc)[r * G + g] = hi | (lo << 16);
+          } else {
+            sc[r * G + g] = pv;
+          }
+          if constexpr (VMF && !VMB) {
             vmx[g] = fmaxf(vmx[g], pv);
           } else if constexpr (VT == kI8) {
             psum[g] += pv;
@@ -1045,7 +1065,7 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         }
       }
     }
-    if constexpr (VMF) {
+    if constexpr (VMF && !VMB) {
       // Each lane rewrites its own rows, so no wave barrier is needed here.
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -1072,7 +1092,70 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    if constexpr (VMF) {
+    if constexpr (VMB) {
+      // ---- pass 2 on the matrix cores, bf16 values (G = 8): per 32-key
+      // block, O += P V with v_mfma_f32_16x16x32_bf16.  The weights' bf16
+      // terms sit in LDS as [key][2 h + t] (the words written above), so the
+      // transposing 16-bit LDS read gives the A operand directly (row
+      // 2 h + t: term t of head h, eight keys per lane); the block's value
+      // rows are staged like the int8 blocks and read the same way for the
+      // B operand.  Both reads take keys 4 quad + 0..3 and 16 + 4 quad +
+      // 0..3 of the block for lane group quad, so the two operands agree on
+      // the order of the keys.  Result row 4 quad + i of lane (quad, n):
+      // head 2 quad + i / 2, term i % 2, dim 16 T + n; the two terms are
+      // added into vacc at the end of the chunk.
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      // 16-byte column blocks of a staged row are XOR-permuted so that the
+      // four rows one 16-lane group reads land on distinct banks.
+      auto vswz = [](int rr) { return D == 64 ? 2 * ((rr >> 1) & 1) : 2 * (rr & 3); };
+      char* vst = reinterpret_cast<char*>(kstage) + wave * kStageBytes;
+      const char* wts = reinterpret_cast<const char*>(sc);
+      const int qd = lane >> 4, n16 = lane & 15;
+      const int tr_row = 4 * qd + (n16 >> 2);  // rows of this lane's reads: tr_row, 16 + tr_row
+      f32x4 cacc[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) cacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int t = 0; t < nv; ++t) {
+        const bool more = t + 1 < nv;  // wave-uniform
+#pragma unroll
+        for (int st = 0; st < VNL; ++st) {
+          const int rr = VRPI * st + lane / CB;
+          *reinterpret_cast<u32x4*>(vst + rr * (D * VB) + 16 * ((lane % CB) ^ vswz(rr))) = vdm[st];
+          if (more) vdm[st] = load_nt<16>(vaddr_mf(t + 1, st));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // A: weight terms of keys tr_row, 16 + tr_row (4 G bytes per key),
+        // 8 bytes at column 8 (n16 % 4) of the key's 16 terms.
+        const int xb = TV0 - A + t * VBK + tr_row;
+        const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(wts + xb * (4 * G) + 8 * (n16 & 3)));
+        const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(wts + (xb + 16) * (4 * G) + 8 * (n16 & 3)));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          // B: dims 16 tt + 4 (n16 % 4) .. of the same keys.
+          const int cb = 2 * tt + ((n16 & 3) >> 1), off = 8 * (n16 & 1);
+          const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vst + tr_row * (D * VB) + 16 * (cb ^ vswz(tr_row)) + off));
+          const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vst + (tr_row + 16) * (D * VB) + 16 * (cb ^ vswz(tr_row + 16)) + off));
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+          cacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, cacc[tt], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        vacc[0][tt] += cacc[tt][0] + cacc[tt][1];
+        vacc[VMB ? 1 : 0][tt] += cacc[tt][2] + cacc[tt][3];
+      }
+    } else if constexpr (VMF) {
       // ---- pass 2 on the matrix cores: per 64-key block, O += P V with the
       // weights' digits as the A operand (row 4 h + t: digit t of head h)
       // and the codes as the B operand.  The block is staged in LDS (rows
@@ -1204,8 +1287,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         if constexpr (VMF) {
           const float* vkeep = reinterpret_cast<const float*>(sxd + wave * D);
 #pragma unroll
-          for (int hg = 0; hg < HG; ++hg)
-            if (4 * hg + kc == g) {
+          for (int hg = 0; hg < VH; ++hg)
+            if (vhead(hg) == g) {
 #pragma unroll
               for (int t = 0; t < NT; ++t)
                 vacc[hg][t] = fmaf(pn, vkeep[16 * t + (lane & 15)], vacc[hg][t] * alpha);
@@ -1257,10 +1340,10 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
     }
     if constexpr (VMF) {
 #pragma unroll
-      for (int hg = 0; hg < HG; ++hg)
-        if (4 * hg + kc < G) {
+      for (int hg = 0; hg < VH; ++hg)
+        if (vhead(hg) < G) {
 #pragma unroll
-          for (int t = 0; t < NT; ++t) sc[2 * G + (4 * hg + kc) * D + 16 * t + vn] = vacc[hg][t];
+          for (int t = 0; t < NT; ++t) sc[2 * G + vhead(hg) * D + 16 * t + vn] = vacc[hg][t];
         }
     } else if (vr == 0) {
 #pragma unroll
@@ -1278,8 +1361,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       float l = 0.0f;
       if constexpr (VMF) {
 #pragma unroll
-        for (int hg = 0; hg < HG; ++hg)
-          if (4 * hg + kc == g) {
+        for (int hg = 0; hg < VH; ++hg)
+          if (vhead(hg) == g) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) vacc[hg][t] = 0.0f;
           }
@@ -1296,8 +1379,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         l = fmaf(wq, st[G + g], l);
         if constexpr (VMF) {
 #pragma unroll
-          for (int hg = 0; hg < HG; ++hg)
-            if (4 * hg + kc == g) {
+          for (int hg = 0; hg < VH; ++hg)
+            if (vhead(hg) == g) {
 #pragma unroll
               for (int t = 0; t < NT; ++t) vacc[hg][t] = fmaf(wq, st[2 * G + g * D + 16 * t + vn], vacc[hg][t]);
             }
@@ -1314,8 +1397,8 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   const int64_t row0 = (static_cast<int64_t>(b) * a.H + kvh * G) * a.max_splits + sigma;
   if constexpr (VMF) {
 #pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      const int h = 4 * hg + kc;
+    for (int hg = 0; hg < VH; ++hg) {
+      const int h = vhead(hg);
       float inv = 0.0f;
 #pragma unroll
       for (int g = 0; g < G; ++g) inv = (h == g) ? 1.0f / l_run[g] : inv;

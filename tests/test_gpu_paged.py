@@ -45,6 +45,8 @@ PAGED = [
          seed=8),
     case("vq8-d256-g2-bs16-softcap-multichunk", 256, 2, 2, W.BF16, W.I8, [1600], 1100, 16,
          softcap=50.0, seed=9),
+    case("bf16-d128-g8-bs16-softcap", 128, 8, 2, W.BF16, W.BF16, [1500, 300], 512, 16, softcap=30.0,
+         seed=10),
 ]
 
 

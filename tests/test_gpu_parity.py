@@ -79,6 +79,11 @@ SMALL = [
     case("f32-d64-g8-long-items", 64, 8, 1, W.F32, W.F32, [3333], 4096, seed=24),
     case("f32-d256-g2-long-items", 256, 2, 1, W.F32, W.F32, [2500, 2049], 2048, seed=25),
     case("bf16-d64-g8-long-items", 64, 8, 1, W.BF16, W.BF16, [2600, 31], 2600, seed=26),
+    # G = 8 over bf16 values (both passes on the matrix cores): one wave
+    # per item with a window starting inside a split, and softcap at d64
+    case("bf16-d128-g8-lone-window", 128, 8, 8, W.BF16, W.BF16, [2048] * 8, 64, window=700, seed=27),
+    case("bf16-d64-g8-softcap-ragged", 64, 8, 2, W.BF16, W.BF16, [1300, 40, 700], 512, softcap=30.0,
+         seed=28),
 ]
 
 

@@ -114,7 +114,7 @@ def test_variant_paged(spec, bs):
 
 
 FULL = ["llama3.1-8b-q8", "gpt-oss-20b-full", "gpt-oss-20b-sliding", "gemma3-27b-global",
-        "gemma3-27b-local", "llama3.1-70b-q8", "llama3.1-70b-vq8"]
+        "gemma3-27b-local", "llama3.1-70b-q8", "llama3.1-70b-vq8", "llama3.1-70b-b32-ctx8k"]
 
 
 @pytest.mark.parametrize("name", FULL)
