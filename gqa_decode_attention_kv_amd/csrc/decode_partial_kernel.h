@@ -829,15 +829,22 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
         for (int hg = 0; hg < HG; ++hg) c[hg] = COp{0, 0, 0, 0};
         if constexpr (KF32) {
           // Segment KNL kc + st of row kr: dims 4 (KNL kc + st) + e, step
-          // 4 st + e.
+          // 4 st + e.  Four accumulators (one per e) added pairwise at the
+          // end: each sum then takes KNL + 2 roundings instead of 4 KNL,
+          // which keeps the scores as close as the vector pass's short
+          // chains and reduction tree.
+          COp ce[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ce[e] = COp{0, 0, 0, 0};
 #pragma unroll
           for (int st = 0; st < KNL; ++st) {
             const int seg = KNL * kc + st;
             const u32x4 kb = stg[64 * (kr / KRPI) + (kr % KRPI) * KSPR + (seg ^ kswz(kr))];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              c[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(qk[4 * st + e], __uint_as_float(kb[e]), c[0], 0, 0, 0);
+              ce[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(qk[4 * st + e], __uint_as_float(kb[e]), ce[e], 0, 0, 0);
           }
+          c[0] = (ce[0] + ce[1]) + (ce[2] + ce[3]);
         }
 #pragma unroll
         for (int st = 0; st < (KF32 ? 0 : KNL); ++st) {

@@ -322,6 +322,20 @@ EDGES = [
      spiky_queries(1000.0), "coop", 100.0, None, None),
     (case("paged-coop-spiky-queries-vq8-g2-d64", 64, 2, 2, W.BF16, W.I8, [3000, 900], 1024,
           seed=18), spiky_queries(300.0), "coop", 100.0, 16, None),
+    # groups of eight heads (the key pass, and for bf16 and int8 values the
+    # value pass, on the matrix cores): bf16 cooperative and lone, f32 with
+    # a sink, q8 with wild value scales, and a paged bf16 cache
+    (case("coop-ramp-up-bf16-g8-d128", 128, 8, 1, W.BF16, W.BF16, [4500, 2000], 1024, seed=26),
+     ramp_up(30.0), "coop", 100.0, None, None),
+    (case("lone-dominant-key-bf16-g8-d64", 64, 8, 32, W.BF16, W.BF16, [2400] * 16, 600, seed=27),
+     dominant_key(20.0), "lone", 100.0, None, 3),
+    (case("coop-ramp-down-f32-g8-sink", 64, 8, 2, W.F32, W.F32, [3000, 1200], 512, sink=True,
+          seed=28), ramp_down(30.0), "coop", 100.0, None, None),
+    (case("coop-ramp-up-wild-value-scales-q8-g8", 128, 8, 1, W.I8, W.I8, [4500, 2000], 1024,
+          seed=29), chain(ramp_up(30.0), wild_value_scales(-6.0, 0.0, 29)), "coop", 100.0, None,
+     None),
+    (case("paged-coop-ramp-up-bf16-g8", 128, 8, 2, W.BF16, W.BF16, [3000, 1500], 512, seed=30),
+     ramp_up(30.0), "coop", 100.0, 16, None),
 ]
 
 
@@ -346,6 +360,10 @@ FUSED = [
      dominant_key(20.0), 100.0, None),
     (case("fused-paged-ramp-down", 128, 4, 2, W.BF16, W.BF16, [3000, 1100], 1024, seed=25),
      ramp_down(30.0), 100.0, 16),
+    # G = 8 over bf16 values: the new row's value merged into the matrix
+    # pass's accumulator
+    (case("fused-new-row-dominant-bf16-g8", 128, 8, 1, W.BF16, W.BF16, [2500, 900], 512, seed=31),
+     dominant_new_row(20.0, then=ramp_down(10.0)), 60.0, None),
 ]
 
 
