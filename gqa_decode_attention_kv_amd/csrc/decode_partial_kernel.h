@@ -216,8 +216,10 @@ struct Elem {
 //     head h itself (rows past G zero), one MFMA per 4 dims: lane l takes
 //     dims (d / 4) (l / 16) + s at step s on both sides, so its key operand
 //     for four steps is one 16-byte LDS read; the result lane holds heads
-//     4 (l / 16) + i of key l % 16.  Products and sums are the f32 ones of
-//     the vector pass, in another order.
+//     4 (l / 16) + i of key l % 16.  The matrix core rounds each product
+//     and each four-product sum (the vector pass fuses its multiply-adds);
+//     four accumulator chains, added pairwise, keep the rounding per score
+//     to d / 16 + 2 steps.
 template <int D, int G, int KT, int VT>
 constexpr bool key_mfma() {
   return ((KT == kBF16 || KT == kI8) && ((G <= 4 && VT == kI8) || (G == 8 && VT != kF32 && D <= 128))) ||
@@ -461,9 +463,10 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   float* sc = smem + wave * (kLdsRows * G);  // this wave's [row][G] scores / weights
   float q[KMF ? 1 : G][KMF ? 1 : KE];
   using AOp = typename std::conditional<KT == kI8, i32x4, bf16x8>::type;
-  // Matrix passes: heads are handled in groups of four (HG groups; G = 8
-  // has two), one A operand and one MFMA chain per group.
-  constexpr bool KF32 = KMF && KT == kF32;  // f32 keys: one chain for all G heads
+  // Matrix key pass over bf16 and int8 keys: heads are handled in groups of
+  // four (HG groups; G = 8 has two), one A operand and one MFMA chain per
+  // group.  f32 keys take all G heads in one A operand (qk).
+  constexpr bool KF32 = KMF && KT == kF32;
   constexpr int HG = KMF ? (KF32 ? 1 : (G + 3) / 4) : 1;
   AOp qa[KF32 ? 1 : HG][KF32 ? 1 : KNL];
   float qk[KF32 ? D / 4 : 1];  // f32 keys: q[lane % 16][(D / 4) (lane / 16) + s]
@@ -1021,13 +1024,15 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
       m_run[g] = m_new;
     }
 
-    // Matrix value pass: the weights pv = p * vscale of the chunk are written
-    // as four base-128 int8 digits of pv / 2^vex[g], 2^vex[g] a power of two
-    // with the head's largest pv of the chunk / 2^vex[g] in [32, 64), packed
-    // one word per row and head (digit t in byte t).  The weights that carry
-    // the output thus keep their full precision whatever the spread of the
-    // value scales.  The weights pass leaves pv in LDS and its largest value
-    // per head in vmx; the digits replace pv after it.
+    // Matrix value pass, int8 values: the weights pv = p * vscale of the
+    // chunk are written as four base-128 int8 digits of pv / 2^vex[g],
+    // 2^vex[g] a power of two with the head's largest pv of the chunk /
+    // 2^vex[g] in [32, 64), packed one word per row and head (digit t in
+    // byte t).  The weights that carry the output thus keep their full
+    // precision whatever the spread of the value scales.  The weights pass
+    // leaves pv in LDS and its largest value per head in vmx; the digits
+    // replace pv after it.  bf16 values: the weights pass writes each word
+    // as the weight's two bf16 terms at once (no scale).
     int vex[G];
     float vmx[G];
 #pragma unroll
