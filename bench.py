@@ -17,7 +17,8 @@ Prints ONE JSON line:
   hbm_stream_probe  a plain streaming read of 1 GiB run before the warm-up: the
                  read rate this part sustains in practice
                  (--stream-probe alone; --gather-probe BYTES reads the same
-                 bytes in scattered pieces, a paged cache's pattern)
+                 bytes in scattered pieces, a paged cache's pattern, or with
+                 --gather-order kv the contiguous cache's K and V in turn)
   cpu_baseline   the CPU oracle (scalar double precision) on a bounded sample of
                  the same workload, on this host's cores
 """
@@ -166,13 +167,47 @@ def cpu_baseline(inputs, min_seconds: float = 8.0) -> dict:
 PROBE_LIBRARY = os.path.join(ROOT, "gqa_decode_attention_kv_amd", "libuaii_probe.so")
 
 
-def gather_probe(piece_bytes: int, nbytes: int = 1 << 30, per_group: int = 2 << 20,
-                 min_seconds: float = 0.3) -> dict:
-    """The read ceiling of a paged cache's access pattern: nbytes of device
-    memory read as pieces of piece_bytes (one cache block of one kv head,
-    e.g. 4096 = 16 rows of d128 bf16) in a seeded random order, per_group
-    bytes of pieces per work-group of four waves, 16-byte non-temporal
-    loads; timed like stream_probe."""
+GATHER_ORDERS = {
+    "random": "seeded random permutation",
+    "sequential": "sequential",
+    "kv": "the two halves in turn, one piece each",
+}
+
+
+def gather_order(n_pieces: int, per: int, order_kind: str):
+    """The piece indices of gather_probe, a permutation of range(n_pieces)
+    read per pieces at a time by each work-group (int64 CPU tensor)."""
+    import torch
+
+    if order_kind == "random":
+        gen = torch.Generator().manual_seed(20240611)
+        order = torch.randperm(n_pieces, generator=gen)
+    elif order_kind == "sequential":
+        order = torch.arange(n_pieces)
+    elif order_kind == "kv":
+        if per % 2 or n_pieces % per:
+            raise ValueError("the kv order needs an even number of pieces per group dividing the buffer")
+        halfper = per // 2
+        base = torch.arange(n_pieces // per)[:, None] * halfper + torch.arange(halfper)[None, :]
+        order = torch.stack([base, base + n_pieces // 2], dim=-1).reshape(-1)
+    else:
+        raise ValueError(f"unknown gather order {order_kind!r} (one of {sorted(GATHER_ORDERS)})")
+    assert order.numel() == n_pieces and int(order.min()) >= 0 and int(order.max()) < n_pieces
+    return order
+
+
+def gather_probe(piece_bytes: int, order_kind: str = "random", nbytes: int = 1 << 30,
+                 per_group: int = 2 << 20, min_seconds: float = 0.3) -> dict:
+    """The read ceiling of a decode kernel's access pattern: nbytes of device
+    memory read as pieces of piece_bytes, per_group bytes of pieces per
+    work-group of four waves, 16-byte non-temporal loads; timed like
+    stream_probe.  order_kind "random" takes the pieces in a seeded random
+    order (a paged cache: one piece is one cache block of one kv head, e.g.
+    4096 = 16 rows of d128 bf16); "kv" gives each work-group consecutive
+    pieces of both halves of the buffer in turn (the contiguous cache's K
+    and V arrays read chunk by chunk, e.g. 131072 = 512 rows of d128 bf16);
+    "sequential" reads every group's range in order (the control: it should
+    match stream_probe)."""
     import ctypes as C
 
     import torch
@@ -185,8 +220,8 @@ def gather_probe(piece_bytes: int, nbytes: int = 1 << 30, per_group: int = 2 << 
                                            C.c_int, C.c_void_p, C.c_void_p]
     n_pieces = nbytes // piece_bytes
     per = max(1, per_group // piece_bytes)
-    gen = torch.Generator().manual_seed(20240611)
-    order = torch.randperm(n_pieces, generator=gen).to(torch.int32).to("cuda")
+    order = gather_order(n_pieces, per, order_kind)
+    order = order.to(torch.int32).to("cuda")
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     sink = torch.zeros(-(-n_pieces // per), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
@@ -217,7 +252,7 @@ def gather_probe(piece_bytes: int, nbytes: int = 1 << 30, per_group: int = 2 << 
     del src, sink, order
     torch.cuda.empty_cache()
     return {"kernel": "gather_read_kernel", "bytes": n_pieces * piece_bytes, "piece_bytes": piece_bytes,
-            "pieces_per_group": per, "order": "seeded random permutation",
+            "pieces_per_group": per, "order": GATHER_ORDERS[order_kind],
             "us_per_launch": round(us, 2), "achieved": round(gbs, 1), "unit": "GB/s",
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "launches": n_settle + reps}
 
@@ -449,6 +484,9 @@ def main() -> int:
     ap.add_argument("--gather-probe", type=int, default=0, metavar="PIECE_BYTES",
                     help="only run the scattered-piece read probe (1 GiB in pieces of PIECE_BYTES, "
                          "a paged cache's pattern) and print its JSON line")
+    ap.add_argument("--gather-order", default="random", choices=sorted(GATHER_ORDERS),
+                    help="order of the pieces of --gather-probe: random (a paged cache), kv (the "
+                         "contiguous cache's K and V chunks in turn) or sequential (the control)")
     ap.add_argument("--workload", default=None, help="workload name (default: the B=32 ctx-8K one)")
     ap.add_argument("--split-size", type=int, default=None)
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK_SIZE",
@@ -487,11 +525,14 @@ def main() -> int:
         print(f"bench: copy probe moved {n * 4} bytes each way", file=sys.stderr, flush=True)
         del src, dst
     if args.gather_probe:
-        probe = gather_probe(args.gather_probe)
+        probe = gather_probe(args.gather_probe, args.gather_order)
+        wl = f"gather-read-1GiB-{args.gather_probe}B-pieces"
+        if args.gather_order != "random":
+            wl += f"-{args.gather_order}"
         print(json.dumps({"metric": "read of device memory in scattered pieces, GB/s",
                           "value": probe["achieved"], "unit": "GB/s", "n_gpus": 1,
                           "higher_is_better": True, "data": "synthetic",
-                          "config": {"workload": f"gather-read-1GiB-{args.gather_probe}B-pieces"},
+                          "config": {"workload": wl},
                           "probe": probe}), flush=True)
         return 0
     if args.stream_probe:

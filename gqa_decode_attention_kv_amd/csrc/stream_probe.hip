@@ -42,16 +42,22 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
 // buffer: work-group g reads pieces order[g * per_group ..] in turn, the
 // access pattern of a paged cache (one piece = one cache block of one kv
 // head).  Chunk i of the group's range is chunk i % 2^lcpp of its piece
-// i / 2^lcpp.
+// i / 2^lcpp.  The group's piece indices are staged in LDS before the first
+// load, so no load waits on a lookup in global memory (a paged kernel reads
+// its block ids ahead of its cache loads in the same way).
+constexpr int kMaxGroupPieces = 4096;
+
 __global__ __launch_bounds__(kThreads) void gather_read_kernel(const u32x4* __restrict__ src, int lcpp,
                                                                const int* __restrict__ order, int n_pieces,
                                                                int pieces_in_src, int per_group, uint32_t* sink) {
+  __shared__ int piece_of[kMaxGroupPieces];
   const int p0 = blockIdx.x * per_group;
   const int p1 = p0 + per_group < n_pieces ? p0 + per_group : n_pieces;
+  for (int k = threadIdx.x; k < p1 - p0; k += kThreads) piece_of[k] = min(max(order[p0 + k], 0), pieces_in_src - 1);
+  __syncthreads();
   const int end = (p1 - p0) << lcpp;
   auto addr = [&](int i) {
-    const int piece = min(max(order[p0 + (i >> lcpp)], 0), pieces_in_src - 1);
-    return (static_cast<int64_t>(piece) << lcpp) + (i & ((1 << lcpp) - 1));
+    return (static_cast<int64_t>(piece_of[i >> lcpp]) << lcpp) + (i & ((1 << lcpp) - 1));
   };
   uint32_t acc = 0;
   int i = threadIdx.x;
@@ -94,14 +100,15 @@ extern "C" int uaii_probe_stream_read(const void* src, size_t bytes, size_t byte
 // (device, 16-byte aligned, pieces_in_src * piece_bytes bytes readable),
 // piece k starting at byte order[k] * piece_bytes; `order` is a device
 // array of n_pieces indices (clamped to [0, pieces_in_src) on the device).
-// pieces_per_group pieces per work-group; `sink` as for
+// pieces_per_group pieces per work-group (at most 4096); `sink` as for
 // uaii_probe_stream_read, of at least ceil(n_pieces / pieces_per_group)
 // words.  Returns 0, or a HIP error code (1 = invalid argument, nothing
 // launched).
 extern "C" int uaii_probe_gather_read(const void* src, size_t pieces_in_src, size_t piece_bytes, const int* order,
                                       int n_pieces, int pieces_per_group, uint32_t* sink, void* stream) {
   if (src == nullptr || order == nullptr || sink == nullptr || piece_bytes < 16 || piece_bytes % 16 != 0 ||
-      n_pieces <= 0 || pieces_per_group <= 0 || pieces_in_src == 0 || pieces_in_src > 0x7FFFFFFF ||
+      n_pieces <= 0 || pieces_per_group <= 0 || pieces_per_group > kMaxGroupPieces || pieces_in_src == 0 ||
+      pieces_in_src > 0x7FFFFFFF ||
       reinterpret_cast<uintptr_t>(src) % 16 != 0)
     return 1;
   const size_t cpp = piece_bytes / 16;

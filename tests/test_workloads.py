@@ -37,3 +37,23 @@ def test_kv_bytes():
     assert W.WORKLOADS["qwen3-vq8"].kv_bytes() == 16 * 8 * 16384 * 388
     assert W.WORKLOADS["gemma2-local"].kv_bytes() == 8 * 8 * 4096 * 1024
     assert W.WORKLOADS["tiny"].kv_bytes() == 2 * 129 * 512
+
+
+def test_gather_probe_orders():
+    """The read probe's piece orders are permutations; the kv order gives
+    each work-group consecutive pieces of the buffer's two halves in turn."""
+    import os
+    import sys
+
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+
+    n, per = 64, 8
+    for kind in bench.GATHER_ORDERS:
+        o = bench.gather_order(n, per, kind).tolist()
+        assert sorted(o) == list(range(n)), kind
+    assert bench.gather_order(n, per, "sequential").tolist() == list(range(n))
+    kv = bench.gather_order(n, per, "kv").tolist()
+    assert kv[:per] == [0, 32, 1, 33, 2, 34, 3, 35]
+    assert kv[per:2 * per] == [4, 36, 5, 37, 6, 38, 7, 39]
+    assert bench.gather_order(n, per, "random").tolist() == bench.gather_order(n, per, "random").tolist()
