@@ -303,7 +303,7 @@ def stream_probe(nbytes: int = 1 << 30, per_group: int = 2 << 20, min_seconds: f
     gbs = nbytes / (us * 1e-6) / 1e9
     del src, sink
     torch.cuda.empty_cache()
-    return {"kernel": "stream_read_kernel", "bytes": nbytes, "bytes_per_group": per_group,
+    return {"kernel": "stream_read_kernel", "bytes": nbytes, "bytes_per_group": per_group, "groups": groups,
             "us_per_launch": round(us, 2), "achieved": round(gbs, 1), "unit": "GB/s",
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "launches": n_settle + reps}
 
@@ -481,6 +481,10 @@ def main() -> int:
                     help="skip the streaming-read probe that runs before the warm-up")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only run the streaming-read probe (1 GiB) and print its JSON line")
+    ap.add_argument("--stream-groups", type=int, default=0, metavar="G",
+                    help="with --stream-probe: split the 1 GiB into G equal work-group streams "
+                         "(default 512 of 2 MiB); G not a multiple of the 256 CUs leaves some CUs "
+                         "more streams than others")
     ap.add_argument("--gather-probe", type=int, default=0, metavar="PIECE_BYTES",
                     help="only run the scattered-piece read probe (1 GiB in pieces of PIECE_BYTES, "
                          "a paged cache's pattern) and print its JSON line")
@@ -536,11 +540,21 @@ def main() -> int:
                           "probe": probe}), flush=True)
         return 0
     if args.stream_probe:
-        probe = stream_probe()
+        wl = "stream-read-1GiB"
+        if args.stream_groups:
+            if args.stream_groups < 1 or args.stream_groups > (1 << 20):
+                print("bench.py: --stream-groups must be in 1..1048576", file=sys.stderr)
+                return 2
+            per = -(-(1 << 30) // args.stream_groups)
+            per = -(-per // 16) * 16
+            probe = stream_probe(per_group=per)
+            wl += f"-{-(-(1 << 30) // per)}-groups"
+        else:
+            probe = stream_probe()
         print(json.dumps({"metric": "plain streaming read of device memory, GB/s",
                           "value": probe["achieved"], "unit": "GB/s", "n_gpus": 1,
                           "higher_is_better": True, "data": "synthetic",
-                          "config": {"workload": "stream-read-1GiB"}, "probe": probe}), flush=True)
+                          "config": {"workload": wl}, "probe": probe}), flush=True)
         return 0
     if args.prefill:
         return prefill_main(args)
