@@ -124,11 +124,17 @@ bool finite_pos(double x) { return std::isfinite(x) && x > 0.0; }
 
 // Visible keys [lo, L) and the splits [first, last] that intersect them,
 // and the launch order of the splits (SeqTable: body splits first, then
-// the last splits by decreasing visible keys).
-void build_table(int B, const int32_t* lens, int32_t window, int32_t split, uaii::SeqTable* t) {
+// the last splits by decreasing visible keys).  Returns true when the
+// splits do not all hold the same number of visible keys.
+bool build_table(int B, const int32_t* lens, int32_t window, int32_t split, uaii::SeqTable* t) {
   std::memset(t, 0, sizeof *t);
   int32_t prefix = 0, body = 0;
   int32_t tail_rows[uaii::kMaxBatch];
+  int32_t rmin = split, rmax = 0;
+  auto rows = [&](int32_t r) {
+    rmin = std::min(rmin, r);
+    rmax = std::max(rmax, r);
+  };
   for (int b = 0; b < B; ++b) {
     const int32_t L = lens[b];
     const int32_t lo = (window > 0 && L > window) ? L - window : 0;
@@ -142,12 +148,16 @@ void build_table(int B, const int32_t* lens, int32_t window, int32_t split, uaii
     body += last - first;
     tail_rows[b] = L - std::max(last * split, lo);
     t->tail_order[b] = b;
+    rows(tail_rows[b]);
+    if (last > first) rows((first + 1) * split - lo);
+    if (last > first + 1) rows(split);
   }
   t->work_prefix[B] = prefix;
   t->body_prefix[B] = body;
   t->n_seq = B;
   std::stable_sort(t->tail_order, t->tail_order + B,
                    [&](int32_t x, int32_t y) { return tail_rows[x] > tail_rows[y]; });
+  return rmin != rmax;
 }
 
 uaii_status device_status(const char* fn, hipError_t e) {
@@ -375,8 +385,9 @@ uaii_status attn_args(const char* fn, const uaii_attn_shape* shape, const uaii_k
   const float s = static_cast<float>(want);
   a.q_mul = softcap > 0.0f ? s : s * log2e;
   a.softcap = softcap;
-  build_table(shape->batch, seq_lens, window, split_size, &a.t);
+  const bool uneven = build_table(shape->batch, seq_lens, window, split_size, &a.t);
   a.coop = a.t.work_prefix[shape->batch] * shape->n_kv_heads < uaii::kCoopBelow ? 1 : 0;
+  a.serp = (!a.coop && uneven) ? 1 : 0;
   if (cache->block_table != nullptr) {
     a.block_table = cache->block_table;
     a.block_size = cache->block_size;

@@ -367,7 +367,21 @@ decode_partial_kernel(const KernelArgs<FUSED> args) {
   // work-group takes one item and its waves (part = wave) share the split's
   // rows as described below, merged through LDS at the end.
   const bool coop = ILV || a.coop != 0;
-  const int item = coop ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) * kWaves + wave;
+  // Serpentine placement (serp: one wave per item, items of unequal size).
+  // Work-group position p runs on CU p mod kCUs, and the work table lists
+  // the items longest first, so in plain order the CUs of the first
+  // positions of every round get the largest items of each round.  Taking
+  // every other round of kCUs positions in reverse pairs them with the
+  // smallest instead, which evens the work per CU (HBM bandwidth is shared
+  // per CU).  The map is a permutation of the positions.
+  int lg = static_cast<int>(blockIdx.x);
+  if (!coop && a.serp != 0) {
+    const int n = static_cast<int>(gridDim.x);
+    const int rnd = lg / kCUs, j = lg % kCUs;
+    const int in_rnd = min(kCUs, n - rnd * kCUs);
+    lg = rnd * kCUs + ((rnd & 1) ? in_rnd - 1 - j : j);
+  }
+  const int item = coop ? lg : lg * kWaves + wave;
   const int part = coop ? wave : 0;
   const int total = a.t.work_prefix[a.t.n_seq] * a.Hkv;
   // Idle waves leave at once.  Cooperative work-groups leave as a whole (the

@@ -89,6 +89,10 @@ struct AttnArgs {
   // waves of a work-group share one item, a quarter of its rows each, and
   // merge their softmax states in LDS (more waves in flight for small steps).
   int32_t coop;
+  // 1: the work-groups of a step with one wave per item and items of unequal
+  // size take the work table's longest-first order in serpentine rounds of
+  // kCUs work-groups (see decode_partial_kernel.h); 0: in order.
+  int32_t serp;
   SeqTable t;
 };
 
@@ -99,6 +103,10 @@ struct AttnArgs {
 #define UAII_COOP_BELOW 2048
 #endif
 constexpr int kCoopBelow = UAII_COOP_BELOW;
+
+// Compute units of an MI355X: the hardware hands out work-groups to them in
+// turn, so work-group position p of a launch lands on CU p mod kCUs.
+constexpr int kCUs = 256;
 
 // uaii_decode_step runs as one kernel up to this many (split, kv head) work
 // items, and as the three kernels back to back above it.  In one kernel,

@@ -270,9 +270,14 @@ EDGES = [
     # one wave per item (>= 2048 items), 600-row splits: two chunks per wave
     (case("lone-ramp-up-d64-g4", 64, 4, 32, W.BF16, W.BF16, [2400] * 16, 600, seed=1),
      ramp_up(30.0), "lone", 100.0, None, 3),
+    # ragged lengths: items of unequal size, so the work-groups take the
+    # serpentine placement (3.8 rounds of 256, the last one partial)
     (case("lone-ramp-down-d128-g4-ragged", 128, 4, 8, W.BF16, W.BF16,
           np.random.default_rng(2).integers(300, 901, 32), 40, seed=2),
      ramp_down(30.0), "lone", 100.0, None, 3),
+    (case("paged-lone-ramp-down-d128-g4-ragged", 128, 4, 8, W.BF16, W.BF16,
+          np.random.default_rng(2).integers(300, 901, 32), 40, seed=8),
+     ramp_down(30.0), "lone", 100.0, 16, 3),
     # cooperative interleaved work-groups, 1024 rows (two chunks) per wave
     (case("coop-ramp-up-d128-g4", 128, 4, 2, W.BF16, W.BF16, [5000, 4500], 4096, seed=3),
      ramp_up(30.0), "coop", 100.0, None, None),
