@@ -481,6 +481,9 @@ def main() -> int:
                     help="skip the streaming-read probe that runs before the warm-up")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only run the streaming-read probe (1 GiB) and print its JSON line")
+    ap.add_argument("--stream-mib", type=int, default=1024, metavar="M",
+                    help="with --stream-probe: read M MiB instead of 1 GiB (512 work-groups unless "
+                         "--stream-groups is given)")
     ap.add_argument("--stream-groups", type=int, default=0, metavar="G",
                     help="with --stream-probe: split the 1 GiB into G equal work-group streams "
                          "(default 512 of 2 MiB); G not a multiple of the 256 CUs leaves some CUs "
@@ -540,17 +543,20 @@ def main() -> int:
                           "probe": probe}), flush=True)
         return 0
     if args.stream_probe:
-        wl = "stream-read-1GiB"
+        if args.stream_mib < 1 or args.stream_mib > (64 << 10):
+            print("bench.py: --stream-mib must be in 1..65536", file=sys.stderr)
+            return 2
+        nbytes = args.stream_mib << 20
+        wl = "stream-read-1GiB" if args.stream_mib == 1024 else f"stream-read-{args.stream_mib}MiB"
+        groups = args.stream_groups or 512
+        if groups < 1 or groups > (1 << 20):
+            print("bench.py: --stream-groups must be in 1..1048576", file=sys.stderr)
+            return 2
+        per = -(-nbytes // groups)  # bytes per work-group, rounded up
+        per = -(-per // 16) * 16     # to whole 16-byte loads
+        probe = stream_probe(nbytes=nbytes, per_group=per)
         if args.stream_groups:
-            if args.stream_groups < 1 or args.stream_groups > (1 << 20):
-                print("bench.py: --stream-groups must be in 1..1048576", file=sys.stderr)
-                return 2
-            per = -(-(1 << 30) // args.stream_groups)
-            per = -(-per // 16) * 16
-            probe = stream_probe(per_group=per)
-            wl += f"-{-(-(1 << 30) // per)}-groups"
-        else:
-            probe = stream_probe()
+            wl += f"-{-(-nbytes // per)}-groups"
         print(json.dumps({"metric": "plain streaming read of device memory, GB/s",
                           "value": probe["achieved"], "unit": "GB/s", "n_gpus": 1,
                           "higher_is_better": True, "data": "synthetic",
