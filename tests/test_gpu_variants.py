@@ -92,6 +92,16 @@ SMALL = [
          sink=True, seed=20),
     case("f32-d128-g8-lone-window", 128, 8, 8, W.F32, W.F32, [2048] * 8, 64, window=900,
          seed=21),
+    # one wave per item over items of unequal size (ragged lengths, 40-key
+    # splits, about 3900 items): the work-groups take the serpentine
+    # placement, here through the int8 and f32 kernels
+    case("q8-d128-g8-lone-ragged", 128, 8, 8, W.I8, W.I8,
+         np.random.default_rng(22).integers(300, 901, 32), 40, seed=22),
+    case("vq8-d128-g4-lone-ragged", 128, 4, 8, W.BF16, W.I8,
+         np.random.default_rng(23).integers(300, 901, 32), 40, seed=23),
+    case("f32-d64-g8-lone-ragged-sink", 64, 8, 8, W.F32, W.F32,
+         np.random.default_rng(24).integers(300, 901, 32), 40, rope=GPT_OSS_YARN, sink=True,
+         seed=24),
 ]
 
 
@@ -103,7 +113,7 @@ def test_variant_small(spec):
 
 PAGED = [
     (SMALL[0], 16), (SMALL[1], 32), (SMALL[5], 16), (SMALL[11], 64), (SMALL[14], 16),
-    (SMALL[15], 32), (SMALL[18], 16), (SMALL[19], 32), (SMALL[20], 16),
+    (SMALL[15], 32), (SMALL[18], 16), (SMALL[19], 32), (SMALL[20], 16), (SMALL[21], 16),
 ]
 
 
