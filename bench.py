@@ -485,9 +485,9 @@ def main() -> int:
                     help="with --stream-probe: read M MiB instead of 1 GiB (512 work-groups unless "
                          "--stream-groups is given)")
     ap.add_argument("--stream-groups", type=int, default=0, metavar="G",
-                    help="with --stream-probe: split the 1 GiB into G equal work-group streams "
-                         "(default 512 of 2 MiB); G not a multiple of the 256 CUs leaves some CUs "
-                         "more streams than others")
+                    help="with --stream-probe: split the read into G equal work-group streams "
+                         "(default 512, 2 MiB each for 1 GiB); G not a multiple of the 256 CUs "
+                         "leaves some CUs more streams than others")
     ap.add_argument("--gather-probe", type=int, default=0, metavar="PIECE_BYTES",
                     help="only run the scattered-piece read probe (1 GiB in pieces of PIECE_BYTES, "
                          "a paged cache's pattern) and print its JSON line")
