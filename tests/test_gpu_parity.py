@@ -84,6 +84,10 @@ SMALL = [
     case("bf16-d128-g8-lone-window", 128, 8, 8, W.BF16, W.BF16, [2048] * 8, 64, window=700, seed=27),
     case("bf16-d64-g8-softcap-ragged", 64, 8, 2, W.BF16, W.BF16, [1300, 40, 700], 512, softcap=30.0,
          seed=28),
+    # one wave per item over items of unequal size, the window cutting every
+    # sequence's first split: the serpentine work-group placement
+    case("bf16-d128-g4-lone-window-ragged", 128, 4, 8, W.BF16, W.BF16,
+         np.random.default_rng(29).integers(300, 901, 32), 32, window=300, seed=29),
 ]
 
 
